@@ -1,0 +1,178 @@
+"""Pins of the NF4 oracle (oracle/nf4.py) against facts fixed outside it.
+
+- level table: invariants of the construction, an independent inverse-normal
+  (bisection on math.erfc) and the equal-probability spacing it encodes;
+- bf16 rounding: torch's own float32 -> bfloat16 conversion;
+- dequant: torch's fp32 multiply followed by torch's bf16 cast (the
+  two-rounding contract as computed by a different implementation);
+- quantize: exact round trips, monotonicity, brute force on one block;
+- packing: a hand-written fixture.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nf4
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _phi(x):
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def _phi_inv(p):
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if _phi(mid) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def test_table_invariants():
+    L = nf4.nf4_levels()
+    assert L.dtype == np.float32 and L.shape == (16,)
+    assert L[7] == 0.0 and not np.signbit(L[7])
+    assert L[0] == -1.0 and L[15] == 1.0
+    assert np.all(np.diff(L) > 0)
+    # 7 strictly negative, 8 strictly positive levels (asymmetric table)
+    assert (L < 0).sum() == 7 and (L > 0).sum() == 8
+
+
+def test_table_matches_independent_inverse_normal():
+    L = nf4.nf4_levels()
+    d = nf4.NF4_DELTA
+    top = _phi_inv(d)
+    want = [-_phi_inv(0.5 + (d - 0.5) * j / 7) / top for j in range(7, 0, -1)]
+    want += [0.0] + [_phi_inv(0.5 + (d - 0.5) * j / 8) / top for j in range(1, 9)]
+    got = L.astype(np.float64)
+    ulp = np.spacing(np.abs(L)).astype(np.float64)
+    assert np.all(np.abs(got - np.array(want)) <= ulp + 1e-300)
+
+
+def test_positive_levels_are_equal_probability_spaced():
+    L = nf4.nf4_levels_f64()
+    top = _phi_inv(nf4.NF4_DELTA)
+    probs = [_phi(L[8 + j] * top) for j in range(8)]
+    steps = np.diff([0.5] + probs)
+    assert np.allclose(steps, steps[0], rtol=0, atol=1e-12)
+    negs = [_phi(-L[6 - j] * top) for j in range(7)]
+    nsteps = np.diff([0.5] + negs)
+    assert np.allclose(nsteps, nsteps[0], rtol=0, atol=1e-12)
+
+
+def test_table_matches_stored_golden():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "nf4_levels.txt")) if not ln.startswith("#")]
+    bits = np.array([int(r[1], 16) for r in rows], dtype=np.uint32)
+    assert np.array_equal(nf4.nf4_levels().view(np.uint32), bits)
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(1)
+    x = g.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** g.integers(-30, 30, 200000)
+    u = x.view(np.uint32)
+    # force exact ties (low 16 bits = 0x8000) on a quarter of the values, both parities
+    u[::4] = (u[::4] & 0xFFFF0000) | 0x8000
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]   # NaN payload handling is not part of the contract
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(nf4.f32_to_bf16_bits(x), want)
+
+
+def _bf16_sweep():
+    # every positive normal bf16 value with exponent in [2^-24, 2^8)
+    exps = np.arange(127 - 24, 127 + 8, dtype=np.uint32)
+    mant = np.arange(128, dtype=np.uint32)
+    bits = ((exps[:, None] << 7) | mant[None, :]).reshape(-1).astype(np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_dequant_equals_torch_two_roundings_all_codes():
+    absmax = _bf16_sweep()
+    n = absmax.size
+    codes = np.tile(np.arange(16, dtype=np.uint8), (n, 4))       # [n][64]
+    packed = nf4.pack_codes(codes)
+    got = nf4.dequant_bf16_bits(packed, absmax[:, None])
+    L = torch.from_numpy(nf4.nf4_levels())
+    prod = L[torch.from_numpy(codes.astype(np.int64))] * torch.from_numpy(absmax)[:, None]  # fp32 RNE
+    want = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    # With this table a single rounding of the exact product (at most 32
+    # significant bits: 24 from the level, 8 from the bf16 absmax) never lands
+    # differently from the two-step rounding on normal values: the contract
+    # holds whichever order an implementation takes.
+    exact = nf4.nf4_levels().astype(np.float64)[codes] * absmax.astype(np.float64)[:, None]
+    mant, ex = np.frexp(exact)                       # exact = mant * 2^ex, |mant| in [0.5, 1)
+    single = np.round(mant * 256.0) * np.exp2(ex - 8.0)   # one rounding to 8 bits, ties to even
+    twice = nf4.bf16_bits_to_f64(want)
+    assert np.array_equal(single, twice)
+
+
+def test_zero_code_and_absmax_roundtrip():
+    g = np.random.default_rng(2)
+    w = nf4.f32_to_bf16_bits(g.standard_normal((32, 256)).astype(np.float32) * np.float32(0.02))
+    packed, absmax = nf4.quantize(w)
+    deq = nf4.dequant_bf16_bits(packed, absmax)
+    wv = nf4.bf16_bits_to_f64(w).reshape(32, 4, 64)
+    dv = nf4.bf16_bits_to_f64(deq).reshape(32, 4, 64)
+    idx = np.abs(wv).argmax(axis=2)
+    assert np.array_equal(np.take_along_axis(dv, idx[..., None], 2), np.take_along_axis(wv, idx[..., None], 2))
+    codes = nf4.unpack_codes(packed)
+    zero = nf4.bf16_bits_to_f64(deq)[codes == 7]
+    assert np.all(zero == 0.0) and not np.any(np.signbit(zero))
+
+
+def test_all_zero_block():
+    w = np.zeros((2, 128), dtype=np.uint16)
+    w[1, 64:] = nf4.f32_to_bf16_bits(np.linspace(-1, 1, 64).astype(np.float32))
+    packed, absmax = nf4.quantize(w)
+    codes = nf4.unpack_codes(packed)
+    assert absmax[0, 0] == 0 and absmax[0, 1] == 0 and absmax[1, 0] == 0 and absmax[1, 1] == 1.0
+    assert np.all(codes[0] == 7) and np.all(codes[1, :64] == 7)
+    assert np.all(nf4.dequant_bf16_bits(packed, absmax)[0] == 0)
+
+
+def test_quantize_dequant_roundtrip_of_codes():
+    g = np.random.default_rng(3)
+    codes = g.integers(0, 16, (16, 512)).astype(np.uint8)
+    codes[:, ::64] = 15                     # every block holds its +1 element
+    absmax = nf4.bf16_bits_to_f64(nf4.f32_to_bf16_bits(
+        np.abs(g.standard_normal((16, 8))).astype(np.float32) * np.float32(0.05) + np.float32(0.01))).astype(np.float32)
+    deq = nf4.dequant_bf16_bits(nf4.pack_codes(codes), absmax)
+    packed2, absmax2 = nf4.quantize(deq)
+    assert np.array_equal(absmax2, absmax)
+    assert np.array_equal(nf4.unpack_codes(packed2), codes)
+
+
+def test_quantize_monotone_and_brute_force_one_block():
+    L = [float(v) for v in nf4.nf4_levels()]
+    xs = np.linspace(-1.0, 1.0, 64).astype(np.float32)
+    w = nf4.f32_to_bf16_bits(xs * np.float32(0.75))[None, :]
+    packed, absmax = nf4.quantize(w)
+    codes = nf4.unpack_codes(packed)[0]
+    assert np.all(np.diff(codes.astype(int)) >= 0)
+    vals = nf4.bf16_bits_to_f64(w)[0]
+    amax = max(abs(v) for v in vals)
+    for v, c in zip(vals, codes):
+        x = v / amax
+        best = min(range(16), key=lambda i: (abs(x - L[i]), i))
+        assert c == best
+
+
+def test_packing_fixture():
+    lines = [ln for ln in open(os.path.join(GOLDEN, "nf4_pack_example.txt")) if not ln.startswith("#")]
+    codes = np.array([int(t) for t in lines[0].split()], dtype=np.uint8)[None, :]
+    want = np.array([int(t, 16) for t in lines[1].split()], dtype=np.uint8)[None, :]
+    assert np.array_equal(nf4.pack_codes(codes), want)
+    assert np.array_equal(nf4.unpack_codes(want), codes)
+
+
+def test_rejects_ragged_k():
+    with pytest.raises(ValueError):
+        nf4.quantize(np.zeros((1, 96), dtype=np.uint16))
