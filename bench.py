@@ -1,0 +1,169 @@
+"""Benchmark: QLoRA gated-MLP forward + backward on one MI355X.
+
+Workload (default): Llama-7B MLP block, 8192 tokens (4 x 2048) x 4096 ->
+11008 -> 4096, NF4 (blocksize 64) gate/up/down, LoRA rank 16, s = 1, SwiGLU,
+synthetic seeded inputs already resident in HBM. One step = qlora_mlp_fwd +
+qlora_mlp_bwd (every kernel of the path). The metric counts algorithmic
+FLOPs only: six base products 2*m*d*h plus the LoRA products (recompute,
+dequant and elementwise work are not counted).
+
+Prints ONE JSON line. Extra fields: roofline (the base-GEMM kernel, timed
+live with HIP events on its launch stream) and cpu_baseline (the fp64 CPU
+oracle on a bounded token sample of the same workload).
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama7b_mlp]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+METRIC = "QLoRA MLP fwd+bwd TFLOP/s + % bf16 MFMA peak, Llama-7B shape, 8192 tok"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama7b_mlp",
+                   choices=["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"])
+    p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
+    p.add_argument("--cpu-tokens", type=int, default=2048,
+                   help="token sample of the CPU oracle baseline (0 = skip)")
+    return p.parse_args()
+
+
+def mlp_flops(m, d, h, r):
+    """Algorithmic FLOPs of one MLP fwd+bwd: six base products 2*m*d*h (no base
+    weight gradient) plus 2*m*r*(in+out) per LoRA projection forward and twice
+    that backward."""
+    return 6 * 2 * m * d * h + 3 * 3 * 2 * m * r * (d + h)
+
+
+def gemm_traffic(lib_src_dir):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(os.path.join(lib_src_dir, "gemm.hip"), "rb").read()).hexdigest()
+    if rec.get("gemm_hip_sha256") != h:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, d, tokens):
+    """fp64 oracle (as it stands) on the first `tokens` tokens of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import nf4 as onf4
+    from oracle import qlora as oq
+
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    t0 = time.perf_counter()
+    W = {wn: onf4.dequant_f64(d[wn + "_codes"].numpy(), d[wn + "_absmax"].numpy())
+         for wn in ("Wg", "Wu", "Wd")}
+    t_dq = time.perf_counter() - t0
+    L = [f64(d[k]) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")]
+    X, dY = f64(d["X"][:tokens]), f64(d["dY"][:tokens])
+    args = (W["Wg"], W["Wu"], W["Wd"], *L, cfg.s, cfg.act)
+    t0 = time.perf_counter()
+    _, sv = oq.mlp_fwd(X, *args)
+    oq.mlp_bwd(dY, X, sv, *args)
+    t = time.perf_counter() - t0 + t_dq     # a step dequantizes its weights too
+    flops = oq.mlp_algorithmic_flops(tokens, cfg.d, cfg.h, cfg.r)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{tokens} of {cfg.m} tokens with the full {cfg.name} weights, fp64 numpy: "
+                      f"weight dequant {t_dq:.2f} s + fwd/bwd {t - t_dq:.2f} s",
+            "tokens_per_s": round(tokens / t, 3), "seconds": round(t, 3)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); "
+              "the multi-GPU data-parallel design is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import qlora_fine_tuning_amd as Q
+    from qlora_fine_tuning_amd import _lib
+    from qlora_fine_tuning_amd import inputs as I
+
+    cfg = {"llama7b_mlp": I.LLAMA_MLP, "mistral7b_mlp": I.MISTRAL_MLP,
+           "gemma7b_mlp": I.GEMMA_MLP}[a.workload]
+    dev = "cuda:0"
+    d = I.mlp_inputs(cfg, dense_w=False)
+    nf = lambda wn: Q.NF4Weight(d[wn + "_codes"].to(dev), d[wn + "_absmax"].to(dev))  # noqa: E731
+    w = Q.MlpWeights(nf("Wg"), nf("Wu"), nf("Wd"),
+                     *(d[k].to(dev) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")),
+                     s=cfg.s, act=cfg.act)
+    X, dY = d["X"].to(dev), d["dY"].to(dev)
+    ws = torch.empty(Q.mlp_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r, a.mode), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        _, sv = Q.mlp_fwd(X, w, mode=a.mode, ws=ws)
+        Q.mlp_bwd(dY, X, sv, w, mode=a.mode, ws=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    Q.trace_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / a.steps
+    launches, gemm_ms, gemm_flops = Q.trace_read()
+    Q.trace_enable(False)
+
+    flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
+    tflops = flops / (ms / 1e3) / 1e12
+    achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
+    traffic = gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"))
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.m, "d": cfg.d, "h": cfg.h, "r": cfg.r,
+                   "s": cfg.s, "act": cfg.act, "weights": "nf4 blocksize 64, fp32 absmax",
+                   "dequant_mode": a.mode, "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(cfg.m / (ms / 1e3), 1),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (base GEMMs, LoRA as K-extension)",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "launches_per_step": launches // a.steps,
+                     "avg_launch_ms": round(gemm_ms / launches, 4),
+                     "gemm_share_of_step": round(gemm_ms / a.steps / ms, 4)},
+    }
+    if a.cpu_tokens > 0:
+        del X, dY, ws, w
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, d, min(a.cpu_tokens, cfg.m))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * qlora.h - C ABI of the MI355X (gfx950) QLoRA linear / gated-MLP library.
+ *
+ * What is computed (the pages' statement of the problem):
+ *   - Frozen base weights W are stored in 4-bit NormalFloat ("QLoRA nf4" on
+ *     q/k/v/o/gate/up/down; Mistral benchmark page, configuration block) and
+ *     dequantized to bfloat16, never to float16 (same page, breakdown item 2,
+ *     "Bitsandbytes bfloat16").
+ *   - A rank-r LoRA side path with scale s = alpha / r (rank 16, alpha 16,
+ *     dropout 0 in the configuration block), bracketed rank-first:
+ *     X A^T is formed before anything of width in x out; the merged weight
+ *     W + s B A is never formed (same page, items 10-11 "manual autograd",
+ *     chained-matmul bracketing).
+ *   - Hand-derived backward producing dX, dA, dB; no gradient of the frozen W
+ *     (Show HN thread: "manual autograd engine - hand derived backprop").
+ *   - Gated MLP gate/up -> act -> down with SwiGLU (silu(g) * u) or tanh-GeGLU
+ *     (gelu_tanh(g) * u) (Gemma page, "GeGLU vs SwiGLU activation"), whose
+ *     activation is recomputed in the backward rather than stored.
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer unless stated otherwise.
+ *     Tensors are row-major and dense (leading dimension = row length).
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - NF4 weight of shape [n][k]: codes uint8 [n][k/2], element 2j of a row in
+ *     the HIGH nibble of byte j and element 2j+1 in the LOW nibble; absmax
+ *     float32 [n][k/64], one per 64 consecutive weights of a row. Dequantized
+ *     value: bf16_rne(fp32_rne(level[code] * absmax)).
+ *   - LoRA factors: A [r][in], B [out][r], bf16.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it and returns; nothing synchronizes the host.
+ *   - The library never allocates device memory. Scratch space is the
+ *     caller's `ws` buffer of at least the size returned by the matching
+ *     *_workspace_bytes() query (any 256-byte aligned device allocation).
+ *   - Validation errors return before anything is enqueued. A HIP launch
+ *     failure returns QLORA_EHIP; qlora_last_error() then gives the HIP
+ *     message (per thread).
+ *   - Shape limits: k, n (and d, h) multiples of 64; m >= 0 (m == 0 is a
+ *     no-op); 1 <= r <= 64 (1 <= r <= 32 for the MLP). Output buffers must
+ *     not alias inputs.
+ *   - Results are deterministic: two identical calls give identical bits
+ *     (no floating-point atomics; fixed reduction order).
+ *   - Calls that share one workspace buffer must not overlap in time.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_EINVAL = -1,     /* null pointer, bad r, non-finite s, unknown act/flag */
+  QLORA_ESHAPE = -2,     /* k or n not a multiple of 64, negative m, size overflow */
+  QLORA_EWORKSPACE = -3, /* ws NULL or ws_bytes below the query's answer */
+  QLORA_EHIP = -4,       /* HIP launch/runtime error (including no device) */
+  QLORA_ENOTIMPL = -5    /* valid request that this build does not implement */
+} qlora_status;
+
+typedef enum { QLORA_ACT_SWIGLU = 0, QLORA_ACT_GEGLU_TANH = 1 } qlora_act;
+
+/* How the NF4 base weight reaches the bf16 matrix cores.
+ *   QLORA_DEQUANT_AUTO   : the library's measured default for the shape.
+ *   QLORA_DEQUANT_FUSED  : codes are dequantized inside the GEMM while the
+ *                          weight tile is staged into LDS (no bf16 copy).
+ *   QLORA_DEQUANT_STAGED : each weight is first dequantized once into the
+ *                          workspace, then a plain bf16 GEMM reads it.
+ * Both give the same dequantized weights; results agree to rounding order. */
+typedef enum {
+  QLORA_DEQUANT_AUTO = 0,
+  QLORA_DEQUANT_FUSED = 1,
+  QLORA_DEQUANT_STAGED = 2
+} qlora_dequant_mode;
+
+/* An NF4-quantized weight of shape [n][k] (device pointers). */
+typedef struct qlora_nf4 {
+  const uint8_t* codes; /* [n][k/2] */
+  const float* absmax;  /* [n][k/64] */
+  int64_t n;
+  int64_t k;
+} qlora_nf4;
+
+/* The three projections of a gated MLP with hidden width d and MLP width h
+ * (Llama/Mistral/Gemma layout): gate, up [h][d]; down [d][h]; LoRA factors
+ * A_gate, A_up [r][d], B_gate, B_up [h][r], A_down [r][h], B_down [d][r].
+ * Passed by HOST pointer; the pointers inside are device pointers. */
+typedef struct qlora_mlp_weights {
+  qlora_nf4 gate, up, down;
+  const uint16_t* a_gate;
+  const uint16_t* b_gate;
+  const uint16_t* a_up;
+  const uint16_t* b_up;
+  const uint16_t* a_down;
+  const uint16_t* b_down;
+  int64_t d, h, r;
+  float s;   /* LoRA scale alpha / r (or any finite scale, e.g. rank-stabilised) */
+  int act;   /* qlora_act */
+} qlora_mlp_weights;
+
+/* LoRA weight gradients of the MLP (device pointers, bf16, same shapes as
+ * the factors). Passed by HOST pointer. */
+typedef struct qlora_mlp_grads {
+  uint16_t* a_gate;
+  uint16_t* b_gate;
+  uint16_t* a_up;
+  uint16_t* b_up;
+  uint16_t* a_down;
+  uint16_t* b_down;
+} qlora_mlp_grads;
+
+/* Text for a status code (static storage, never NULL). */
+const char* qlora_status_string(int status);
+
+/* Message of the last QLORA_EHIP on the calling thread ("" if none). */
+const char* qlora_last_error(void);
+
+/* Library version string, e.g. "qlora-mi355x 0.1 gfx950". */
+const char* qlora_version(void);
+
+/* The 16 NF4 levels compiled into the library, ascending (host buffer). */
+void qlora_nf4_levels(float out_host[16]);
+
+/* Standalone dequantization: out [n][k] bf16 = dequant(W). Bit-exact
+ * contract: bf16_rne(fp32_rne(level[code] * absmax)). */
+int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------- linear layer --
+ * Forward:  U = X A^T (saved, fp32 [m][r]);  Y = X W^T + s U B^T.
+ * Backward: T = dY B;  dX = dY W + s T A;  dA = s T^T X;  dB = s dY^T U.
+ * X [m][k], W NF4 [n][k], A [r][k], B [n][r], Y/dY [m][n], dX [m][k],
+ * dA [r][k], dB [n][r]. dX may be NULL (not wanted, e.g. first layer).
+ * (Mistral benchmark page, items 10-11; Reddit talk summary, "fused LoRA".) */
+size_t qlora_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r, int mode);
+
+int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                     uint16_t* Y, float* U_save, int mode,
+                     void* ws, size_t ws_bytes, void* stream);
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U,
+                     int64_t m, qlora_nf4 w,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                     uint16_t* dX, uint16_t* dA, uint16_t* dB, int mode,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ gated MLP --
+ * Forward:  g = X Wg^T + s (X Ag^T) Bg^T;  u likewise;  H = act(g) * u;
+ *           Y = H Wd^T + s (H Ad^T) Bd^T.
+ * Saved for the backward (caller-owned): g, u bf16 [m][h]; Ug, Uu fp32
+ * [m][r] (= X Ag^T, X Au^T); Ud fp32 [m][r] (= H Ad^T). H is not saved.
+ * Backward: recomputes H = act(g) * u; dH = dY Wd + s (dY Bd) Ad;
+ *           dg = dH * u * act'(g); du = dH * act(g);
+ *           dX = dg Wg + du Wu + s (dg Bg) Ag + s (du Bu) Au;
+ *           LoRA gradients as for the linear layer, per projection.
+ * (Mistral benchmark page, breakdown row "Manual Autograd MLP"; Gemma page,
+ * "GeGLU vs SwiGLU activation"; Reddit talk summary, "SwiGLU" kernel.) */
+size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int mode);
+
+int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w,
+                  uint16_t* Y, uint16_t* g_save, uint16_t* u_save,
+                  float* Ug, float* Uu, float* Ud, int mode,
+                  void* ws, size_t ws_bytes, void* stream);
+
+int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X,
+                  const uint16_t* g_save, const uint16_t* u_save,
+                  const float* Ug, const float* Uu, const float* Ud,
+                  int64_t m, const qlora_mlp_weights* w,
+                  uint16_t* dX, const qlora_mlp_grads* grads, int mode,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- tracing --
+ * Kernel timing aid for benchmarks and profiling. While enabled, every
+ * dense-contraction (base GEMM) launch made by the entry points above is
+ * bracketed by a pair of HIP events recorded on the launch stream, together
+ * with its algorithmic FLOP count (2 m n k of the base product plus
+ * 2 m n r of the LoRA term it carries). Enabling/disabling and reading are
+ * host calls; reading waits for the recorded events. Not thread-safe with
+ * concurrent entry-point calls. Disabled by default; costs nothing when off.
+ *   qlora_trace_enable(1) clears previous records and starts recording.
+ *   qlora_trace_read(...) returns the number of recorded launches, their
+ *   summed GPU time in milliseconds and summed algorithmic FLOPs. */
+int qlora_trace_enable(int on);
+int qlora_trace_read(int64_t* launches, double* total_ms, double* total_flops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,20 @@
+"""MI355X (gfx950) QLoRA linear layer and gated MLP, forward and backward.
+
+The computation lives in the HIP library libqlora_mi355x.so (C ABI in
+include/qlora.h); this package is its thin Python binding plus the seeded
+synthetic-input generator (``inputs``). Importing the package does not load
+the library; the first call does, and fails loudly if it was not built.
+"""
+
+__all__ = [
+    "NF4Weight", "MlpWeights", "version", "nf4_levels", "nf4_dequant",
+    "linear_workspace_bytes", "linear_fwd", "linear_bwd",
+    "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read",
+]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import api
+        return getattr(api, name)
+    raise AttributeError(name)

@@ -1,0 +1,105 @@
+"""ctypes binding of libqlora_mi355x.so (the C ABI in include/qlora.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed
+to the library, and every step of the computation runs in the library's
+gfx950 kernels. There is no fallback: if the library is missing or a call
+fails, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqlora_mi355x.so")
+
+QLORA_OK = 0
+STATUS = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLORA_EWORKSPACE",
+          -4: "QLORA_EHIP", -5: "QLORA_ENOTIMPL"}
+ACT = {"swiglu": 0, "geglu_tanh": 1}
+MODE = {"auto": 0, "fused": 1, "staged": 2}
+
+c_i64 = ctypes.c_int64
+c_vp = ctypes.c_void_p
+
+
+class Nf4(ctypes.Structure):
+    _fields_ = [("codes", c_vp), ("absmax", c_vp), ("n", c_i64), ("k", c_i64)]
+
+
+class MlpWeights(ctypes.Structure):
+    _fields_ = [("gate", Nf4), ("up", Nf4), ("down", Nf4),
+                ("a_gate", c_vp), ("b_gate", c_vp), ("a_up", c_vp), ("b_up", c_vp),
+                ("a_down", c_vp), ("b_down", c_vp),
+                ("d", c_i64), ("h", c_i64), ("r", c_i64), ("s", ctypes.c_float), ("act", ctypes.c_int)]
+
+
+class MlpGrads(ctypes.Structure):
+    _fields_ = [("a_gate", c_vp), ("b_gate", c_vp), ("a_up", c_vp), ("b_up", c_vp),
+                ("a_down", c_vp), ("b_down", c_vp)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m qlora_fine_tuning_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.qlora_status_string.restype = ctypes.c_char_p
+        L.qlora_status_string.argtypes = [ctypes.c_int]
+        L.qlora_last_error.restype = ctypes.c_char_p
+        L.qlora_last_error.argtypes = []
+        L.qlora_version.restype = ctypes.c_char_p
+        L.qlora_version.argtypes = []
+        L.qlora_nf4_levels.restype = None
+        L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        L.qlora_nf4_dequant.restype = ctypes.c_int
+        L.qlora_nf4_dequant.argtypes = [Nf4, c_vp, c_vp]
+        L.qlora_linear_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_linear_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
+        L.qlora_linear_fwd.restype = ctypes.c_int
+        L.qlora_linear_fwd.argtypes = [c_vp, c_i64, Nf4, c_vp, c_vp, c_i64, ctypes.c_float,
+                                       c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_linear_bwd.restype = ctypes.c_int
+        L.qlora_linear_bwd.argtypes = [c_vp, c_vp, c_vp, c_i64, Nf4, c_vp, c_vp, c_i64,
+                                       ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_int, c_vp,
+                                       ctypes.c_size_t, c_vp]
+        L.qlora_mlp_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_mlp_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
+        L.qlora_mlp_fwd.restype = ctypes.c_int
+        L.qlora_mlp_fwd.argtypes = [c_vp, c_i64, ctypes.POINTER(MlpWeights), c_vp, c_vp, c_vp,
+                                    c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_mlp_bwd.restype = ctypes.c_int
+        L.qlora_mlp_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                    ctypes.POINTER(MlpWeights), c_vp, ctypes.POINTER(MlpGrads),
+                                    ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_trace_enable.restype = ctypes.c_int
+        L.qlora_trace_enable.argtypes = [ctypes.c_int]
+        L.qlora_trace_read.restype = ctypes.c_int
+        L.qlora_trace_read.argtypes = [ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+        _LIB = L
+    return _LIB
+
+
+def check(status: int, what: str) -> None:
+    if status != QLORA_OK:
+        L = lib()
+        msg = L.qlora_status_string(status).decode()
+        extra = L.qlora_last_error().decode() if status == -4 else ""
+        raise RuntimeError(f"{what}: {STATUS.get(status, status)}: {msg} {extra}".strip())
+
+
+EXPORTED = [
+    "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
+    "qlora_nf4_dequant", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
+    "qlora_trace_enable", "qlora_trace_read",
+]

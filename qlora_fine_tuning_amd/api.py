@@ -1,0 +1,237 @@
+"""Tensor-level entry points over the C ABI (same names as the exported calls).
+
+Each function checks its torch tensors (device, dtype, shape, contiguity),
+allocates outputs and the workspace with torch (device memory only), and
+enqueues the library call on torch's current HIP stream. All computation
+happens in the library's gfx950 kernels.
+
+Shapes (row-major): X [m][k], NF4 weight [n][k] (codes uint8 [n][k/2],
+absmax float32 [n][k/64]), LoRA A [r][k], B [n][r]; MLP: X [m][d],
+gate/up [h][d], down [d][h], A_gate/A_up [r][d], B_gate/B_up [h][r],
+A_down [r][h], B_down [d][r]. bf16 everywhere except U/T (fp32) and absmax.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_WS = {}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes (256-byte aligned by torch)."""
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+@dataclasses.dataclass
+class NF4Weight:
+    """NF4 weight of shape [n][k]: codes uint8 [n][k/2], absmax float32 [n][k/64]."""
+    codes: torch.Tensor
+    absmax: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1] * 2
+
+    def c_struct(self) -> _lib.Nf4:
+        _need(self.codes, "codes", torch.uint8, (self.n, self.k // 2))
+        _need(self.absmax, "absmax", torch.float32, (self.n, self.k // 64))
+        return _lib.Nf4(self.codes.data_ptr(), self.absmax.data_ptr(), self.n, self.k)
+
+    def to(self, device):
+        return NF4Weight(self.codes.to(device), self.absmax.to(device))
+
+
+def version() -> str:
+    return _lib.lib().qlora_version().decode()
+
+
+def trace_enable(on: bool = True) -> None:
+    """Start (clearing old records) or stop timing every base-GEMM launch."""
+    _lib.check(_lib.lib().qlora_trace_enable(1 if on else 0), "qlora_trace_enable")
+
+
+def trace_read():
+    """(launches, total GPU ms, total algorithmic FLOPs) of the recorded GEMMs."""
+    n, ms, fl = _lib.c_i64(0), ctypes.c_double(0), ctypes.c_double(0)
+    _lib.check(_lib.lib().qlora_trace_read(ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)),
+               "qlora_trace_read")
+    return n.value, ms.value, fl.value
+
+
+def nf4_levels() -> torch.Tensor:
+    buf = (ctypes.c_float * 16)()
+    _lib.lib().qlora_nf4_levels(buf)
+    return torch.tensor(list(buf), dtype=torch.float32)
+
+
+def nf4_dequant(w: NF4Weight) -> torch.Tensor:
+    out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
+    _lib.check(_lib.lib().qlora_nf4_dequant(w.c_struct(), _ptr(out), _stream()), "qlora_nf4_dequant")
+    return out
+
+
+# ------------------------------------------------------------- linear layer --
+def linear_workspace_bytes(m, k, n, r, mode="auto") -> int:
+    return int(_lib.lib().qlora_linear_workspace_bytes(m, k, n, r, _lib.MODE[mode]))
+
+
+def linear_fwd(X, w: NF4Weight, A, B, s: float, mode="auto", ws=None):
+    """Returns (Y [m][n] bf16, U [m][r] fp32)."""
+    m, k, n, r = X.shape[0], w.k, w.n, A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(A, "A", torch.bfloat16, (r, k))
+    _need(B, "B", torch.bfloat16, (n, r))
+    Y = torch.empty((m, n), dtype=torch.bfloat16, device=X.device)
+    U = torch.empty((m, r), dtype=torch.float32, device=X.device)
+    nb = linear_workspace_bytes(m, k, n, r, mode)
+    ws = workspace(nb, X.device) if ws is None else ws
+    st = _lib.lib().qlora_linear_fwd(_ptr(X), m, w.c_struct(), _ptr(A), _ptr(B), r, float(s),
+                                     _ptr(Y), _ptr(U), _lib.MODE[mode], _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_linear_fwd")
+    return Y, U
+
+
+def linear_bwd(dY, X, U, w: NF4Weight, A, B, s: float, need_dx=True, mode="auto", ws=None):
+    """Returns (dX [m][k] or None, dA [r][k], dB [n][r]), all bf16."""
+    m, k, n, r = X.shape[0], w.k, w.n, A.shape[0]
+    _need(dY, "dY", torch.bfloat16, (m, n))
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(U, "U", torch.float32, (m, r))
+    _need(A, "A", torch.bfloat16, (r, k))
+    _need(B, "B", torch.bfloat16, (n, r))
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=X.device) if need_dx else None
+    dA = torch.empty((r, k), dtype=torch.bfloat16, device=X.device)
+    dB = torch.empty((n, r), dtype=torch.bfloat16, device=X.device)
+    nb = linear_workspace_bytes(m, k, n, r, mode)
+    ws = workspace(nb, X.device) if ws is None else ws
+    st = _lib.lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(U), m, w.c_struct(), _ptr(A), _ptr(B),
+                                     r, float(s), _ptr(dX), _ptr(dA), _ptr(dB), _lib.MODE[mode],
+                                     _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+# ---------------------------------------------------------------- gated MLP --
+@dataclasses.dataclass
+class MlpWeights:
+    gate: NF4Weight
+    up: NF4Weight
+    down: NF4Weight
+    a_gate: torch.Tensor
+    b_gate: torch.Tensor
+    a_up: torch.Tensor
+    b_up: torch.Tensor
+    a_down: torch.Tensor
+    b_down: torch.Tensor
+    s: float
+    act: str = "swiglu"
+
+    @property
+    def d(self):
+        return self.gate.k
+
+    @property
+    def h(self):
+        return self.gate.n
+
+    @property
+    def r(self):
+        return self.a_gate.shape[0]
+
+    def c_struct(self) -> _lib.MlpWeights:
+        d, h, r = self.d, self.h, self.r
+        for name, t, shape in (("a_gate", self.a_gate, (r, d)), ("a_up", self.a_up, (r, d)),
+                               ("a_down", self.a_down, (r, h)), ("b_gate", self.b_gate, (h, r)),
+                               ("b_up", self.b_up, (h, r)), ("b_down", self.b_down, (d, r))):
+            _need(t, name, torch.bfloat16, shape)
+        return _lib.MlpWeights(self.gate.c_struct(), self.up.c_struct(), self.down.c_struct(),
+                               self.a_gate.data_ptr(), self.b_gate.data_ptr(), self.a_up.data_ptr(),
+                               self.b_up.data_ptr(), self.a_down.data_ptr(), self.b_down.data_ptr(),
+                               d, h, r, float(self.s), _lib.ACT[self.act])
+
+
+def mlp_workspace_bytes(m, d, h, r, mode="auto") -> int:
+    return int(_lib.lib().qlora_mlp_workspace_bytes(m, d, h, r, _lib.MODE[mode]))
+
+
+def mlp_fwd(X, w: MlpWeights, mode="auto", ws=None):
+    """Returns (Y [m][d] bf16, saved) with saved = dict(g, u, Ug, Uu, Ud)."""
+    m, d, h, r = X.shape[0], w.d, w.h, w.r
+    _need(X, "X", torch.bfloat16, (m, d))
+    dev = X.device
+    Y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    saved = dict(g=torch.empty((m, h), dtype=torch.bfloat16, device=dev),
+                 u=torch.empty((m, h), dtype=torch.bfloat16, device=dev),
+                 Ug=torch.empty((m, r), dtype=torch.float32, device=dev),
+                 Uu=torch.empty((m, r), dtype=torch.float32, device=dev),
+                 Ud=torch.empty((m, r), dtype=torch.float32, device=dev))
+    nb = mlp_workspace_bytes(m, d, h, r, mode)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = _lib.lib().qlora_mlp_fwd(_ptr(X), m, ctypes.byref(cw), _ptr(Y), _ptr(saved["g"]),
+                                  _ptr(saved["u"]), _ptr(saved["Ug"]), _ptr(saved["Uu"]),
+                                  _ptr(saved["Ud"]), _lib.MODE[mode], _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_mlp_fwd")
+    return Y, saved
+
+
+def mlp_bwd(dY, X, saved, w: MlpWeights, need_dx=True, mode="auto", ws=None):
+    """Returns dict(dX, dAg, dBg, dAu, dBu, dAd, dBd), all bf16."""
+    m, d, h, r = X.shape[0], w.d, w.h, w.r
+    _need(dY, "dY", torch.bfloat16, (m, d))
+    _need(X, "X", torch.bfloat16, (m, d))
+    for k_, sh, dt in (("g", (m, h), torch.bfloat16), ("u", (m, h), torch.bfloat16),
+                       ("Ug", (m, r), torch.float32), ("Uu", (m, r), torch.float32),
+                       ("Ud", (m, r), torch.float32)):
+        _need(saved[k_], k_, dt, sh)
+    dev = X.device
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    out = dict(dX=e(m, d) if need_dx else None, dAg=e(r, d), dBg=e(h, r), dAu=e(r, d),
+               dBu=e(h, r), dAd=e(r, h), dBd=e(d, r))
+    grads = _lib.MlpGrads(out["dAg"].data_ptr(), out["dBg"].data_ptr(), out["dAu"].data_ptr(),
+                          out["dBu"].data_ptr(), out["dAd"].data_ptr(), out["dBd"].data_ptr())
+    nb = mlp_workspace_bytes(m, d, h, r, mode)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = _lib.lib().qlora_mlp_bwd(_ptr(dY), _ptr(X), _ptr(saved["g"]), _ptr(saved["u"]),
+                                  _ptr(saved["Ug"]), _ptr(saved["Uu"]), _ptr(saved["Ud"]), m,
+                                  ctypes.byref(cw), _ptr(out["dX"]), ctypes.byref(grads),
+                                  _lib.MODE[mode], _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_mlp_bwd")
+    return out

@@ -1,0 +1,571 @@
+// C ABI of the QLoRA linear / gated-MLP library (declared in include/qlora.h).
+//
+// This file validates arguments, carves the caller's workspace and enqueues
+// the gfx950 kernels on the caller's stream in dependency order. It never
+// allocates and never synchronizes the host.
+//
+// Step order follows the pages' manual autograd with rank-first bracketing
+// (Mistral benchmark page, items 10-11; breakdown row "Manual Autograd MLP"):
+//   linear fwd : U = X A^T  ->  Y = X W^T + s U B^T (one GEMM, LoRA as K-extension)
+//   linear bwd : T = dY B, dB = s dY^T U  ->  dX = dY W + s T A (one GEMM)  ->  dA = s T^T X
+//   MLP fwd    : [Ug|Uu] = X [Ag;Au]^T -> gate||up GEMM with act epilogue (g, u, H)
+//                -> Ud = H Ad^T -> down GEMM
+//   MLP bwd    : Td = dY Bd, dBd -> dH GEMM with act' epilogue (dg, du) -> dAd (H recomputed)
+//                -> [Tg|Tu] = [dg|du] blockdiag(Bg,Bu), dBg, dBu -> dX GEMM (K = 2h) -> dAg, dAu
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/qlora.h"
+#include "kernels.hpp"
+
+using namespace qlora;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return QLORA_EHIP;
+}
+
+#define QL_TRY(expr, where)                        \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// Bump allocator over the caller's workspace (or a size counter when base == nullptr).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+inline int64_t ceil16(int64_t x) { return (x + 15) / 16 * 16; }
+
+bool bad_nf4(const qlora_nf4& w) { return !w.codes || !w.absmax; }
+
+int resolve_mode(int mode) {
+  if (mode == QLORA_DEQUANT_AUTO) return QLORA_DEQUANT_STAGED;
+  return mode;
+}
+
+bool valid_mode(int mode) { return mode >= QLORA_DEQUANT_AUTO && mode <= QLORA_DEQUANT_STAGED; }
+
+// ------------------------------------------------------------ linear plan --
+struct LinearFwdWs {
+  uint16_t* bext;  // [n][KE]
+  uint16_t* uext;  // [m][KE]
+  uint16_t* wbf;   // [n][k] (staged)
+};
+
+size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearFwdWs* w) {
+  const int64_t KE = ceil16(2 * r);
+  LinearFwdWs t;
+  t.bext = c.take<uint16_t>(n * KE);
+  t.uext = c.take<uint16_t>(m * KE);
+  t.wbf = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(n * k) : nullptr;
+  if (w) *w = t;
+  return c.off;
+}
+
+struct LinearBwdWs {
+  uint16_t* lt;    // [r][n]   B^T
+  uint16_t* bext;  // [k][KE]  [A^T | A^T]
+  float* t;        // [m][r]
+  uint16_t* text;  // [m][KE]
+  float* part;     // [chunks][max(n,k)][r]
+  uint16_t* wt;    // [k][n]   dequantized W^T
+};
+
+size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, LinearBwdWs* w) {
+  const int64_t KE = ceil16(2 * r);
+  const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
+  LinearBwdWs t;
+  t.lt = c.take<uint16_t>(r * n);
+  t.bext = c.take<uint16_t>(k * KE);
+  t.t = c.take<float>(m * r);
+  t.text = c.take<uint16_t>(m * KE);
+  t.part = c.take<float>(chunks * std::max(n, k) * r);
+  t.wt = c.take<uint16_t>(k * n);
+  if (w) *w = t;
+  return c.off;
+}
+
+// --------------------------------------------------------------- MLP plan --
+struct MlpFwdWs {
+  uint16_t* lgu;     // [2r][d]
+  uint16_t* bextgu;  // [2h][KEgu]
+  uint16_t* bextd;   // [d][KEd]
+  uint16_t* uextgu;  // [m][KEgu]
+  uint16_t* uextd;   // [m][KEd]
+  uint16_t* H;       // [m][h]
+  uint16_t* wgu;     // [2h][d] staged, 32-row interleave of gate/up
+  uint16_t* wd;      // [d][h]  staged
+};
+
+size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpFwdWs* w) {
+  const int64_t KEgu = ceil16(4 * r), KEd = ceil16(2 * r);
+  MlpFwdWs t;
+  t.lgu = c.take<uint16_t>(2 * r * d);
+  t.bextgu = c.take<uint16_t>(2 * h * KEgu);
+  t.bextd = c.take<uint16_t>(d * KEd);
+  t.uextgu = c.take<uint16_t>(m * KEgu);
+  t.uextd = c.take<uint16_t>(m * KEd);
+  t.H = c.take<uint16_t>(m * h);
+  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  t.wgu = staged ? c.take<uint16_t>(2 * h * d) : nullptr;
+  t.wd = staged ? c.take<uint16_t>(d * h) : nullptr;
+  if (w) *w = t;
+  return c.off;
+}
+
+struct MlpBwdWs {
+  uint16_t* ltd;     // [r][d]     Bd^T
+  uint16_t* bextdh;  // [h][KEd]   [Ad^T | Ad^T]
+  uint16_t* ltgu;    // [2r][2h]   blockdiag(Bg^T, Bu^T)
+  uint16_t* bextdx;  // [d][KEgu]  [Ag^T | Au^T | Ag^T | Au^T]
+  float* td;         // [m][r]
+  uint16_t* textd;   // [m][KEd]
+  uint16_t* dgu;     // [m][2h]
+  float* tgu;        // [m][2r]
+  uint16_t* textgu;  // [m][KEgu]
+  float* part;       // [chunks][max(d,h)][2r]
+  uint16_t* wdt;     // [h][d]
+  uint16_t* wgut;    // [d][2h]
+};
+
+size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, MlpBwdWs* w) {
+  const int64_t KEgu = ceil16(4 * r), KEd = ceil16(2 * r);
+  const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
+  MlpBwdWs t;
+  t.ltd = c.take<uint16_t>(r * d);
+  t.bextdh = c.take<uint16_t>(h * KEd);
+  t.ltgu = c.take<uint16_t>(2 * r * 2 * h);
+  t.bextdx = c.take<uint16_t>(d * KEgu);
+  t.td = c.take<float>(m * r);
+  t.textd = c.take<uint16_t>(m * KEd);
+  t.dgu = c.take<uint16_t>(m * 2 * h);
+  t.tgu = c.take<float>(m * 2 * r);
+  t.textgu = c.take<uint16_t>(m * KEgu);
+  t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
+  t.wdt = c.take<uint16_t>(h * d);
+  t.wgut = c.take<uint16_t>(d * 2 * h);
+  if (w) *w = t;
+  return c.off;
+}
+
+bool dims_ok(int64_t m, int64_t k, int64_t n) {
+  const int64_t lim = (int64_t)1 << 30;
+  return m >= 0 && k > 0 && n > 0 && k % 64 == 0 && n % 64 == 0 && m < lim && k < lim && n < lim;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need && (!ws || ws_bytes < need)) return QLORA_EWORKSPACE;
+  if (ws && ((uintptr_t)ws & 255)) return QLORA_EWORKSPACE;
+  return QLORA_OK;
+}
+
+GemmArgs gemm_args() {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  return a;
+}
+
+// ---- tracing: HIP events around base-GEMM launches (off by default) ----
+struct TraceRec {
+  hipEvent_t start, stop;
+  double flops;
+};
+bool g_trace_on = false;
+std::vector<TraceRec> g_trace;
+
+void trace_clear() {
+  for (auto& t : g_trace) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_trace.clear();
+}
+
+// Launch one base GEMM; r_alg is the LoRA rank the algorithmic count charges.
+hipError_t run_gemm(const GemmArgs& g, int64_t r_alg, hipStream_t st) {
+  if (!g_trace_on) return launch_gemm(g, st);
+  TraceRec t;
+  t.flops = 2.0 * g.M * (double)g.N * ((double)g.K + (double)r_alg);
+  hipError_t e = hipEventCreate(&t.start);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&t.stop);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.start, st);
+  if (e != hipSuccess) return e;
+  e = launch_gemm(g, st);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.stop, st);
+  if (e != hipSuccess) return e;
+  g_trace.push_back(t);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_EINVAL: return "invalid argument (null pointer, rank, scale, activation or mode)";
+    case QLORA_ESHAPE: return "invalid shape (k, n, d, h must be positive multiples of 64; m >= 0)";
+    case QLORA_EWORKSPACE: return "workspace missing, misaligned or smaller than the query's answer";
+    case QLORA_EHIP: return "HIP runtime or launch error (see qlora_last_error)";
+    case QLORA_ENOTIMPL: return "not implemented in this build";
+  }
+  return "unknown status";
+}
+
+const char* qlora_last_error(void) { return g_last_error.c_str(); }
+
+const char* qlora_version(void) { return "qlora-mi355x 0.1 gfx950"; }
+
+int qlora_trace_enable(int on) {
+  trace_clear();
+  g_trace_on = on != 0;
+  return QLORA_OK;
+}
+
+int qlora_trace_read(int64_t* launches, double* total_ms, double* total_flops) {
+  if (!launches || !total_ms || !total_flops) return QLORA_EINVAL;
+  double ms = 0.0, fl = 0.0;
+  for (auto& t : g_trace) {
+    QL_TRY(hipEventSynchronize(t.stop), "trace_read");
+    float e = 0.0f;
+    QL_TRY(hipEventElapsedTime(&e, t.start, t.stop), "trace_read");
+    ms += e;
+    fl += t.flops;
+  }
+  *launches = (int64_t)g_trace.size();
+  *total_ms = ms;
+  *total_flops = fl;
+  return QLORA_OK;
+}
+
+void qlora_nf4_levels(float out_host[16]) { nf4_levels_host(out_host); }
+
+int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream) {
+  if (bad_nf4(w) || !out) return QLORA_EINVAL;
+  if (!dims_ok(0, w.k, w.n)) return QLORA_ESHAPE;
+  QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, w.n, w.k, out, w.k, 0, (hipStream_t)stream),
+         "nf4_dequant");
+  return QLORA_OK;
+}
+
+// ------------------------------------------------------------ linear layer --
+size_t qlora_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
+  if (!dims_ok(m, k, n) || r < 1 || r > 64 || !valid_mode(mode)) return 0;
+  mode = resolve_mode(mode);
+  Carver a(nullptr), b(nullptr);
+  return std::max(plan_linear_fwd(a, m, k, n, r, mode, nullptr), plan_linear_bwd(b, m, k, n, r, nullptr));
+}
+
+int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* A,
+                     const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save, int mode,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !A || !B || !Y || bad_nf4(w)) return QLORA_EINVAL;
+  if (r < 1 || r > 64 || !std::isfinite(s) || !valid_mode(mode)) return QLORA_EINVAL;
+  const int64_t k = w.k, n = w.n;
+  if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
+  mode = resolve_mode(mode);
+  const size_t need = qlora_linear_workspace_bytes(m, k, n, r, mode);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  if (m == 0) return QLORA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  LinearFwdWs t;
+  plan_linear_fwd(c, m, k, n, r, mode, &t);
+  const int KE = (int)ceil16(2 * r);
+
+  QL_TRY(launch_zero(t.bext, (size_t)n * KE * 2, st), "linear_fwd: zero");
+  QL_TRY(launch_copy2d(B, r, 1, (int)n, (int)r, t.bext, KE, 1, 0, st), "linear_fwd: Bext");
+  QL_TRY(launch_copy2d(B, r, 1, (int)n, (int)r, t.bext + r, KE, 1, 0, st), "linear_fwd: Bext");
+  if (mode == QLORA_DEQUANT_STAGED)
+    QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, n, k, t.wbf, k, 0, st), "linear_fwd: dequant");
+  QL_TRY(launch_rowdot(X, k, A, k, (int)m, (int)k, (int)r, s, U_save, nullptr, (int)r, r, t.uext,
+                       KE, KE, st),
+         "linear_fwd: U = X A^T");
+  GemmArgs g = gemm_args();
+  g.A = X; g.lda = k;
+  if (mode == QLORA_DEQUANT_STAGED) { g.bsrc = BSRC_BF16; g.B = t.wbf; g.ldb = k; }
+  else { g.bsrc = BSRC_NF4; g.codes0 = w.codes; g.absmax0 = w.absmax; }
+  g.Ae = t.uext; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
+  g.M = (int)m; g.N = (int)n; g.K = (int)k; g.KE = KE;
+  g.epi = EPI_STORE; g.C = Y; g.ldc = n;
+  QL_TRY(run_gemm(g, r, st), "linear_fwd: GEMM");
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m, qlora_nf4 w,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* dX,
+                     uint16_t* dA, uint16_t* dB, int mode, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!dY || !X || !U || !A || !B || !dA || !dB || bad_nf4(w)) return QLORA_EINVAL;
+  if (r < 1 || r > 64 || !std::isfinite(s) || !valid_mode(mode)) return QLORA_EINVAL;
+  const int64_t k = w.k, n = w.n;
+  if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
+  mode = resolve_mode(mode);
+  const size_t need = qlora_linear_workspace_bytes(m, k, n, r, mode);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (m == 0) {  // empty batch: zero weight gradients
+    QL_TRY(launch_zero(dA, (size_t)r * k * 2, st), "linear_bwd: zero dA");
+    QL_TRY(launch_zero(dB, (size_t)n * r * 2, st), "linear_bwd: zero dB");
+    return QLORA_OK;
+  }
+  Carver c(ws);
+  LinearBwdWs t;
+  plan_linear_bwd(c, m, k, n, r, &t);
+  const int KE = (int)ceil16(2 * r);
+  const int chunks = colreduce_chunks((int)m);
+
+  QL_TRY(launch_copy2d(B, 1, r, (int)r, (int)n, t.lt, n, 1, 0, st), "linear_bwd: B^T");
+  QL_TRY(launch_zero(t.bext, (size_t)k * KE * 2, st), "linear_bwd: zero");
+  QL_TRY(launch_copy2d(A, 1, k, (int)k, (int)r, t.bext, KE, 1, 0, st), "linear_bwd: A^T");
+  QL_TRY(launch_copy2d(A, 1, k, (int)k, (int)r, t.bext + r, KE, 1, 0, st), "linear_bwd: A^T");
+  // T = dY B
+  QL_TRY(launch_rowdot(dY, n, t.lt, n, (int)m, (int)n, (int)r, s, t.t, nullptr, (int)r, r, t.text,
+                       KE, KE, st),
+         "linear_bwd: T = dY B");
+  // dB = s dY^T U
+  QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, n, (int)m, (int)n, U, r, (int)r, t.part, st),
+         "linear_bwd: dB partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)n, (int)r, 0, (int)r, s, dB, r, 1, st),
+         "linear_bwd: dB");
+  // dX = dY W + s T A
+  if (dX) {
+    QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
+           "linear_bwd: dequant W^T");
+    GemmArgs g = gemm_args();
+    g.A = dY; g.lda = n; g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = n;
+    g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
+    g.M = (int)m; g.N = (int)k; g.K = (int)n; g.KE = KE;
+    g.epi = EPI_STORE; g.C = dX; g.ldc = k;
+    QL_TRY(run_gemm(g, r, st), "linear_bwd: dX GEMM");
+  }
+  // dA = s T^T X
+  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, k, (int)m, (int)k, t.t, r, (int)r, t.part, st),
+         "linear_bwd: dA partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)k, (int)r, 0, (int)r, s, dA, 1, k, st),
+         "linear_bwd: dA");
+  return QLORA_OK;
+}
+
+// --------------------------------------------------------------- gated MLP --
+static int check_mlp(const qlora_mlp_weights* w, int mode) {
+  if (!w) return QLORA_EINVAL;
+  if (bad_nf4(w->gate) || bad_nf4(w->up) || bad_nf4(w->down)) return QLORA_EINVAL;
+  if (!w->a_gate || !w->b_gate || !w->a_up || !w->b_up || !w->a_down || !w->b_down) return QLORA_EINVAL;
+  if (w->r < 1 || w->r > 32 || !std::isfinite(w->s)) return QLORA_EINVAL;
+  if (w->act != QLORA_ACT_SWIGLU && w->act != QLORA_ACT_GEGLU_TANH) return QLORA_EINVAL;
+  if (!valid_mode(mode)) return QLORA_EINVAL;
+  const int64_t d = w->d, h = w->h;
+  if (!dims_ok(0, d, h)) return QLORA_ESHAPE;
+  if (w->gate.n != h || w->gate.k != d || w->up.n != h || w->up.k != d || w->down.n != d ||
+      w->down.k != h)
+    return QLORA_ESHAPE;
+  return QLORA_OK;
+}
+
+size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
+  if (!dims_ok(m, d, h) || r < 1 || r > 32 || !valid_mode(mode)) return 0;
+  mode = resolve_mode(mode);
+  Carver a(nullptr), b(nullptr);
+  return std::max(plan_mlp_fwd(a, m, d, h, r, mode, nullptr), plan_mlp_bwd(b, m, d, h, r, nullptr));
+}
+
+int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint16_t* Y,
+                  uint16_t* g_save, uint16_t* u_save, float* Ug, float* Uu, float* Ud, int mode,
+                  void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_mlp(w, mode)) return e;
+  if (!X || !Y || !g_save || !u_save || !Ug || !Uu || !Ud) return QLORA_EINVAL;
+  const int64_t d = w->d, h = w->h, r = w->r;
+  if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  mode = resolve_mode(mode);
+  const size_t need = qlora_mlp_workspace_bytes(m, d, h, r, mode);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  if (m == 0) return QLORA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  MlpFwdWs t;
+  plan_mlp_fwd(c, m, d, h, r, mode, &t);
+  const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
+  const float s = w->s;
+
+  // LoRA operand layouts
+  QL_TRY(launch_copy2d(w->a_gate, d, 1, (int)r, (int)d, t.lgu, d, 1, 0, st), "mlp_fwd: Lgu");
+  QL_TRY(launch_copy2d(w->a_up, d, 1, (int)r, (int)d, t.lgu + r * d, d, 1, 0, st), "mlp_fwd: Lgu");
+  QL_TRY(launch_zero(t.bextgu, (size_t)2 * h * KEgu * 2, st), "mlp_fwd: zero");
+  QL_TRY(launch_copy2d(w->b_gate, r, 1, (int)h, (int)r, t.bextgu, KEgu, 1, 1, st), "mlp_fwd: Bext");
+  QL_TRY(launch_copy2d(w->b_gate, r, 1, (int)h, (int)r, t.bextgu + 2 * r, KEgu, 1, 1, st), "mlp_fwd: Bext");
+  QL_TRY(launch_copy2d(w->b_up, r, 1, (int)h, (int)r, t.bextgu + r, KEgu, 1, 2, st), "mlp_fwd: Bext");
+  QL_TRY(launch_copy2d(w->b_up, r, 1, (int)h, (int)r, t.bextgu + 3 * r, KEgu, 1, 2, st), "mlp_fwd: Bext");
+  QL_TRY(launch_zero(t.bextd, (size_t)d * KEd * 2, st), "mlp_fwd: zero");
+  QL_TRY(launch_copy2d(w->b_down, r, 1, (int)d, (int)r, t.bextd, KEd, 1, 0, st), "mlp_fwd: Bext");
+  QL_TRY(launch_copy2d(w->b_down, r, 1, (int)d, (int)r, t.bextd + r, KEd, 1, 0, st), "mlp_fwd: Bext");
+  if (mode == QLORA_DEQUANT_STAGED) {
+    QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
+    QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
+    QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, st), "mlp_fwd: dequant");
+  }
+  // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
+  QL_TRY(launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
+                       t.uextgu, KEgu, KEgu, st),
+         "mlp_fwd: Ug, Uu");
+  // gate || up GEMM with the activation epilogue
+  GemmArgs g = gemm_args();
+  g.A = X; g.lda = d;
+  if (mode == QLORA_DEQUANT_STAGED) { g.bsrc = BSRC_BF16; g.B = t.wgu; g.ldb = d; }
+  else {
+    g.bsrc = BSRC_NF4_PAIR;
+    g.codes0 = w->gate.codes; g.absmax0 = w->gate.absmax;
+    g.codes1 = w->up.codes; g.absmax1 = w->up.absmax;
+  }
+  g.Ae = t.uextgu; g.ldae = KEgu; g.Be = t.bextgu; g.ldbe = KEgu;
+  g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
+  g.epi = EPI_GATEUP; g.g_out = g_save; g.u_out = u_save; g.h_out = t.H; g.hdim = h; g.act = w->act;
+  QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
+  // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
+  QL_TRY(launch_rowdot(t.H, h, w->a_down, h, (int)m, (int)h, (int)r, s, Ud, nullptr, (int)r, r,
+                       t.uextd, KEd, KEd, st),
+         "mlp_fwd: Ud");
+  GemmArgs g2 = gemm_args();
+  g2.A = t.H; g2.lda = h;
+  if (mode == QLORA_DEQUANT_STAGED) { g2.bsrc = BSRC_BF16; g2.B = t.wd; g2.ldb = h; }
+  else { g2.bsrc = BSRC_NF4; g2.codes0 = w->down.codes; g2.absmax0 = w->down.absmax; }
+  g2.Ae = t.uextd; g2.ldae = KEd; g2.Be = t.bextd; g2.ldbe = KEd;
+  g2.M = (int)m; g2.N = (int)d; g2.K = (int)h; g2.KE = KEd;
+  g2.epi = EPI_STORE; g2.C = Y; g2.ldc = d;
+  QL_TRY(run_gemm(g2, r, st), "mlp_fwd: down GEMM");
+  return QLORA_OK;
+}
+
+int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
+                  const uint16_t* u_save, const float* Ug, const float* Uu, const float* Ud,
+                  int64_t m, const qlora_mlp_weights* w, uint16_t* dX,
+                  const qlora_mlp_grads* gr, int mode, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_mlp(w, mode)) return e;
+  if (!dY || !X || !g_save || !u_save || !Ug || !Uu || !Ud || !gr) return QLORA_EINVAL;
+  if (!gr->a_gate || !gr->b_gate || !gr->a_up || !gr->b_up || !gr->a_down || !gr->b_down)
+    return QLORA_EINVAL;
+  const int64_t d = w->d, h = w->h, r = w->r;
+  if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  mode = resolve_mode(mode);
+  const size_t need = qlora_mlp_workspace_bytes(m, d, h, r, mode);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (m == 0) {
+    QL_TRY(launch_zero(gr->a_gate, (size_t)r * d * 2, st), "mlp_bwd: zero");
+    QL_TRY(launch_zero(gr->a_up, (size_t)r * d * 2, st), "mlp_bwd: zero");
+    QL_TRY(launch_zero(gr->a_down, (size_t)r * h * 2, st), "mlp_bwd: zero");
+    QL_TRY(launch_zero(gr->b_gate, (size_t)h * r * 2, st), "mlp_bwd: zero");
+    QL_TRY(launch_zero(gr->b_up, (size_t)h * r * 2, st), "mlp_bwd: zero");
+    QL_TRY(launch_zero(gr->b_down, (size_t)d * r * 2, st), "mlp_bwd: zero");
+    return QLORA_OK;
+  }
+  Carver c(ws);
+  MlpBwdWs t;
+  plan_mlp_bwd(c, m, d, h, r, &t);
+  const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
+  const int chunks = colreduce_chunks((int)m);
+  const float s = w->s;
+
+  // LoRA operand layouts
+  QL_TRY(launch_copy2d(w->b_down, 1, r, (int)r, (int)d, t.ltd, d, 1, 0, st), "mlp_bwd: Bd^T");
+  QL_TRY(launch_zero(t.bextdh, (size_t)h * KEd * 2, st), "mlp_bwd: zero");
+  QL_TRY(launch_copy2d(w->a_down, 1, h, (int)h, (int)r, t.bextdh, KEd, 1, 0, st), "mlp_bwd: Ad^T");
+  QL_TRY(launch_copy2d(w->a_down, 1, h, (int)h, (int)r, t.bextdh + r, KEd, 1, 0, st), "mlp_bwd: Ad^T");
+  QL_TRY(launch_zero(t.ltgu, (size_t)2 * r * 2 * h * 2, st), "mlp_bwd: zero");
+  QL_TRY(launch_copy2d(w->b_gate, 1, r, (int)r, (int)h, t.ltgu, 2 * h, 1, 0, st), "mlp_bwd: Bg^T");
+  QL_TRY(launch_copy2d(w->b_up, 1, r, (int)r, (int)h, t.ltgu + r * 2 * h + h, 2 * h, 1, 0, st),
+         "mlp_bwd: Bu^T");
+  QL_TRY(launch_zero(t.bextdx, (size_t)d * KEgu * 2, st), "mlp_bwd: zero");
+  QL_TRY(launch_copy2d(w->a_gate, 1, d, (int)d, (int)r, t.bextdx, KEgu, 1, 0, st), "mlp_bwd: Ag^T");
+  QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
+  QL_TRY(launch_copy2d(w->a_gate, 1, d, (int)d, (int)r, t.bextdx + 2 * r, KEgu, 1, 0, st), "mlp_bwd: Ag^T");
+  QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + 3 * r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
+  // dequantized transposed weights for the two backward GEMMs
+  QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
+         "mlp_bwd: dequant Wd^T");
+  QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, st),
+         "mlp_bwd: dequant Wg^T");
+  QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, st),
+         "mlp_bwd: dequant Wu^T");
+
+  // down projection: Td = dY Bd ; dBd = s dY^T Ud
+  QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
+                       t.textd, KEd, KEd, st),
+         "mlp_bwd: Td");
+  QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, d, (int)m, (int)d, Ud, r, (int)r, t.part, st),
+         "mlp_bwd: dBd partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, gr->b_down, r, 1, st),
+         "mlp_bwd: dBd");
+  // dH = dY Wd + s Td Ad, with dg, du in the epilogue
+  GemmArgs g = gemm_args();
+  g.A = dY; g.lda = d; g.bsrc = BSRC_BF16; g.B = t.wdt; g.ldb = d;
+  g.Ae = t.textd; g.ldae = KEd; g.Be = t.bextdh; g.ldbe = KEd;
+  g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
+  g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
+  QL_TRY(run_gemm(g, r, st), "mlp_bwd: dH GEMM");
+  // dAd = s Td^T H, H recomputed from g, u
+  QL_TRY(launch_colreduce(nullptr, g_save, u_save, w->act, h, (int)m, (int)h, t.td, r, (int)r,
+                          t.part, st),
+         "mlp_bwd: dAd partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->a_down, 1, h, st),
+         "mlp_bwd: dAd");
+  // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)
+  QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s, t.tgu,
+                       nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, st),
+         "mlp_bwd: Tg, Tu");
+  // dBg = s dg^T Ug ; dBu = s du^T Uu
+  QL_TRY(launch_colreduce(t.dgu, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Ug, r, (int)r, t.part, st),
+         "mlp_bwd: dBg partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_gate, r, 1, st),
+         "mlp_bwd: dBg");
+  QL_TRY(launch_colreduce(t.dgu + h, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Uu, r, (int)r,
+                          t.part, st),
+         "mlp_bwd: dBu partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_up, r, 1, st),
+         "mlp_bwd: dBu");
+  // dX = [dg | du] [Wg; Wu] + s [Tg | Tu] [Ag; Au]
+  if (dX) {
+    GemmArgs g2 = gemm_args();
+    g2.A = t.dgu; g2.lda = 2 * h; g2.bsrc = BSRC_BF16; g2.B = t.wgut; g2.ldb = 2 * h;
+    g2.Ae = t.textgu; g2.ldae = KEgu; g2.Be = t.bextdx; g2.ldbe = KEgu;
+    g2.M = (int)m; g2.N = (int)d; g2.K = (int)(2 * h); g2.KE = KEgu;
+    g2.epi = EPI_STORE; g2.C = dX; g2.ldc = d;
+    QL_TRY(run_gemm(g2, 2 * r, st), "mlp_bwd: dX GEMM");
+  }
+  // dAg = s Tg^T X ; dAu = s Tu^T X
+  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),
+                          t.part, st),
+         "mlp_bwd: dAg, dAu partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), 0, (int)r, s, gr->a_gate, 1, d, st),
+         "mlp_bwd: dAg");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), (int)r, (int)r, s, gr->a_up, 1,
+                                 d, st),
+         "mlp_bwd: dAu");
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+void nf4_levels_host(float out[16]);
+
+// ---- NF4 dequant (nf4.hip) ----
+// out[dest_row(i)][j] = W[i][j]; interleave 0: dest_row(i) = i; 1/2: the 32-row
+// interleave of a gate (1) / up (2) pair: 64*(i/32) + 32*(interleave-1) + i%32.
+hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, int64_t n, int64_t k,
+                                   uint16_t* out, int64_t ld_out, int interleave,
+                                   hipStream_t stream);
+// out[j][col_ofs + i] = W[i][j]   (n, k multiples of 64)
+hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, const float* absmax, int64_t n,
+                                        int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
+                                        hipStream_t stream);
+
+// ---- GEMM (gemm.hip) ----
+enum GemmEpilogue {
+  EPI_STORE = 0,     // C bf16 [M][N]
+  EPI_GATEUP = 1,    // columns interleaved by 32 (gate, up); writes g, u, H = act(g) * u
+  EPI_ACT_BWD = 2,   // C = dH [M][h]; reads g, u; writes dgu = [dg | du] [M][2h]
+};
+
+// How the B operand ([N][K] weight, K contiguous) reaches the tile:
+//   bf16 rows, or NF4 codes dequantized while the tile is staged in LDS.
+enum GemmBSource { BSRC_BF16 = 0, BSRC_NF4 = 1, BSRC_NF4_PAIR = 2 };
+
+struct GemmArgs {
+  // main operands: A [M][K] bf16 (lda); B [N][K] bf16 (ldb) or NF4
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  int bsrc;
+  const uint8_t* codes0;   // NF4 of B rows (pair mode: gate rows)
+  const float* absmax0;
+  const uint8_t* codes1;   // pair mode: up rows
+  const float* absmax1;
+  // K-extension: C += Ae [M][KE] * Be [N][KE]^T (KE multiple of 16, may be 0)
+  const uint16_t* Ae;
+  int64_t ldae;
+  const uint16_t* Be;
+  int64_t ldbe;
+  int M, N, K, KE;
+  // epilogue
+  int epi;
+  uint16_t* C;
+  int64_t ldc;
+  uint16_t* g_out;
+  uint16_t* u_out;
+  uint16_t* h_out;
+  const uint16_t* g_in;
+  const uint16_t* u_in;
+  uint16_t* dgu;
+  int64_t hdim;
+  int act;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// ---- LoRA skinny kernels (lora.hip) ----
+// U = G L^T for G [M][K] bf16 (ldg), L [R][K] bf16 (ldl), 1 <= R <= 64.
+// Writes columns j < split to Uf [M][ldu] and j >= split to Uf2 (column
+// j - split) as fp32 (either may be null) and, if Ue is non-null,
+// Ue [M][KE] bf16 = [hi(s U) | lo(s U) | 0 ...] with hi = bf16(sU),
+// lo = bf16(sU - hi), KE = ceil16(2R).
+hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
+                         int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
+                         uint16_t* Ue, int64_t ldue, int KE, hipStream_t stream);
+
+// Column reduction over tokens, first stage: for each chunk c of rows,
+// part[c][col][j] = sum_{i in chunk} G[i][col] * V[i][vofs + j], j < R.
+// G is bf16 [M][C] (ldg) or, when gate/up are given, H = act(g) * u
+// recomputed from bf16 g, u [M][C] (ldg).
+int colreduce_chunks(int M);
+hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint16_t* up, int act,
+                            int64_t ldg, int M, int C, const float* V, int64_t ldv, int R,
+                            float* part, hipStream_t stream);
+// Second stage: out[col * ocs + (j - j0) * ojs] = bf16(s * sum_c part[c][col][j]), j0 <= j < j0+nj.
+hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, int j0, int nj,
+                                   float s, uint16_t* out, int64_t ocs, int64_t ojs,
+                                   hipStream_t stream);
+
+// ---- small layout kernels (lora.hip) ----
+// dst[drow(r) * d_rs + c * d_cs] = src[r * s_rs + c * s_cs] for r < rows, c < cols;
+// drow(r) = r, or the 32-row interleave (as for the dequant) when interleave > 0.
+hipError_t launch_copy2d(const uint16_t* src, int64_t s_rs, int64_t s_cs, int rows, int cols,
+                         uint16_t* dst, int64_t d_rs, int64_t d_cs, int interleave,
+                         hipStream_t stream);
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,130 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+- the built library loads and exports every function include/qlora.h declares;
+- the compiled-in NF4 table equals the oracle's table bit for bit;
+- status strings, workspace queries and argument validation (errors are
+  returned before anything is enqueued).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from qlora_fine_tuning_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from qlora_fine_tuning_amd import build
+        build.build(verbose=False)
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_nf4_table_matches_oracle(L):
+    from oracle import nf4
+    buf = (ctypes.c_float * 16)()
+    L.qlora_nf4_levels(buf)
+    got = np.array(list(buf), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4.nf4_levels().view(np.uint32))
+
+
+def test_status_strings_and_version(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.qlora_status_string(code)
+    assert L.qlora_status_string(12345) == b"unknown status"
+    assert b"gfx950" in L.qlora_version()
+
+
+def test_workspace_queries(L):
+    for mode in (0, 1, 2):
+        assert L.qlora_linear_workspace_bytes(8192, 4096, 4096, 16, mode) > 0
+        assert L.qlora_mlp_workspace_bytes(8192, 4096, 11008, 16, mode) > 0
+    # invalid shapes / ranks / modes give 0
+    assert L.qlora_linear_workspace_bytes(8, 100, 64, 16, 0) == 0
+    assert L.qlora_linear_workspace_bytes(8, 64, 64, 0, 0) == 0
+    assert L.qlora_linear_workspace_bytes(8, 64, 64, 65, 0) == 0
+    assert L.qlora_linear_workspace_bytes(8, 64, 64, 8, 7) == 0
+    assert L.qlora_mlp_workspace_bytes(8, 64, 64, 33, 0) == 0
+    # staged keeps a bf16 copy of the weight, fused does not
+    assert L.qlora_mlp_workspace_bytes(8192, 4096, 11008, 16, 2) >= L.qlora_mlp_workspace_bytes(
+        8192, 4096, 11008, 16, 1)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _nf4(n, k, ok=True):
+    return _lib.Nf4(0x1000 if ok else 0, 0x2000 if ok else 0, n, k)
+
+
+def test_linear_validation_errors(L):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 40
+    f = L.qlora_linear_fwd
+    # null pointer
+    assert f(None, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == -1
+    assert f(FAKE, 8, _nf4(64, 64, ok=False), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == -1
+    # rank / scale / mode
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 0, 1.0, FAKE, None, 0, ws, big, None) == -1
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 65, 1.0, FAKE, None, 0, ws, big, None) == -1
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, float("nan"), FAKE, None, 0, ws, big, None) == -1
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 9, ws, big, None) == -1
+    # shapes: k, n multiples of 64; m >= 0
+    assert f(FAKE, 8, _nf4(64, 96), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == -2
+    assert f(FAKE, 8, _nf4(100, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == -2
+    assert f(FAKE, -1, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == -2
+    # workspace missing / too small / misaligned
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, None, 0, None) == -3
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, 16, None) == -3
+    assert f(FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ctypes.c_void_p(0x100010),
+             big, None) == -3
+    # m == 0 is a no-op that succeeds without touching memory
+    assert f(FAKE, 0, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, None, 0, ws, big, None) == 0
+    b = L.qlora_linear_bwd
+    assert b(FAKE, FAKE, None, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, None, FAKE, FAKE, 0, ws, big,
+             None) == -1
+    assert b(FAKE, FAKE, FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, None, FAKE, FAKE, 0, None, 0,
+             None) == -3
+
+
+def test_mlp_validation_errors(L):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 40
+    w = _lib.MlpWeights(_nf4(128, 64), _nf4(128, 64), _nf4(64, 128), 1, 1, 1, 1, 1, 1, 64, 128, 8,
+                        1.0, 0)
+    f = L.qlora_mlp_fwd
+    args = lambda ww: (FAKE, 8, ctypes.byref(ww), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None)  # noqa: E731
+    bad = _lib.MlpWeights.from_buffer_copy(w)
+    bad.act = 5
+    assert f(*args(bad)) == -1
+    bad = _lib.MlpWeights.from_buffer_copy(w)
+    bad.r = 40
+    assert f(*args(bad)) == -1
+    bad = _lib.MlpWeights.from_buffer_copy(w)
+    bad.down = _nf4(64, 64)          # down must be [d][h]
+    assert f(*args(bad)) == -2
+    bad = _lib.MlpWeights.from_buffer_copy(w)
+    bad.b_up = 0
+    assert f(*args(bad)) == -1
+    assert f(FAKE, 0, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == 0
+    assert f(FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == -1
