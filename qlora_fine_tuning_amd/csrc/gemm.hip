@@ -64,9 +64,10 @@ __constant__ uint32_t c_nf4_levels_gemm[16] = {QLORA_NF4_LEVEL_BITS};
 template <int BSRC, int EPI>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_nt_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * BK];
   __shared__ float lut[16];
+  uint16_t (*sA)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(smem);
+  uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(smem + 2 * BM * BK);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -212,66 +213,107 @@ void gemm_nt_kernel(GemmArgs p) {
 
   // ---- epilogue ----
   // acc[mt][nt][v] holds C[row][col] with
-  //   row = wm*128 + mt*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*128 + nt*32 + lane%32
-  const int rbase = m0 + wm * 128 + 4 * (lane >> 5);
-  const int cbase = n0 + wn * 128 + (lane & 31);
-  if (EPI == EPI_STORE) {
+  //   row = wm*128 + mt*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*128 + nt*32 + lane%32.
+  // Each 32-row slab (one mt) of a wave's 128 x 128 tile goes through LDS
+  // (fp32, padded pitch) so that the global side moves 16 contiguous bytes
+  // per lane; register indices stay compile-time constants.
+  constexpr int SP = 136;  // floats per staged row: 4*SP = 32 mod 64 banks
+  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
+  const int row0 = m0 + wm * 128;
+  const int col0 = n0 + wn * 128;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = cbase + nt * 32;
-        if (col >= p.N) continue;
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + mt * 32 + 8 * (v >> 2) + (v & 3);
-          if (row < p.M) p.C[(int64_t)row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[mt][nt][v]);
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * SP + nt * 32 + (lane & 31)] = acc[mt][nt][v];
+    __syncthreads();
+    if (EPI == EPI_STORE) {
+      // lane: 8 consecutive columns of one row per step, 4 rows per step
+      const int cc = (lane & 15) * 8;
+      for (int q = 0; q < 8; ++q) {
+        const int rr = q * 4 + (lane >> 4);
+        const int row = row0 + mt * 32 + rr;
+        const int col = col0 + cc;
+        const f32x4_t x0 = *(const f32x4_t*)&stage[rr * SP + cc];
+        const f32x4_t x1 = *(const f32x4_t*)&stage[rr * SP + cc + 4];
+        if (row < p.M && col < p.N) {
+          u32x4_t o;
+          o[0] = pack_bf16x2(x0[0], x0[1]);
+          o[1] = pack_bf16x2(x0[2], x0[3]);
+          o[2] = pack_bf16x2(x1[0], x1[1]);
+          o[3] = pack_bf16x2(x1[2], x1[3]);
+          *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
         }
       }
-  } else if (EPI == EPI_GATEUP) {
-    // n-tiles 0/1 and 2/3 of a wave are (gate, up) for the same 32 columns j
+    } else if (EPI == EPI_GATEUP) {
+      // staged columns: [gate j0..j0+31 | up j0.. | gate j0+32.. | up j0+32..]
+      const int jj = (lane & 7) * 8;
+      const int blk = jj >> 5, w = jj & 31;
+      const int64_t j = (int64_t)(col0 >> 1) + jj;
+      for (int q = 0; q < 4; ++q) {
+        const int rr = q * 8 + (lane >> 3);
+        const int row = row0 + mt * 32 + rr;
+        const float* gs = &stage[rr * SP + blk * 64 + w];
+        const float* us = gs + 32;
+        if (row < p.M && col0 < p.N) {
+          u32x4_t og, ou, oh;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+          for (int e = 0; e < 4; ++e) {
+            float hv[2];
+            uint32_t gb[2], ub[2];
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int pcol = n0 + wn * 128 + pr * 64;  // interleaved column of the gate block
-        if (pcol >= p.N) continue;
-        const int64_t j = (int64_t)(pcol >> 1) + (lane & 31);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + mt * 32 + 8 * (v >> 2) + (v & 3);
-          if (row >= p.M) continue;
-          const uint32_t gb = f32_to_bf16(acc[mt][2 * pr][v]);
-          const uint32_t ub = f32_to_bf16(acc[mt][2 * pr + 1][v]);
-          const float hv = act_fwd(p.act, bf16_to_f32(gb)) * bf16_to_f32(ub);
+            for (int t = 0; t < 2; ++t) {
+              gb[t] = f32_to_bf16(gs[2 * e + t]);
+              ub[t] = f32_to_bf16(us[2 * e + t]);
+              hv[t] = act_fwd(p.act, bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
+            }
+            og[e] = gb[0] | (gb[1] << 16);
+            ou[e] = ub[0] | (ub[1] << 16);
+            oh[e] = pack_bf16x2(hv[0], hv[1]);
+          }
           const int64_t o = (int64_t)row * p.hdim + j;
-          p.g_out[o] = (uint16_t)gb;
-          p.u_out[o] = (uint16_t)ub;
-          p.h_out[o] = (uint16_t)f32_to_bf16(hv);
+          *(u32x4_t*)(p.g_out + o) = og;
+          *(u32x4_t*)(p.u_out + o) = ou;
+          *(u32x4_t*)(p.h_out + o) = oh;
         }
       }
-  } else {  // EPI_ACT_BWD: acc = dH
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = cbase + nt * 32;
-        if (col >= p.N) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + mt * 32 + 8 * (v >> 2) + (v & 3);
-          if (row >= p.M) continue;
+    } else {  // EPI_ACT_BWD: staged values are dH
+      const int cc = (lane & 15) * 8;
+      for (int q = 0; q < 8; ++q) {
+        const int rr = q * 4 + (lane >> 4);
+        const int row = row0 + mt * 32 + rr;
+        const int col = col0 + cc;
+        if (row < p.M && col < p.N) {
           const int64_t o = (int64_t)row * p.hdim + col;
-          const float g = bf16_to_f32(p.g_in[o]);
-          const float u = bf16_to_f32(p.u_in[o]);
-          float a, da;
-          act_fwd_bwd(p.act, g, &a, &da);
-          const float dh = acc[mt][nt][v];
+          const u32x4_t gw = *(const u32x4_t*)(p.g_in + o);
+          const u32x4_t uw = *(const u32x4_t*)(p.u_in + o);
+          const float* dh = &stage[rr * SP + cc];
+          u32x4_t odg, odu;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float dg[2], du[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const float g = bf16_to_f32(t ? (gw[e] >> 16) : (gw[e] & 0xFFFFu));
+              const float u = bf16_to_f32(t ? (uw[e] >> 16) : (uw[e] & 0xFFFFu));
+              float a, da;
+              act_fwd_bwd(p.act, g, &a, &da);
+              const float d = dh[2 * e + t];
+              dg[t] = d * u * da;
+              du[t] = d * a;
+            }
+            odg[e] = pack_bf16x2(dg[0], dg[1]);
+            odu[e] = pack_bf16x2(du[0], du[1]);
+          }
           const int64_t od = (int64_t)row * (2 * p.hdim) + col;
-          p.dgu[od] = (uint16_t)f32_to_bf16(dh * u * da);
-          p.dgu[od + p.hdim] = (uint16_t)f32_to_bf16(dh * a);
+          *(u32x4_t*)(p.dgu + od) = odg;
+          *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
         }
       }
+    }
+    __syncthreads();
   }
 }
 
