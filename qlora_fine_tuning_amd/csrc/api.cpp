@@ -70,6 +70,7 @@ struct LinearFwdWs {
   uint16_t* bext;  // [n][KE]
   uint16_t* uext;  // [m][KE]
   uint16_t* wbf;   // [n][k] (staged)
+  float* rpart;    // row-product split partials
 };
 
 size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearFwdWs* w) {
@@ -78,6 +79,7 @@ size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.bext = c.take<uint16_t>(n * KE);
   t.uext = c.take<uint16_t>(m * KE);
   t.wbf = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(n * k) : nullptr;
+  t.rpart = c.take<float>(16 * m * r);
   if (w) *w = t;
   return c.off;
 }
@@ -89,6 +91,7 @@ struct LinearBwdWs {
   uint16_t* text;  // [m][KE]
   float* part;     // [chunks][max(n,k)][r]
   uint16_t* wt;    // [k][n]   dequantized W^T
+  float* rpart;    // row-product split partials
 };
 
 size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, LinearBwdWs* w) {
@@ -101,6 +104,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, Li
   t.text = c.take<uint16_t>(m * KE);
   t.part = c.take<float>(chunks * std::max(n, k) * r);
   t.wt = c.take<uint16_t>(k * n);
+  t.rpart = c.take<float>(16 * m * r);
   if (w) *w = t;
   return c.off;
 }
@@ -115,6 +119,7 @@ struct MlpFwdWs {
   uint16_t* H;       // [m][h]
   uint16_t* wgu;     // [2h][d] staged, 32-row interleave of gate/up
   uint16_t* wd;      // [d][h]  staged
+  float* rpart;      // row-product split partials
 };
 
 size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpFwdWs* w) {
@@ -129,6 +134,7 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   const bool staged = mode == QLORA_DEQUANT_STAGED;
   t.wgu = staged ? c.take<uint16_t>(2 * h * d) : nullptr;
   t.wd = staged ? c.take<uint16_t>(d * h) : nullptr;
+  t.rpart = c.take<float>(16 * m * 2 * r);
   if (w) *w = t;
   return c.off;
 }
@@ -146,6 +152,7 @@ struct MlpBwdWs {
   float* part;       // [chunks][max(d,h)][2r]
   uint16_t* wdt;     // [h][d]
   uint16_t* wgut;    // [d][2h]
+  float* rpart;      // row-product split partials
 };
 
 size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, MlpBwdWs* w) {
@@ -164,6 +171,7 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, MlpBw
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
   t.wdt = c.take<uint16_t>(h * d);
   t.wgut = c.take<uint16_t>(d * 2 * h);
+  t.rpart = c.take<float>(16 * m * 2 * r);
   if (w) *w = t;
   return c.off;
 }
@@ -303,7 +311,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* 
   if (mode == QLORA_DEQUANT_STAGED)
     QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, n, k, t.wbf, k, 0, st), "linear_fwd: dequant");
   QL_TRY(launch_rowdot(X, k, A, k, (int)m, (int)k, (int)r, s, U_save, nullptr, (int)r, r, t.uext,
-                       KE, KE, st),
+                       KE, KE, t.rpart, st),
          "linear_fwd: U = X A^T");
   GemmArgs g = gemm_args();
   g.A = X; g.lda = k;
@@ -345,7 +353,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   QL_TRY(launch_copy2d(A, 1, k, (int)k, (int)r, t.bext + r, KE, 1, 0, st), "linear_bwd: A^T");
   // T = dY B
   QL_TRY(launch_rowdot(dY, n, t.lt, n, (int)m, (int)n, (int)r, s, t.t, nullptr, (int)r, r, t.text,
-                       KE, KE, st),
+                       KE, KE, t.rpart, st),
          "linear_bwd: T = dY B");
   // dB = s dY^T U
   QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, n, (int)m, (int)n, U, r, (int)r, t.part, st),
@@ -430,7 +438,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   }
   // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
   QL_TRY(launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
-                       t.uextgu, KEgu, KEgu, st),
+                       t.uextgu, KEgu, KEgu, t.rpart, st),
          "mlp_fwd: Ug, Uu");
   // gate || up GEMM with the activation epilogue
   GemmArgs g = gemm_args();
@@ -447,7 +455,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
   // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
   QL_TRY(launch_rowdot(t.H, h, w->a_down, h, (int)m, (int)h, (int)r, s, Ud, nullptr, (int)r, r,
-                       t.uextd, KEd, KEd, st),
+                       t.uextd, KEd, KEd, t.rpart, st),
          "mlp_fwd: Ud");
   GemmArgs g2 = gemm_args();
   g2.A = t.H; g2.lda = h;
@@ -514,7 +522,7 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
 
   // down projection: Td = dY Bd ; dBd = s dY^T Ud
   QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
-                       t.textd, KEd, KEd, st),
+                       t.textd, KEd, KEd, t.rpart, st),
          "mlp_bwd: Td");
   QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, d, (int)m, (int)d, Ud, r, (int)r, t.part, st),
          "mlp_bwd: dBd partials");
@@ -535,7 +543,7 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
          "mlp_bwd: dAd");
   // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)
   QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s, t.tgu,
-                       nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, st),
+                       nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
          "mlp_bwd: Tg, Tu");
   // dBg = s dg^T Ug ; dBu = s du^T Uu
   QL_TRY(launch_colreduce(t.dgu, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Ug, r, (int)r, t.part, st),

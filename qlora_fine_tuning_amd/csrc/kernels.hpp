@@ -69,9 +69,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // j - split) as fp32 (either may be null) and, if Ue is non-null,
 // Ue [M][KE] bf16 = [hi(s U) | lo(s U) | 0 ...] with hi = bf16(sU),
 // lo = bf16(sU - hi), KE = ceil16(2R).
+// part: scratch of rowdot_splits(M, K) * M * R floats.
+int rowdot_splits(int M, int K);
 hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
                          int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
-                         uint16_t* Ue, int64_t ldue, int KE, hipStream_t stream);
+                         uint16_t* Ue, int64_t ldue, int KE, float* part, hipStream_t stream);
 
 // Column reduction over tokens, first stage: for each chunk c of rows,
 // part[c][col][j] = sum_{i in chunk} G[i][col] * V[i][vofs + j], j < R.

@@ -7,14 +7,15 @@
 // these read one large bf16 operand once (X, dY, H, dg|du: 2 B per element)
 // and are bound by HBM bandwidth, not by arithmetic.
 //
-//  rowdot     : U = G L^T  ([M][K] x [R][K]^T -> [M][R]) on MFMA 16x16x32 with
-//               operand fragments loaded straight from global memory; K split
-//               across the 8 waves of a block, partials summed in LDS in a
-//               fixed order. Also emits the K-extension operand of the big
-//               GEMM: [hi(sU) | lo(sU)] in bf16.
-//  colreduce  : part[c][col][j] = sum_{i in chunk c} G[i][col] V[i][j]; each
-//               lane owns two columns, V's row is wave-uniform (scalar loads).
-//               G may be H = act(g) * u recomputed on the fly from g, u.
+//  rowdot     : U = G L^T  ([M][K] x [R][K]^T -> [M][R]) on MFMA 16x16x32;
+//               64-row x 128-column tiles of G and L reach LDS by direct
+//               loads in a 3-deep ring; K is split over blocks and the
+//               partials are summed in a fixed order by a finish pass, which
+//               also emits the K-extension operand of the big GEMM:
+//               [hi(sU) | lo(sU)] in bf16.
+//  colreduce  : part[c][col][j] = sum_{i in chunk c} G[i][col] V[i][j] on MFMA
+//               (G^T as the row operand via 2-byte LDS gathers, V as bf16
+//               hi + lo). G may be H = act(g) * u recomputed from g, u.
 //  finish     : fixed-order sum over chunks, scale, bf16, any output stride.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -22,95 +23,186 @@
 namespace qlora {
 
 // ------------------------------------------------------------------ rowdot --
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int RD_ROWS = 64, RD_KT = 128, RD_STAGES = 3;
+
+// element offset of (row, 16-byte chunk) in a [rows][128] bf16 tile: 16
+// chunks per 256-byte row, XOR-swizzled by row so the 16 lanes of a fragment
+// read (16 rows, one chunk) hit 16 different bank groups.
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * RD_KT + ((chunk ^ (row & 15)) << 3); }
+
+}  // namespace
+
+int rowdot_splits(int M, int K) {
+  const int blocks = (M + RD_ROWS - 1) / RD_ROWS;
+  int ns = (1024 + blocks - 1) / blocks;
+  const int kmax = (K + RD_KT - 1) / RD_KT;
+  if (ns > kmax) ns = kmax;
+  if (ns > 16) ns = 16;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+// part[split][i][j] = sum over the split's K range of G[i][k] * L[j][k].
+// 64 rows x 128 K per step, staged by direct-to-LDS loads in a 3-deep ring;
+// wave w owns rows 16w..16w+15 and all RT*16 columns (MFMA 16x16x32).
 template <int RT>
-__global__ __launch_bounds__(512) void rowdot_kernel(const uint16_t* __restrict__ G, int64_t ldg,
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ G, int64_t ldg,
                                                      const uint16_t* __restrict__ L, int64_t ldl,
-                                                     int M, int K, int R, float s,
-                                                     float* __restrict__ Uf,
-                                                     float* __restrict__ Uf2, int split,
-                                                     int64_t ldu, uint16_t* __restrict__ Ue,
-                                                     int64_t ldue, int KE) {
-  constexpr int RW = RT * 16;
-  __shared__ float red[8][16][RW + 1];
+                                                     int M, int K, int R, int kper,
+                                                     float* __restrict__ part) {
+  constexpr int GB = RD_ROWS * RD_KT * 2;     // G tile bytes
+  constexpr int LB = RT * 16 * RD_KT * 2;     // L tile bytes
+  constexpr int STAGE = GB + LB;
+  constexpr int NL = 4 + RT;                  // DMA instructions per stage per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RD_STAGES * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = blockIdx.x * 16;
-  const int nsteps = K >> 5;
-  const int per = (nsteps + 7) >> 3;
-  const int s0 = wave * per;
-  const int s1 = min(nsteps, s0 + per);
-  const int row = min(i0 + (lane & 15), M - 1);
-  const int kq = (lane >> 4) * 8;
-  const uint16_t* gp = G + (int64_t)row * ldg + kq;
-  const uint16_t* lp[RT];
-  bool lv[RT];
+  const int r0 = blockIdx.x * RD_ROWS;
+  const int kbeg = blockIdx.y * kper;
+  const int kend = min(K, kbeg + kper);
+  const int nst = (kend - kbeg + RD_KT - 1) / RD_KT;
+
+  const uint16_t* srcG[4];
+  int chG[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int row = slot >> 4, chunk = (slot & 15) ^ (row & 15);
+    srcG[j] = G + (int64_t)min(r0 + row, M - 1) * ldg;
+    chG[j] = chunk * 8;
+  }
+  const uint16_t* srcL[RT];
+  int chL[RT];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    const int slot = (wave * RT + j) * 64 + lane;
+    const int row = slot >> 4, chunk = (slot & 15) ^ (row & 15);
+    srcL[j] = L + (int64_t)min(row, R - 1) * ldl;
+    chL[j] = chunk * 8;
+  }
+
+  auto issue = [&](int st) {
+    uint8_t* b = smem + (st % RD_STAGES) * STAGE;
+    const int k0 = kbeg + st * RD_KT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = (k0 + chG[j] < kend) ? k0 + chG[j] : kbeg;  // past the end: any valid column
+      dma16(srcG[j] + k, b + (wave * 4 + j) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const int k = (k0 + chL[j] < kend) ? k0 + chL[j] : kbeg;
+      dma16(srcL[j] + k, b + GB + (wave * RT + j) * 1024);
+    }
+  };
+
   f32x4_t acc[RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int j = t * 16 + (lane & 15);
-    lv[t] = j < R;
-    lp[t] = L + (int64_t)min(j, R - 1) * ldl + kq;
-    acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-#pragma unroll 4
-  for (int st = s0; st < s1; ++st) {
-    const int k0 = st * 32;
-    const bf16x8_t a = *(const bf16x8_t*)(gp + k0);
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int g = lane >> 4, m = lane & 15;
+
+  const int npro = min(RD_STAGES - 1, nst);
+  for (int st = 0; st < npro; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) wait_vm_lgkm0<NL>();   // this wave's stage st landed
+    else wait_vm_lgkm0<0>();
+    raw_barrier();
+    if (st + RD_STAGES - 1 < nst) issue(st + RD_STAGES - 1);
+    const uint16_t* sg = (const uint16_t*)(smem + (st % RD_STAGES) * STAGE);
+    const uint16_t* sl = (const uint16_t*)(smem + (st % RD_STAGES) * STAGE + GB);
+    const int nsub = min(RD_KT, kend - (kbeg + st * RD_KT)) >> 5;
+    for (int ks = 0; ks < nsub; ++ks) {
+      const bf16x8_t a = *(const bf16x8_t*)&sg[rswz(wave * 16 + m, 4 * ks + g)];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      bf16x8_t b = *(const bf16x8_t*)(lp[t] + k0);
-      if (!lv[t]) b = bf16x8_t{};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+      for (int t = 0; t < RT; ++t) {
+        const bf16x8_t b = *(const bf16x8_t*)&sl[rswz(t * 16 + m, 4 * ks + g)];
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+      }
     }
   }
-  // acc[t][v] = partial U[i0 + 4*(lane/16) + v][t*16 + lane%16]
+  // acc[t][v] = partial U[r0 + 16*wave + 4*g + v][t*16 + m]
+  float* out = part + (int64_t)blockIdx.y * M * R;
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][t * 16 + (lane & 15)] = acc[t][v];
-  __syncthreads();
-  for (int e = tid; e < 16 * RW; e += 512) {
-    const int i = e / RW, j = e - (e / RW) * RW;
-    const int gi = i0 + i;
-    if (gi >= M || j >= R) continue;
+    for (int v = 0; v < 4; ++v) {
+      const int row = r0 + wave * 16 + 4 * g + v;
+      const int j = t * 16 + m;
+      if (row < M && j < R) out[(int64_t)row * R + j] = acc[t][v];
+    }
+}
+
+// U = sum of the split partials (fixed order); writes fp32 U (split across
+// two outputs at column `split`) and the bf16 K-extension operand.
+__global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restrict__ part,
+                                                            int nsplit, int M, int R, float s,
+                                                            float* __restrict__ Uf,
+                                                            float* __restrict__ Uf2, int split,
+                                                            int64_t ldu, uint16_t* __restrict__ Ue,
+                                                            int64_t ldue, int KE) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int W = KE > R ? KE : R;
+  if (e >= (int64_t)M * W) return;
+  const int i = (int)(e / W), j = (int)(e - (int64_t)i * W);
+  if (j < R) {
     float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) sum += red[w][i][j];
+    for (int q = 0; q < nsplit; ++q) sum += part[((int64_t)q * M + i) * R + j];
     if (j < split) {
-      if (Uf) Uf[(int64_t)gi * ldu + j] = sum;
+      if (Uf) Uf[(int64_t)i * ldu + j] = sum;
     } else if (Uf2) {
-      Uf2[(int64_t)gi * ldu + (j - split)] = sum;
+      Uf2[(int64_t)i * ldu + (j - split)] = sum;
     }
     if (Ue) {
       const float su = s * sum;
       const uint32_t hi = f32_to_bf16(su);
-      const float lo = su - bf16_to_f32(hi);
-      Ue[(int64_t)gi * ldue + j] = (uint16_t)hi;
-      Ue[(int64_t)gi * ldue + R + j] = (uint16_t)f32_to_bf16(lo);
+      Ue[(int64_t)i * ldue + j] = (uint16_t)hi;
+      Ue[(int64_t)i * ldue + R + j] = (uint16_t)f32_to_bf16(su - bf16_to_f32(hi));
     }
-  }
-  if (Ue) {
-    const int pad = KE - 2 * R;
-    for (int e = tid; e < 16 * pad; e += 512) {
-      const int i = e / pad, j = 2 * R + (e - (e / pad) * pad);
-      const int gi = i0 + i;
-      if (gi < M) Ue[(int64_t)gi * ldue + j] = 0;
-    }
+  } else if (Ue && j >= 2 * R && j < KE) {
+    Ue[(int64_t)i * ldue + j] = 0;
   }
 }
 
 hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
                          int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
-                         uint16_t* Ue, int64_t ldue, int KE, hipStream_t stream) {
+                         uint16_t* Ue, int64_t ldue, int KE, float* part, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  dim3 grid((unsigned)((M + 15) / 16)), block(512);
-  const int rt = (R + 15) / 16;
-  switch (rt) {
-    case 1: rowdot_kernel<1><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE); break;
-    case 2: rowdot_kernel<2><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE); break;
-    case 3: rowdot_kernel<3><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE); break;
-    case 4: rowdot_kernel<4><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE); break;
-    default: return hipErrorInvalidValue;
+  if (R < 1 || R > 64 || K % 64) return hipErrorInvalidValue;
+  const int ns = rowdot_splits(M, K);
+  int kper = (K + ns - 1) / ns;
+  kper = (kper + RD_KT - 1) / RD_KT * RD_KT;
+  const int nsplit = (K + kper - 1) / kper;
+  dim3 grid((unsigned)((M + RD_ROWS - 1) / RD_ROWS), (unsigned)nsplit), block(256);
+  switch ((R + 15) / 16) {
+    case 1: rowdot_kernel<1><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
+    case 2: rowdot_kernel<2><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
+    case 3: rowdot_kernel<3><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
+    case 4: rowdot_kernel<4><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int W = KE > R ? KE : R;
+  const int64_t total = (int64_t)M * W;
+  rowdot_finish_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
+      part, nsplit, M, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE);
   return hipGetLastError();
 }
 
@@ -122,6 +214,16 @@ int colreduce_chunks(int M) {
   return c;
 }
 
+// part[chunk][col][j] = sum over the chunk's rows i of G[i][col] * V[i][j].
+// MFMA 16x16x32 with D[col][j] = sum_k G^T[col][k] V[k][j]: a block owns 256
+// columns and walks its rows 32 at a time. The 32 x 256 G tile is staged in
+// LDS with a 544-byte row pitch; lane group g = lane/16 takes rows 4t + g
+// (t = 0..7) of the step as its 8 K-elements (a fixed permutation of K, used
+// for both operands), so each 2-byte gather of a fragment hits 4 distinct
+// 32-byte bank groups. V is split into bf16 hi + lo (V - hi) halves, stored
+// transposed and permuted, so its fragments are single 16-byte LDS reads;
+// hi and lo are accumulated by two MFMAs into the same fp32 sum.
+// HMODE: G = H = bf16(act(g) * u), recomputed from g and u.
 template <int RT, bool HMODE>
 __global__ __launch_bounds__(256) void colreduce_kernel(const uint16_t* __restrict__ G,
                                                         const uint16_t* __restrict__ gate,
@@ -130,55 +232,131 @@ __global__ __launch_bounds__(256) void colreduce_kernel(const uint16_t* __restri
                                                         const float* __restrict__ V, int64_t ldv,
                                                         int R, int rows_per_chunk,
                                                         float* __restrict__ part) {
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 2;
+  constexpr int CT = 256, KS = 32, PITCH = 544;
+  __shared__ __attribute__((aligned(16))) uint8_t gt[2][KS * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][2][RT * 16][KS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * CT;
   const int chunk = blockIdx.y;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(M, r0 + rows_per_chunk);
-  const bool valid = c < C;
-  const int cc = valid ? c : 0;
-  float acc0[RT], acc1[RT];
+  const int nsteps = (r1 - r0 + KS - 1) / KS;
+
+  // padding columns j >= R of the V tiles stay zero
+  for (int e = tid; e < 2 * 2 * RT * 16 * KS; e += 256) (&vt[0][0][0][0])[e] = 0;
+
+  // G tile loads: 32 rows x 32 chunks of 16 B; thread t takes chunks t + 256 q
+  constexpr int NV = 2 * RT;  // V values per thread per step (32 rows x RT*16 cols)
+  u32x4_t rg[4];
+  u32x4_t ru[HMODE ? 4 : 1];
+  float rv[NV];
+  auto load = [&](int st) {
+    const int rbase = r0 + st * KS;
 #pragma unroll
-  for (int j = 0; j < RT; ++j) acc0[j] = acc1[j] = 0.0f;
-  for (int i = r0; i < r1; ++i) {
-    float x0, x1;
-    if (HMODE) {
-      const uint32_t gw = *(const uint32_t*)(gate + (int64_t)i * ldg + cc);
-      const uint32_t uw = *(const uint32_t*)(up + (int64_t)i * ldg + cc);
-      const float h0 = act_fwd(act, bf16_to_f32(gw & 0xFFFFu)) * bf16_to_f32(uw & 0xFFFFu);
-      const float h1 = act_fwd(act, bf16_to_f32(gw >> 16)) * bf16_to_f32(uw >> 16);
-      x0 = bf16_to_f32(f32_to_bf16(h0));
-      x1 = bf16_to_f32(f32_to_bf16(h1));
-    } else {
-      const uint32_t w = *(const uint32_t*)(G + (int64_t)i * ldg + cc);
-      x0 = bf16_to_f32(w & 0xFFFFu);
-      x1 = bf16_to_f32(w >> 16);
-    }
-    const float* vr = V + (int64_t)i * ldv;
-#pragma unroll
-    for (int j = 0; j < RT; ++j) {
-      if (j < R) {
-        const float vj = vr[j];
-        acc0[j] = fmaf(x0, vj, acc0[j]);
-        acc1[j] = fmaf(x1, vj, acc1[j]);
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      const int row = min(rbase + (idx >> 5), M - 1);
+      const int col = min(c0 + (idx & 31) * 8, C - 8);
+      if (HMODE) {
+        rg[q] = *(const u32x4_t*)(gate + (int64_t)row * ldg + col);
+        ru[q] = *(const u32x4_t*)(up + (int64_t)row * ldg + col);
+      } else {
+        rg[q] = *(const u32x4_t*)(G + (int64_t)row * ldg + col);
       }
     }
-  }
-  if (valid) {
-    float* o = part + ((int64_t)chunk * C + c) * R;
-    for (int j = 0; j < R && j < RT; ++j) {
-      o[j] = acc0[j];
-      o[R + j] = acc1[j];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int idx = tid + 256 * q;
+      const int row = rbase + idx / R;
+      rv[q] = (idx < KS * R && row < r1) ? V[(int64_t)row * ldv + idx % R] : 0.0f;
     }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      u32x4_t v = rg[q];
+      if (HMODE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float h0 = act_fwd(act, bf16_to_f32(rg[q][e] & 0xFFFFu)) * bf16_to_f32(ru[q][e] & 0xFFFFu);
+          const float h1 = act_fwd(act, bf16_to_f32(rg[q][e] >> 16)) * bf16_to_f32(ru[q][e] >> 16);
+          v[e] = pack_bf16x2(h0, h1);
+        }
+      }
+      *(u32x4_t*)&gt[buf][(idx >> 5) * PITCH + (idx & 31) * 16] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < KS * R) {
+        const int row = idx / R, j = idx % R;
+        const int pp = 8 * (row & 3) + (row >> 2);
+        const uint32_t hi = f32_to_bf16(rv[q]);
+        vt[buf][0][j][pp] = (uint16_t)hi;
+        vt[buf][1][j][pp] = (uint16_t)f32_to_bf16(rv[q] - bf16_to_f32(hi));
+      }
+    }
+  };
+
+  f32x4_t acc[4][RT];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) acc[ct][jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int g = lane >> 4, m = lane & 15;
+  if (nsteps > 0) {
+    load(0);
+    __syncthreads();  // zero-fill of vt done before the first store
+    store(0);
+    __syncthreads();
   }
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) load(st + 1);
+    bf16x8_t bh[RT], bl[RT];
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) {
+      bh[jt] = *(const bf16x8_t*)&vt[buf][0][jt * 16 + m][8 * g];
+      bl[jt] = *(const bf16x8_t*)&vt[buf][1][jt * 16 + m][8 * g];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const uint8_t* base = &gt[buf][(wave * 64 + ct * 16 + m) * 2];
+      bf16x8_t a;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a[t] = *(const __bf16*)(base + (4 * t + g) * PITCH);
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        acc[ct][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[jt], acc[ct][jt], 0, 0, 0);
+        acc[ct][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[jt], acc[ct][jt], 0, 0, 0);
+      }
+    }
+    if (st + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+  // acc[ct][jt][v] = part for column c0 + wave*64 + ct*16 + 4*g + v, j = jt*16 + m
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int col = c0 + wave * 64 + ct * 16 + 4 * g + v;
+        const int j = jt * 16 + m;
+        if (col < C && j < R) part[((int64_t)chunk * C + col) * R + j] = acc[ct][jt][v];
+      }
 }
 
 hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint16_t* up, int act,
                             int64_t ldg, int M, int C, const float* V, int64_t ldv, int R,
                             float* part, hipStream_t stream) {
   if (M <= 0 || C <= 0) return hipSuccess;
+  if (R < 1 || R > 64 || C % 8) return hipErrorInvalidValue;
   const int chunks = colreduce_chunks(M);
   const int rpc = (M + chunks - 1) / chunks;
-  dim3 grid((unsigned)((C + 511) / 512), (unsigned)chunks), block(256);
+  dim3 grid((unsigned)((C + 255) / 256), (unsigned)chunks), block(256);
   const bool hm = gate != nullptr;
 #define QL_CR(RTV)                                                                              \
   do {                                                                                          \
@@ -189,11 +367,9 @@ hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint1
       colreduce_kernel<RTV, false><<<grid, block, 0, stream>>>(G, gate, up, act, ldg, M, C, V,  \
                                                                ldv, R, rpc, part);              \
   } while (0)
-  if (R <= 8) QL_CR(8);
-  else if (R <= 16) QL_CR(16);
-  else if (R <= 32) QL_CR(32);
-  else if (R <= 64) QL_CR(64);
-  else return hipErrorInvalidValue;
+  if (R <= 16) QL_CR(1);
+  else if (R <= 32) QL_CR(2);
+  else QL_CR(4);
 #undef QL_CR
   return hipGetLastError();
 }
