@@ -94,7 +94,7 @@ struct LinearBwdWs {
   float* rpart;    // row-product split partials
 };
 
-size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, LinearBwdWs* w) {
+size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearBwdWs* w) {
   const int64_t KE = ceil16(2 * r);
   const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
   LinearBwdWs t;
@@ -103,7 +103,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, Li
   t.t = c.take<float>(m * r);
   t.text = c.take<uint16_t>(m * KE);
   t.part = c.take<float>(chunks * std::max(n, k) * r);
-  t.wt = c.take<uint16_t>(k * n);
+  t.wt = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
   if (w) *w = t;
   return c.off;
@@ -155,7 +155,7 @@ struct MlpBwdWs {
   float* rpart;      // row-product split partials
 };
 
-size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, MlpBwdWs* w) {
+size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpBwdWs* w) {
   const int64_t KEgu = ceil16(4 * r), KEd = ceil16(2 * r);
   const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
   MlpBwdWs t;
@@ -169,8 +169,9 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, MlpBw
   t.tgu = c.take<float>(m * 2 * r);
   t.textgu = c.take<uint16_t>(m * KEgu);
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
-  t.wdt = c.take<uint16_t>(h * d);
-  t.wgut = c.take<uint16_t>(d * 2 * h);
+  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  t.wdt = staged ? c.take<uint16_t>(h * d) : nullptr;
+  t.wgut = staged ? c.take<uint16_t>(d * 2 * h) : nullptr;
   t.rpart = c.take<float>(16 * m * 2 * r);
   if (w) *w = t;
   return c.off;
@@ -285,7 +286,7 @@ size_t qlora_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r, 
   if (!dims_ok(m, k, n) || r < 1 || r > 64 || !valid_mode(mode)) return 0;
   mode = resolve_mode(mode);
   Carver a(nullptr), b(nullptr);
-  return std::max(plan_linear_fwd(a, m, k, n, r, mode, nullptr), plan_linear_bwd(b, m, k, n, r, nullptr));
+  return std::max(plan_linear_fwd(a, m, k, n, r, mode, nullptr), plan_linear_bwd(b, m, k, n, r, mode, nullptr));
 }
 
 int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* A,
@@ -343,7 +344,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   }
   Carver c(ws);
   LinearBwdWs t;
-  plan_linear_bwd(c, m, k, n, r, &t);
+  plan_linear_bwd(c, m, k, n, r, mode, &t);
   const int KE = (int)ceil16(2 * r);
   const int chunks = colreduce_chunks((int)m);
 
@@ -362,10 +363,15 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
          "linear_bwd: dB");
   // dX = dY W + s T A
   if (dX) {
-    QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
-           "linear_bwd: dequant W^T");
     GemmArgs g = gemm_args();
-    g.A = dY; g.lda = n; g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = n;
+    g.A = dY; g.lda = n;
+    if (mode == QLORA_DEQUANT_STAGED) {
+      QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
+             "linear_bwd: dequant W^T");
+      g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = n;
+    } else {
+      g.bsrc = BSRC_NF4_T; g.codes0 = w.codes; g.absmax0 = w.absmax;
+    }
     g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
     g.M = (int)m; g.N = (int)k; g.K = (int)n; g.KE = KE;
     g.epi = EPI_STORE; g.C = dX; g.ldc = k;
@@ -399,7 +405,7 @@ size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int
   if (!dims_ok(m, d, h) || r < 1 || r > 32 || !valid_mode(mode)) return 0;
   mode = resolve_mode(mode);
   Carver a(nullptr), b(nullptr);
-  return std::max(plan_mlp_fwd(a, m, d, h, r, mode, nullptr), plan_mlp_bwd(b, m, d, h, r, nullptr));
+  return std::max(plan_mlp_fwd(a, m, d, h, r, mode, nullptr), plan_mlp_bwd(b, m, d, h, r, mode, nullptr));
 }
 
 int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint16_t* Y,
@@ -493,7 +499,7 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   }
   Carver c(ws);
   MlpBwdWs t;
-  plan_mlp_bwd(c, m, d, h, r, &t);
+  plan_mlp_bwd(c, m, d, h, r, mode, &t);
   const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
   const int chunks = colreduce_chunks((int)m);
   const float s = w->s;
@@ -512,13 +518,16 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
   QL_TRY(launch_copy2d(w->a_gate, 1, d, (int)d, (int)r, t.bextdx + 2 * r, KEgu, 1, 0, st), "mlp_bwd: Ag^T");
   QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + 3 * r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
-  // dequantized transposed weights for the two backward GEMMs
-  QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
-         "mlp_bwd: dequant Wd^T");
-  QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, st),
-         "mlp_bwd: dequant Wg^T");
-  QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, st),
-         "mlp_bwd: dequant Wu^T");
+  // staged mode: dequantized transposed weights for the two backward GEMMs
+  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  if (staged) {
+    QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
+           "mlp_bwd: dequant Wd^T");
+    QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, st),
+           "mlp_bwd: dequant Wg^T");
+    QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, st),
+           "mlp_bwd: dequant Wu^T");
+  }
 
   // down projection: Td = dY Bd ; dBd = s dY^T Ud
   QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
@@ -530,7 +539,9 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
          "mlp_bwd: dBd");
   // dH = dY Wd + s Td Ad, with dg, du in the epilogue
   GemmArgs g = gemm_args();
-  g.A = dY; g.lda = d; g.bsrc = BSRC_BF16; g.B = t.wdt; g.ldb = d;
+  g.A = dY; g.lda = d;
+  if (staged) { g.bsrc = BSRC_BF16; g.B = t.wdt; g.ldb = d; }
+  else { g.bsrc = BSRC_NF4_T; g.codes0 = w->down.codes; g.absmax0 = w->down.absmax; }
   g.Ae = t.textd; g.ldae = KEd; g.Be = t.bextdh; g.ldbe = KEd;
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
@@ -558,7 +569,14 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   // dX = [dg | du] [Wg; Wu] + s [Tg | Tu] [Ag; Au]
   if (dX) {
     GemmArgs g2 = gemm_args();
-    g2.A = t.dgu; g2.lda = 2 * h; g2.bsrc = BSRC_BF16; g2.B = t.wgut; g2.ldb = 2 * h;
+    g2.A = t.dgu; g2.lda = 2 * h;
+    if (staged) { g2.bsrc = BSRC_BF16; g2.B = t.wgut; g2.ldb = 2 * h; }
+    else {
+      g2.bsrc = BSRC_NF4_T;
+      g2.codes0 = w->gate.codes; g2.absmax0 = w->gate.absmax;
+      g2.codes1 = w->up.codes; g2.absmax1 = w->up.absmax;
+      g2.ksplit = (int)h;
+    }
     g2.Ae = t.textgu; g2.ldae = KEgu; g2.Be = t.bextdx; g2.ldbe = KEgu;
     g2.M = (int)m; g2.N = (int)d; g2.K = (int)(2 * h); g2.KE = KEgu;
     g2.epi = EPI_STORE; g2.C = dX; g2.ldc = d;

@@ -11,18 +11,23 @@
 //
 // Tiling: 256 x 256 output tile per workgroup of 8 waves (2 per SIMD) laid
 // out 2 x 4, each wave 128 x 64 = 4 x 2 MFMA 32x32x16 tiles (128 fp32
-// accumulators per lane). Two waves per SIMD let one wave's LDS or barrier
-// wait be covered by the other's matrix work. K is walked in 32-wide steps
-// through a 4-deep LDS ring (4 x 32 KB of the 160 KB per CU) filled by
-// direct-to-LDS loads (global_load_lds_dwordx4) issued three steps ahead, so
-// operands never pass through VGPRs. LDS rows are 64 B; the 16-byte chunk
-// index is XOR-swizzled with ((row >> 1) ^ (row >> 3)) & 3, which keeps
-// every 16-lane phase of a ds_read_b128 fragment load (and every 8-lane one)
-// on distinct banks.
+// accumulators per lane). K is walked in 64-wide steps through a 2-deep LDS
+// ring filled by direct-to-LDS loads (global_load_lds_dwordx4): operands
+// never pass through VGPRs and every row request covers a full 128-byte
+// line. LDS rows are 128 B; the 16-byte chunk index is XOR-swizzled with
+// (row >> 1) & 7 so each 16-lane phase of a ds_read_b128 fragment load hits
+// 16 different bank groups. Fragments of the next substep are read while the
+// matrix cores work on the current one, across the stage barrier too.
 //
-// Weight operand B comes either as bf16 rows or as NF4 codes that are
-// dequantized while the tile is staged into LDS (one weight row per thread,
-// 64 weights = exactly one absmax block per K-step).
+// A 256 x 256 tile with bf16 operands needs 64 KB of operands per 64-wide
+// k-step, which at full matrix rate exceeds what L2 can feed a CU. With NF4
+// weights (B) the feed carries the 4-bit codes and the fp32 absmax instead
+// (8 KB + 1 KB per step instead of 32 KB); the block dequantizes the next
+// step's codes in LDS, bf16_rne(fp32_rne(level[code] * absmax)) exactly as
+// the standalone dequant, while its matrix cores work on the current step.
+// BSRC_NF4_T reads the weight transposed (the backward dX = dY W): the tile's
+// rows are input features, its K runs over output features, and the dequant
+// writes the transposed bf16 tile.
 //
 // Tile order: workgroup ids are dealt to the 8 XCDs round-robin; ids are
 // remapped so that each XCD walks a contiguous range of tiles, grouped 8
@@ -35,23 +40,21 @@ namespace qlora {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 512, NWAVE = 8;
-constexpr int NSTAGE = 4;          // LDS ring depth
-constexpr int PREF = NSTAGE - 1;   // k-tiles in flight ahead of the one computed
+constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
+constexpr int NSTAGE = 2;
 
-// Per-stage LDS layout (bytes): A [256][32] bf16, B [256][32] bf16, then (NF4
-// modes) the raw codes [256][16 B] and one fp32 absmax per B row.
+// Per-stage LDS layout (bytes): A [256][64] bf16, B [256][64] bf16, then (NF4
+// modes) the raw codes of the step (8 KB) and 256 fp32 absmax (+ a spare copy).
 constexpr int A_BYTES = BM * BK * 2;
 constexpr int B_BYTES = BN * BK * 2;
-constexpr int C_BYTES = BN * 16;
-constexpr int S_BYTES = BN * 4;
+constexpr int C_BYTES = 8192;
+constexpr int S_BYTES = 2048;
 constexpr int STAGE_BF16 = A_BYTES + B_BYTES;
 constexpr int STAGE_NF4 = A_BYTES + B_BYTES + C_BYTES + S_BYTES;
 
-// element offset of (row, 16-byte chunk) in a [rows][32] bf16 LDS tile; see
-// the swizzle note above.
+// element offset of (row, 16-byte chunk) in a [rows][64] bf16 LDS tile
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 3);
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 __device__ __forceinline__ int xcd_remap(int pid, int n) {
@@ -72,6 +75,14 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
 }
 
+// LDS store the compiler does not track: it is not ordered against the DMA
+// still in flight to other LDS regions (the compiler would otherwise wait for
+// all of them). Completion is covered by the lgkmcnt(0) of wait_vm<>.
+__device__ __forceinline__ void lds_store16(void* p, u32x4_t v) {
+  const uint32_t off = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+  asm volatile("ds_write_b128 %0, %1" : : "v"(off), "v"(v) : "memory");
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding and
 // all of its LDS operations are done (expcnt left unconstrained).
 // gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14, expcnt[6:4], lgkmcnt[11:8].
@@ -82,33 +93,14 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would wait for every DMA in flight (vmcnt(0)) and drain the LDS ring. The
-// waves wait for their own DMA stage with wait_vm<> first, so after the
-// barrier every wave's data for that stage is in LDS. The empty asm keeps the
-// compiler from moving LDS accesses across the barrier.
+// would wait for every DMA in flight (vmcnt(0)). Waves wait for their own
+// DMA with wait_vm<> first, so after the barrier every wave's data for that
+// stage is in LDS. The empty asm keeps the compiler from moving LDS accesses
+// across the barrier.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-template <int L>
-__device__ __forceinline__ void wait_vm_stages(int later) {
-  if (later >= 2) wait_vm<2 * L>();
-  else if (later == 1) wait_vm<L>();
-  else wait_vm<0>();
-}
-
-__device__ __forceinline__ u32x4_t dq8(uint32_t word, float amax, const float* lut) {
-  u32x4_t o;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    uint32_t byte = (word >> (8 * b)) & 0xFFu;
-    float w0 = lut[byte >> 4] * amax;
-    float w1 = lut[byte & 0xFu] * amax;
-    o[b] = pack_bf16x2(w0, w1);
-  }
-  return o;
 }
 
 }  // namespace
@@ -120,9 +112,8 @@ __global__ __launch_bounds__(NTHR)
 void gemm_nt_kernel(GemmArgs p) {
   constexpr bool NF4 = BSRC != BSRC_BF16;
   constexpr int STAGE = NF4 ? STAGE_NF4 : STAGE_BF16;
-  constexpr int L = NF4 ? 3 : 4;  // DMA instructions per stage per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
-  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE + (NF4 ? 64 : 0)];
+  float* lut = reinterpret_cast<float*>(smem + NSTAGE * STAGE);  // NF4 only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -151,111 +142,224 @@ void gemm_nt_kernel(GemmArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // ---- per-lane DMA sources (row and swizzled chunk fixed; k advances) ----
-  // Tile A/B: wave w, instruction j fills LDS slots (w*2 + j)*64 + lane of
-  // the [256][4 x 16 B] tile; slot -> (row, physical chunk) -> logical chunk.
-  const uint16_t* srcA[2];
-  const uint16_t* srcB[2];
+  // A/B tile: wave w, instruction j fills LDS slots (w*4 + j)*64 + lane of the
+  // [256][8 x 16 B] tile; slot -> (row, physical chunk) -> logical chunk.
+  const uint16_t* srcA[4];
+  const uint16_t* srcB[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int slot = (wave * 2 + j) * 64 + lane;
-    const int row = slot >> 2, phys = slot & 3;
-    const int chunk = phys ^ (((row >> 1) ^ (row >> 3)) & 3);
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int row = slot >> 3, phys = slot & 7;
+    const int chunk = phys ^ ((row >> 1) & 7);
     srcA[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + chunk * 8;
     if (!NF4) srcB[j] = p.B + (int64_t)min(n0 + row, p.N - 1) * p.ldb + chunk * 8;
   }
-  // NF4: waves 0-3 move the 16 code bytes of B rows w*64 + lane, waves 4-7
-  // the absmax of B rows (w-4)*64 + lane, one k-tile per stage.
+  // NF4 raw data of one k-step: 8 KB of codes + 256 absmax; wave w moves one
+  // 1 KB piece of codes and one 256 B piece of absmax (waves 4-7 duplicate
+  // the absmax pieces of waves 0-3 into a spare copy, so every wave issues
+  // the same number of loads).
+  //   BSRC_NF4 / _PAIR: codes piece = rows w*32 .. w*32+31 of the tile
+  //     (32 B = 64 codes each), absmax = one value per tile row.
+  //   BSRC_NF4_T: the tile's K runs over weight rows: codes piece = weight
+  //     rows k0 + w*8 .. +7, 128 B each (the tile's 256 input features);
+  //     absmax = 64 weight rows x 4 blocks of 64 input features.
   const uint8_t* srcC = nullptr;
   const float* srcS = nullptr;
+  const uint8_t* srcC1 = nullptr;  // transposed mode: second stacked weight
+  const float* srcS1 = nullptr;
+  int64_t cstep = 0, sstep = 0;    // source advance per k-step (bytes / floats)
   if (NF4) {
-    const int gn = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
-    const uint8_t* codes = p.codes0;
-    const float* amax = p.absmax0;
-    int64_t wrow = gn;
-    if (BSRC == BSRC_NF4_PAIR) {
-      const int which = (gn >> 5) & 1;
-      wrow = (int64_t)((gn >> 6) << 5) + (gn & 31);
-      codes = which ? p.codes1 : p.codes0;
-      amax = which ? p.absmax1 : p.absmax0;
+    if (BSRC == BSRC_NF4_T) {
+      // weight [Nw][Kw]: Nw = GEMM K (reduction) rows, Kw = GEMM N features
+      const int64_t kw = p.N;
+      const int crow = wave * 8 + (lane >> 3);                        // weight row in step
+      const int ccol = min(n0 + (lane & 7) * 32, p.N - 32);           // first feature of the piece
+      srcC = p.codes0 + (int64_t)crow * (kw >> 1) + (ccol >> 1);
+      srcC1 = p.codes1 ? p.codes1 + (int64_t)crow * (kw >> 1) + (ccol >> 1) : nullptr;
+      cstep = (int64_t)BK * (kw >> 1);
+      const int srow = (wave & 3) * 16 + (lane >> 2);                 // weight row in step
+      const int sblk = min((n0 >> 6) + (lane & 3), (p.N >> 6) - 1);   // 64-feature block
+      srcS = p.absmax0 + (int64_t)srow * (kw >> 6) + sblk;
+      srcS1 = p.absmax1 ? p.absmax1 + (int64_t)srow * (kw >> 6) + sblk : nullptr;
+      sstep = (int64_t)BK * (kw >> 6);
+    } else {
+      const int r = wave * 32 + (lane >> 1);
+      int gn = min(n0 + r, p.N - 1);
+      const uint8_t* codes = p.codes0;
+      const float* amax = p.absmax0;
+      int64_t wrow = gn;
+      if (BSRC == BSRC_NF4_PAIR) {
+        const int which = (gn >> 5) & 1;
+        wrow = (int64_t)((gn >> 6) << 5) + (gn & 31);
+        codes = which ? p.codes1 : p.codes0;
+        amax = which ? p.absmax1 : p.absmax0;
+      }
+      srcC = codes + wrow * (int64_t)(p.K >> 1) + (lane & 1) * 16;
+      cstep = BK >> 1;
+      const int r2 = (wave & 3) * 64 + lane;
+      gn = min(n0 + r2, p.N - 1);
+      codes = p.codes0;
+      amax = p.absmax0;
+      wrow = gn;
+      if (BSRC == BSRC_NF4_PAIR) {
+        const int which = (gn >> 5) & 1;
+        wrow = (int64_t)((gn >> 6) << 5) + (gn & 31);
+        amax = which ? p.absmax1 : p.absmax0;
+      }
+      srcS = amax + wrow * (int64_t)(p.K >> 6);
+      sstep = 1;
     }
-    srcC = codes + wrow * (int64_t)(p.K >> 1);
-    srcS = amax + wrow * (int64_t)(p.K >> 6);
   }
 
+  auto stage_ptr = [&](int kt) { return smem + (kt % NSTAGE) * STAGE; };
+  // NF4 issue order: codes, absmax, then A, so that waiting for a step's
+  // codes leaves its A loads in flight (vmcnt counts in order).
   auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % NSTAGE) * STAGE;
+    uint8_t* st = stage_ptr(kt);
+    if (NF4) {
+      const uint8_t* c = srcC;
+      const float* sc = srcS;
+      int kl = kt;
+      if (BSRC == BSRC_NF4_T && p.ksplit > 0 && kt * BK >= p.ksplit) {
+        c = srcC1;
+        sc = srcS1;
+        kl = kt - p.ksplit / BK;
+      }
+      dma16(c + kl * cstep, st + A_BYTES + B_BYTES + wave * 1024);
+      dma4(sc + kl * sstep, st + A_BYTES + B_BYTES + C_BYTES + wave * 256);
+    }
     const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(srcA[j] + k0, st + (wave * 2 + j) * 1024);
+    for (int j = 0; j < 4; ++j) dma16(srcA[j] + k0, st + (wave * 4 + j) * 1024);
     if (!NF4) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16(srcB[j] + k0, st + A_BYTES + (wave * 2 + j) * 1024);
-    } else if (wave < 4) {
-      dma16(srcC + (k0 >> 1), st + A_BYTES + B_BYTES + wave * 1024);
+      for (int j = 0; j < 4; ++j) dma16(srcB[j] + k0, st + A_BYTES + (wave * 4 + j) * 1024);
+    }
+  };
+  constexpr int L = NF4 ? 6 : 8;   // loads per wave per k-step
+  constexpr int LA = 4;            // the A loads among them (issued last)
+
+  // NF4: dequantize the raw codes of a landed k-step into its bf16 B tile.
+  auto dequant_stage = [&](int kt) {
+    uint8_t* st = stage_ptr(kt);
+    const uint8_t* cb = st + A_BYTES + B_BYTES;
+    const float* sb = (const float*)(st + A_BYTES + B_BYTES + C_BYTES);
+    uint16_t* bt = (uint16_t*)(st + A_BYTES);
+    if (BSRC != BSRC_NF4_T) {
+      // thread t: tile row t/2, 32 weights (k half t&1) = chunks 4*(t&1) .. +3
+      const int row = tid >> 1, half = tid & 1;
+      const u32x4_t w = *(const u32x4_t*)(cb + row * 32 + half * 16);
+      const float amax = sb[row];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4_t o;
+        const uint32_t word = w[c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t byte = (word >> (8 * b)) & 0xFFu;
+          o[b] = pack_bf16x2(lut[byte >> 4] * amax, lut[byte & 0xFu] * amax);
+        }
+        lds_store16(&bt[swz(row, half * 4 + c)], o);
+      }
     } else {
-      dma4(srcS + (kt >> 1), st + A_BYTES + B_BYTES + C_BYTES + (wave - 4) * 256);
+      // thread t: tile rows (input features) f0 .. f0+3, f0 = 4*(t & 63),
+      // K (weight rows) q0 .. q0+7, q0 = 8*(t >> 6). Codes of weight row q,
+      // features f0..f0+3 are 2 bytes at q*128 + f0/2; absmax of (q, f0/64).
+      const int f0 = 4 * (tid & 63), q0 = 8 * (tid >> 6);
+      float w[8][4];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t two = *(const uint16_t*)(cb + (q0 + q) * 128 + (f0 >> 1));
+        const float amax = sb[(q0 + q) * 4 + (f0 >> 6)];
+        w[q][0] = lut[(two >> 4) & 0xFu] * amax;   // byte 0 high nibble: feature f0
+        w[q][1] = lut[two & 0xFu] * amax;          // byte 0 low nibble: f0 + 1
+        w[q][2] = lut[(two >> 12) & 0xFu] * amax;  // byte 1 high nibble: f0 + 2
+        w[q][3] = lut[(two >> 8) & 0xFu] * amax;   // byte 1 low nibble: f0 + 3
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(w[2 * e][f], w[2 * e + 1][f]);
+        lds_store16(&bt[swz(f0 + f, q0 >> 3)], o);
+      }
     }
   };
 
-  // NF4: two threads per B row (16 weights each) dequantize a landed stage
-  // into its bf16 region.
-  auto dequant_stage = [&](int kt) {
-    uint8_t* st = smem + (kt % NSTAGE) * STAGE;
-    const int row = tid >> 1, half = tid & 1;
-    const u32x2_t w = *(const u32x2_t*)(st + A_BYTES + B_BYTES + row * 16 + half * 8);
-    const float amax = *(const float*)(st + A_BYTES + B_BYTES + C_BYTES + row * 4);
-    uint16_t* sb = (uint16_t*)(st + A_BYTES);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) *(u32x4_t*)&sb[swz(row, half * 2 + c)] = dq8(w[c], amax, lut);
+  // Fragments of one 16-wide K substep: 4 A (rows of the wave) + 2 B (columns).
+  struct Frag {
+    bf16x8_t a[4], b[2];
   };
-
-  auto compute = [&](const uint8_t* st, int nsub) {
+  auto load_frag = [&](Frag& f, const uint8_t* st, int ks) {
     const uint16_t* sa = (const uint16_t*)st;
     const uint16_t* sb = (const uint16_t*)(st + A_BYTES);
-    for (int ks = 0; ks < nsub; ++ks) {
-      bf16x8_t a[4], b[2];
-      const int ch = 2 * ks + (lane >> 5);
+    const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *(const bf16x8_t*)&sa[swz(wm * 128 + mt * 32 + (lane & 31), ch)];
+    for (int mt = 0; mt < 4; ++mt)
+      f.a[mt] = *(const bf16x8_t*)&sa[swz(wm * 128 + mt * 32 + (lane & 31), ch)];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      f.b[nt] = *(const bf16x8_t*)&sb[swz(wn * 64 + nt * 32 + (lane & 31), ch)];
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        b[nt] = *(const bf16x8_t*)&sb[swz(wn * 64 + nt * 32 + (lane & 31), ch)];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
+  };
+  auto compute = [&](const uint8_t* st, int nsub) {
+    for (int ks = 0; ks < nsub; ++ks) {
+      Frag f;
+      load_frag(f, st, ks);
+      mma(f);
     }
   };
 
-  // ---- main K loop ----
-  if (!NF4) {
-    // bf16 operands: NSTAGE-deep LDS ring, PREF k-tiles of DMA in flight.
-    const int npro = min(PREF, nk);
-    for (int kt = 0; kt < npro; ++kt) issue(kt);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vm_stages<L>(min(nk - 1 - kt, PREF - 1));  // this wave's stage kt landed
-      ring_barrier();                                 // everyone's stage kt landed; kt-1 consumed
-      if (kt + PREF < nk) issue(kt + PREF);
-      compute(smem + (kt % NSTAGE) * STAGE, BK / 16);
-    }
-  } else {
-    // NF4 weights: raw codes/absmax arrive by DMA one k-tile ahead and are
-    // dequantized in LDS by the block. The in-loop LDS stores are ordered
-    // after all DMA in flight, so the raw data runs one stage ahead only.
-    issue(0);
-    if (nk > 1) issue(1);
-    wait_vm_stages<L>(nk > 1 ? 1 : 0);
-    ring_barrier();  // stage 0 raw data and lut visible
+  // ---- main K loop: 2-deep ring, DMA of step kt+1 in flight during step kt ----
+  // Iteration kt: issue step kt+1; (NF4) once its codes land, dequantize
+  // them; the MFMAs of step kt run meanwhile, with the fragments of the next
+  // substep (and, across the barrier, of step kt+1's first substep) loaded
+  // ahead. The closing barrier publishes step kt+1 and retires step kt.
+  issue(0);
+  wait_vm<0>();
+  ring_barrier();   // step 0 raw data (and lut) visible
+  if (NF4) {
     dequant_stage(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vm<0>();   // stage kt+1 raw data landed (and the dequant stores of stage kt done)
-      ring_barrier();
-      if (kt + 1 < nk) dequant_stage(kt + 1);
-      if (kt + 2 < nk) issue(kt + 2);
-      compute(smem + (kt % NSTAGE) * STAGE, BK / 16);
+    wait_vm<0>();
+    ring_barrier();
+  }
+  Frag f0, f1;
+  load_frag(f0, stage_ptr(0), 0);
+  wait_vm<0>();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) issue(kt + 1);
+    const uint8_t* st = stage_ptr(kt);
+    load_frag(f1, st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(f0, st, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (NF4 && more) {
+      wait_vm<LA>();   // codes + absmax of step kt+1 landed (A may still fly)
+      ring_barrier();  // ... for every wave
+      dequant_stage(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    load_frag(f1, st, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<0>();      // step kt+1 landed; all LDS traffic of this wave done
+    ring_barrier();
+    load_frag(f0, stage_ptr(more ? kt + 1 : kt), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
 
@@ -266,8 +370,8 @@ void gemm_nt_kernel(GemmArgs p) {
     uint16_t* sa = (uint16_t*)smem;
     uint16_t* sb = (uint16_t*)(smem + A_BYTES);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (tid >> 2) + 128 * i, chunk = tid & 3;
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 64 * i, chunk = tid & 7;
       const int ga = min(m0 + row, p.M - 1), gb = min(n0 + row, p.N - 1);
       u32x4_t za = {0u, 0u, 0u, 0u}, zb = {0u, 0u, 0u, 0u};
       if (chunk < nch) {
@@ -410,6 +514,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     case BSRC_BF16: return launch_b<BSRC_BF16>(a, stream);
     case BSRC_NF4: return launch_b<BSRC_NF4>(a, stream);
     case BSRC_NF4_PAIR: return launch_b<BSRC_NF4_PAIR>(a, stream);
+    case BSRC_NF4_T: return launch_b<BSRC_NF4_T>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -28,7 +28,13 @@ enum GemmEpilogue {
 
 // How the B operand ([N][K] weight, K contiguous) reaches the tile:
 //   bf16 rows, or NF4 codes dequantized while the tile is staged in LDS.
-enum GemmBSource { BSRC_BF16 = 0, BSRC_NF4 = 1, BSRC_NF4_PAIR = 2 };
+enum GemmBSource {
+  BSRC_BF16 = 0,      // B bf16 [N][K]
+  BSRC_NF4 = 1,       // B = NF4 weight [N][K]
+  BSRC_NF4_PAIR = 2,  // B rows interleaved by 32 from two NF4 weights [N/2][K] (gate, up)
+  BSRC_NF4_T = 3      // B = W^T for an NF4 weight W [K][N]; with codes1, W = [W0; W1]
+                      // stacked along K (rows >= ksplit come from W1)
+};
 
 struct GemmArgs {
   // main operands: A [M][K] bf16 (lda); B [N][K] bf16 (ldb) or NF4
@@ -39,8 +45,9 @@ struct GemmArgs {
   int bsrc;
   const uint8_t* codes0;   // NF4 of B rows (pair mode: gate rows)
   const float* absmax0;
-  const uint8_t* codes1;   // pair mode: up rows
+  const uint8_t* codes1;   // pair mode: up rows; transposed mode: second stacked weight
   const float* absmax1;
+  int ksplit;              // transposed mode: first K index served by codes1 (0 = none)
   // K-extension: C += Ae [M][KE] * Be [N][KE]^T (KE multiple of 16, may be 0)
   const uint16_t* Ae;
   int64_t ldae;
