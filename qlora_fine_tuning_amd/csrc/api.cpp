@@ -306,9 +306,13 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* 
   plan_linear_fwd(c, m, k, n, r, mode, &t);
   const int KE = (int)ceil16(2 * r);
 
-  QL_TRY(launch_zero(t.bext, (size_t)n * KE * 2, st), "linear_fwd: zero");
-  QL_TRY(launch_copy2d(B, r, 1, (int)n, (int)r, t.bext, KE, 1, 0, st), "linear_fwd: Bext");
-  QL_TRY(launch_copy2d(B, r, 1, (int)n, (int)r, t.bext + r, KE, 1, 0, st), "linear_fwd: Bext");
+  {  // Bext = [B | B | 0]
+    PrepJobs J;
+    J.copy(B, r, 1, n, r, t.bext, KE, 1);
+    J.copy(B, r, 1, n, r, t.bext + r, KE, 1);
+    J.zero(n, KE - 2 * r, t.bext + 2 * r, KE, 1);
+    QL_TRY(launch_prep(J, st), "linear_fwd: LoRA layouts");
+  }
   if (mode == QLORA_DEQUANT_STAGED)
     QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, n, k, t.wbf, k, 0, st), "linear_fwd: dequant");
   QL_TRY(launch_rowdot(X, k, A, k, (int)m, (int)k, (int)r, s, U_save, nullptr, (int)r, r, t.uext,
@@ -338,8 +342,10 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (m == 0) {  // empty batch: zero weight gradients
-    QL_TRY(launch_zero(dA, (size_t)r * k * 2, st), "linear_bwd: zero dA");
-    QL_TRY(launch_zero(dB, (size_t)n * r * 2, st), "linear_bwd: zero dB");
+    PrepJobs J;
+    J.zero(r, k, dA, k, 1);
+    J.zero(n, r, dB, r, 1);
+    QL_TRY(launch_prep(J, st), "linear_bwd: zero grads");
     return QLORA_OK;
   }
   Carver c(ws);
@@ -348,10 +354,14 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   const int KE = (int)ceil16(2 * r);
   const int chunks = colreduce_chunks((int)m);
 
-  QL_TRY(launch_copy2d(B, 1, r, (int)r, (int)n, t.lt, n, 1, 0, st), "linear_bwd: B^T");
-  QL_TRY(launch_zero(t.bext, (size_t)k * KE * 2, st), "linear_bwd: zero");
-  QL_TRY(launch_copy2d(A, 1, k, (int)k, (int)r, t.bext, KE, 1, 0, st), "linear_bwd: A^T");
-  QL_TRY(launch_copy2d(A, 1, k, (int)k, (int)r, t.bext + r, KE, 1, 0, st), "linear_bwd: A^T");
+  {  // lt = B^T ; bext = [A^T | A^T | 0]
+    PrepJobs J;
+    J.copy(B, 1, r, r, n, t.lt, n, 1);
+    J.copy(A, 1, k, k, r, t.bext, KE, 1);
+    J.copy(A, 1, k, k, r, t.bext + r, KE, 1);
+    J.zero(k, KE - 2 * r, t.bext + 2 * r, KE, 1);
+    QL_TRY(launch_prep(J, st), "linear_bwd: LoRA layouts");
+  }
   // T = dY B
   QL_TRY(launch_rowdot(dY, n, t.lt, n, (int)m, (int)n, (int)r, s, t.t, nullptr, (int)r, r, t.text,
                        KE, KE, t.rpart, st),
@@ -427,16 +437,25 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   const float s = w->s;
 
   // LoRA operand layouts
-  QL_TRY(launch_copy2d(w->a_gate, d, 1, (int)r, (int)d, t.lgu, d, 1, 0, st), "mlp_fwd: Lgu");
-  QL_TRY(launch_copy2d(w->a_up, d, 1, (int)r, (int)d, t.lgu + r * d, d, 1, 0, st), "mlp_fwd: Lgu");
-  QL_TRY(launch_zero(t.bextgu, (size_t)2 * h * KEgu * 2, st), "mlp_fwd: zero");
-  QL_TRY(launch_copy2d(w->b_gate, r, 1, (int)h, (int)r, t.bextgu, KEgu, 1, 1, st), "mlp_fwd: Bext");
-  QL_TRY(launch_copy2d(w->b_gate, r, 1, (int)h, (int)r, t.bextgu + 2 * r, KEgu, 1, 1, st), "mlp_fwd: Bext");
-  QL_TRY(launch_copy2d(w->b_up, r, 1, (int)h, (int)r, t.bextgu + r, KEgu, 1, 2, st), "mlp_fwd: Bext");
-  QL_TRY(launch_copy2d(w->b_up, r, 1, (int)h, (int)r, t.bextgu + 3 * r, KEgu, 1, 2, st), "mlp_fwd: Bext");
-  QL_TRY(launch_zero(t.bextd, (size_t)d * KEd * 2, st), "mlp_fwd: zero");
-  QL_TRY(launch_copy2d(w->b_down, r, 1, (int)d, (int)r, t.bextd, KEd, 1, 0, st), "mlp_fwd: Bext");
-  QL_TRY(launch_copy2d(w->b_down, r, 1, (int)d, (int)r, t.bextd + r, KEd, 1, 0, st), "mlp_fwd: Bext");
+  {  // Lgu = [Ag; Au]; Bext_gu rows interleaved by 32 (gate: [Bg 0 Bg 0 0..],
+     // up: [0 Bu 0 Bu 0..]); Bext_d = [Bd | Bd | 0]
+    PrepJobs J;
+    J.copy(w->a_gate, d, 1, r, d, t.lgu, d, 1);
+    J.copy(w->a_up, d, 1, r, d, t.lgu + r * d, d, 1);
+    J.copy(w->b_gate, r, 1, h, r, t.bextgu, KEgu, 1, 1);
+    J.zero(h, r, t.bextgu + r, KEgu, 1, 1);
+    J.copy(w->b_gate, r, 1, h, r, t.bextgu + 2 * r, KEgu, 1, 1);
+    J.zero(h, KEgu - 3 * r, t.bextgu + 3 * r, KEgu, 1, 1);
+    J.zero(h, r, t.bextgu, KEgu, 1, 2);
+    J.copy(w->b_up, r, 1, h, r, t.bextgu + r, KEgu, 1, 2);
+    J.zero(h, r, t.bextgu + 2 * r, KEgu, 1, 2);
+    J.copy(w->b_up, r, 1, h, r, t.bextgu + 3 * r, KEgu, 1, 2);
+    J.zero(h, KEgu - 4 * r, t.bextgu + 4 * r, KEgu, 1, 2);
+    J.copy(w->b_down, r, 1, d, r, t.bextd, KEd, 1);
+    J.copy(w->b_down, r, 1, d, r, t.bextd + r, KEd, 1);
+    J.zero(d, KEd - 2 * r, t.bextd + 2 * r, KEd, 1);
+    QL_TRY(launch_prep(J, st), "mlp_fwd: LoRA layouts");
+  }
   if (mode == QLORA_DEQUANT_STAGED) {
     QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
     QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
@@ -489,12 +508,14 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (m == 0) {
-    QL_TRY(launch_zero(gr->a_gate, (size_t)r * d * 2, st), "mlp_bwd: zero");
-    QL_TRY(launch_zero(gr->a_up, (size_t)r * d * 2, st), "mlp_bwd: zero");
-    QL_TRY(launch_zero(gr->a_down, (size_t)r * h * 2, st), "mlp_bwd: zero");
-    QL_TRY(launch_zero(gr->b_gate, (size_t)h * r * 2, st), "mlp_bwd: zero");
-    QL_TRY(launch_zero(gr->b_up, (size_t)h * r * 2, st), "mlp_bwd: zero");
-    QL_TRY(launch_zero(gr->b_down, (size_t)d * r * 2, st), "mlp_bwd: zero");
+    PrepJobs J;
+    J.zero(r, d, gr->a_gate, d, 1);
+    J.zero(r, d, gr->a_up, d, 1);
+    J.zero(r, h, gr->a_down, h, 1);
+    J.zero(h, r, gr->b_gate, r, 1);
+    J.zero(h, r, gr->b_up, r, 1);
+    J.zero(d, r, gr->b_down, r, 1);
+    QL_TRY(launch_prep(J, st), "mlp_bwd: zero grads");
     return QLORA_OK;
   }
   Carver c(ws);
@@ -505,19 +526,24 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   const float s = w->s;
 
   // LoRA operand layouts
-  QL_TRY(launch_copy2d(w->b_down, 1, r, (int)r, (int)d, t.ltd, d, 1, 0, st), "mlp_bwd: Bd^T");
-  QL_TRY(launch_zero(t.bextdh, (size_t)h * KEd * 2, st), "mlp_bwd: zero");
-  QL_TRY(launch_copy2d(w->a_down, 1, h, (int)h, (int)r, t.bextdh, KEd, 1, 0, st), "mlp_bwd: Ad^T");
-  QL_TRY(launch_copy2d(w->a_down, 1, h, (int)h, (int)r, t.bextdh + r, KEd, 1, 0, st), "mlp_bwd: Ad^T");
-  QL_TRY(launch_zero(t.ltgu, (size_t)2 * r * 2 * h * 2, st), "mlp_bwd: zero");
-  QL_TRY(launch_copy2d(w->b_gate, 1, r, (int)r, (int)h, t.ltgu, 2 * h, 1, 0, st), "mlp_bwd: Bg^T");
-  QL_TRY(launch_copy2d(w->b_up, 1, r, (int)r, (int)h, t.ltgu + r * 2 * h + h, 2 * h, 1, 0, st),
-         "mlp_bwd: Bu^T");
-  QL_TRY(launch_zero(t.bextdx, (size_t)d * KEgu * 2, st), "mlp_bwd: zero");
-  QL_TRY(launch_copy2d(w->a_gate, 1, d, (int)d, (int)r, t.bextdx, KEgu, 1, 0, st), "mlp_bwd: Ag^T");
-  QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
-  QL_TRY(launch_copy2d(w->a_gate, 1, d, (int)d, (int)r, t.bextdx + 2 * r, KEgu, 1, 0, st), "mlp_bwd: Ag^T");
-  QL_TRY(launch_copy2d(w->a_up, 1, d, (int)d, (int)r, t.bextdx + 3 * r, KEgu, 1, 0, st), "mlp_bwd: Au^T");
+  {  // ltd = Bd^T; bextdh = [Ad^T | Ad^T | 0]; ltgu = blockdiag(Bg^T, Bu^T);
+     // bextdx = [Ag^T | Au^T | Ag^T | Au^T | 0]
+    PrepJobs J;
+    J.copy(w->b_down, 1, r, r, d, t.ltd, d, 1);
+    J.copy(w->a_down, 1, h, h, r, t.bextdh, KEd, 1);
+    J.copy(w->a_down, 1, h, h, r, t.bextdh + r, KEd, 1);
+    J.zero(h, KEd - 2 * r, t.bextdh + 2 * r, KEd, 1);
+    J.copy(w->b_gate, 1, r, r, h, t.ltgu, 2 * h, 1);
+    J.zero(r, h, t.ltgu + h, 2 * h, 1);
+    J.zero(r, h, t.ltgu + r * 2 * h, 2 * h, 1);
+    J.copy(w->b_up, 1, r, r, h, t.ltgu + r * 2 * h + h, 2 * h, 1);
+    J.copy(w->a_gate, 1, d, d, r, t.bextdx, KEgu, 1);
+    J.copy(w->a_up, 1, d, d, r, t.bextdx + r, KEgu, 1);
+    J.copy(w->a_gate, 1, d, d, r, t.bextdx + 2 * r, KEgu, 1);
+    J.copy(w->a_up, 1, d, d, r, t.bextdx + 3 * r, KEgu, 1);
+    J.zero(d, KEgu - 4 * r, t.bextdx + 4 * r, KEgu, 1);
+    QL_TRY(launch_prep(J, st), "mlp_bwd: LoRA layouts");
+  }
   // staged mode: dequantized transposed weights for the two backward GEMMs
   const bool staged = mode == QLORA_DEQUANT_STAGED;
   if (staged) {

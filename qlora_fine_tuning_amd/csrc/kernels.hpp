@@ -96,11 +96,33 @@ hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, 
                                    hipStream_t stream);
 
 // ---- small layout kernels (lora.hip) ----
+// One copy (src != null) or zero-fill (src == null) job:
 // dst[drow(r) * d_rs + c * d_cs] = src[r * s_rs + c * s_cs] for r < rows, c < cols;
 // drow(r) = r, or the 32-row interleave (as for the dequant) when interleave > 0.
-hipError_t launch_copy2d(const uint16_t* src, int64_t s_rs, int64_t s_cs, int rows, int cols,
-                         uint16_t* dst, int64_t d_rs, int64_t d_cs, int interleave,
-                         hipStream_t stream);
+struct PrepJob {
+  const uint16_t* src;
+  int64_t s_rs, s_cs;
+  int rows, cols;
+  uint16_t* dst;
+  int64_t d_rs, d_cs;
+  int interleave;
+};
+constexpr int kMaxPrepJobs = 16;
+struct PrepJobs {
+  PrepJob j[kMaxPrepJobs];
+  int n = 0;
+  void copy(const uint16_t* src, int64_t s_rs, int64_t s_cs, int64_t rows, int64_t cols,
+            uint16_t* dst, int64_t d_rs, int64_t d_cs, int interleave = 0) {
+    j[n++] = PrepJob{src, s_rs, s_cs, (int)rows, (int)cols, dst, d_rs, d_cs, interleave};
+  }
+  void zero(int64_t rows, int64_t cols, uint16_t* dst, int64_t d_rs, int64_t d_cs,
+            int interleave = 0) {
+    if (rows > 0 && cols > 0)
+      j[n++] = PrepJob{nullptr, 0, 0, (int)rows, (int)cols, dst, d_rs, d_cs, interleave};
+  }
+};
+// Jobs must write disjoint elements (they run concurrently).
+hipError_t launch_prep(const PrepJobs& jobs, hipStream_t stream);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace qlora

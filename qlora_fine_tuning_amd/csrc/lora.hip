@@ -17,6 +17,8 @@
 //               (G^T as the row operand via 2-byte LDS gathers, V as bf16
 //               hi + lo). G may be H = act(g) * u recomputed from g, u.
 //  finish     : fixed-order sum over chunks, scale, bf16, any output stride.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -399,26 +401,31 @@ hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, 
 }
 
 // ---------------------------------------------------------------- layout --
-__global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict__ src, int64_t s_rs,
-                                                     int64_t s_cs, int rows, int cols,
-                                                     uint16_t* __restrict__ dst, int64_t d_rs,
-                                                     int64_t d_cs, int interleave) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)rows * cols) return;
-  const int r = (int)(e / cols);
-  const int c = (int)(e - (int64_t)r * cols);
-  int64_t dr = r;
-  if (interleave) dr = 64 * (r >> 5) + 32 * (interleave - 1) + (r & 31);
-  dst[dr * d_rs + (int64_t)c * d_cs] = src[(int64_t)r * s_rs + (int64_t)c * s_cs];
+// All small LoRA operand layouts of one entry point in a single launch: job j
+// (blockIdx.y) copies a strided rows x cols view (or writes zeros when its
+// source is null). Jobs never overlap, so their order does not matter.
+__global__ __launch_bounds__(256) void prep_kernel(PrepJobs jobs) {
+  const PrepJob& jb = jobs.j[blockIdx.y];
+  const int64_t total = (int64_t)jb.rows * jb.cols;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int r = (int)(e / jb.cols);
+    const int c = (int)(e - (int64_t)r * jb.cols);
+    int64_t dr = r;
+    if (jb.interleave) dr = 64 * (r >> 5) + 32 * (jb.interleave - 1) + (r & 31);
+    jb.dst[dr * jb.d_rs + (int64_t)c * jb.d_cs] =
+        jb.src ? jb.src[(int64_t)r * jb.s_rs + (int64_t)c * jb.s_cs] : (uint16_t)0;
+  }
 }
 
-hipError_t launch_copy2d(const uint16_t* src, int64_t s_rs, int64_t s_cs, int rows, int cols,
-                         uint16_t* dst, int64_t d_rs, int64_t d_cs, int interleave,
-                         hipStream_t stream) {
-  const int64_t total = (int64_t)rows * cols;
-  if (total <= 0) return hipSuccess;
-  copy2d_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-      src, s_rs, s_cs, rows, cols, dst, d_rs, d_cs, interleave);
+hipError_t launch_prep(const PrepJobs& jobs, hipStream_t stream) {
+  if (jobs.n <= 0) return hipSuccess;
+  if (jobs.n > kMaxPrepJobs) return hipErrorInvalidValue;
+  int64_t most = 0;
+  for (int i = 0; i < jobs.n; ++i) most = std::max(most, (int64_t)jobs.j[i].rows * jobs.j[i].cols);
+  int64_t bx = (most + 255) / 256;
+  if (bx < 1) bx = 1;
+  if (bx > 512) bx = 512;
+  prep_kernel<<<dim3((unsigned)bx, (unsigned)jobs.n), dim3(256), 0, stream>>>(jobs);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ __device__ __forceinline__ int64_t dest_row(int64_t n, int interleave) {
   return 64 * (n >> 5) + 32 * (interleave - 1) + (n & 31);
 }
 
-// One thread per 8 weights. Grid-stride over n * k / 8 groups.
+// One thread per 8 weights (4 code bytes in, 16 bf16 bytes out). Grid-stride
+// over n * k / 8 groups.
 __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int interleave) {
@@ -59,57 +60,55 @@ __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
   const int64_t total = n * groups_per_row;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
-    int64_t row = t / groups_per_row;
-    int64_t grp = t - row * groups_per_row;
-    uint32_t word = *(const uint32_t*)(codes + row * (k >> 1) + grp * 4);
-    float amax = absmax[row * (k >> 6) + (grp >> 3)];
-    u32x4_t v = dequant8(word, amax, lut);
-    *(u32x4_t*)(out + dest_row(row, interleave) * ld_out + grp * 8) = v;
+    const int64_t row = t / groups_per_row;
+    const int64_t grp = t - row * groups_per_row;
+    const uint32_t word = *(const uint32_t*)(codes + row * (k >> 1) + grp * 4);
+    const float amax = absmax[row * (k >> 6) + (grp >> 3)];
+    *(u32x4_t*)(out + dest_row(row, interleave) * ld_out + grp * 8) = dequant8(word, amax, lut);
   }
 }
 
-// Transposing dequant: out[kk][col_ofs + nn] = W[nn][kk]. One 64 x 64 tile
-// per block, staged through LDS so both the code reads and the bf16 writes
-// are row-contiguous.
+// Transposing dequant: out[kk][col_ofs + nn] = W[nn][kk]. A block covers 64
+// weight rows x 128 input features: the 4 KB of codes go through LDS, then
+// thread t dequantizes 8 weight rows x 4 features and writes 4 output rows
+// of 8 consecutive values; 8 lanes cover one 128-byte output row segment.
 __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t col_ofs) {
   __shared__ float lut[16];
-  __shared__ uint16_t tile[64][64 + 2];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[64 * 64];
+  __shared__ float at[64][2];
   const int tid = threadIdx.x;
   if (tid < 16) lut[tid] = __uint_as_float(c_nf4_levels[tid]);
-  __syncthreads();
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 128;
+  const int kvalid = (int)min((int64_t)128, k - k0);   // 64 or 128 (k is a multiple of 64)
   {
-    // thread: row n0 + tid/4, 16 consecutive k starting at (tid%4)*16
-    const int r = tid >> 2, c16 = (tid & 3) * 16;
-    const int64_t row = n0 + r;
-    const uint8_t* src = codes + row * (k >> 1) + ((k0 + c16) >> 1);
-    float amax = absmax[row * (k >> 6) + (k0 >> 6)];
-    u32x2_t words = *(const u32x2_t*)src;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      u32x4_t v = dequant8(words[w], amax, lut);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        tile[c16 + w * 8 + 2 * q][r] = (uint16_t)(v[q] & 0xFFFFu);
-        tile[c16 + w * 8 + 2 * q + 1][r] = (uint16_t)(v[q] >> 16);
-      }
-    }
+    const int r = tid >> 2, c = (tid & 3) * 16;   // 64 rows x 64 code bytes
+    if (2 * c < kvalid)
+      *(u32x4_t*)&ct[r * 64 + c] = *(const u32x4_t*)(codes + (n0 + r) * (k >> 1) + (k0 >> 1) + c);
+    if (tid < 128 && 64 * (tid & 1) < kvalid)
+      at[tid >> 1][tid & 1] = absmax[(n0 + (tid >> 1)) * (k >> 6) + (k0 >> 6) + (tid & 1)];
   }
   __syncthreads();
-  {
-    // thread: output row k0 + tid/4, 16 consecutive n starting at (tid%4)*16
-    const int kk = tid >> 2, c16 = (tid & 3) * 16;
-    u32x4_t a, b;
+  const int qg = tid & 7, kq = tid >> 3;          // rows 8qg..8qg+7, features 4kq..4kq+3
+  if (4 * kq >= kvalid) return;
+  float w[8][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = (uint32_t)tile[kk][c16 + 2 * q] | ((uint32_t)tile[kk][c16 + 2 * q + 1] << 16);
-      b[q] = (uint32_t)tile[kk][c16 + 8 + 2 * q] | ((uint32_t)tile[kk][c16 + 8 + 2 * q + 1] << 16);
-    }
-    uint16_t* dst = out + (k0 + kk) * ld_out + col_ofs + n0 + c16;
-    *(u32x4_t*)dst = a;
-    *(u32x4_t*)(dst + 8) = b;
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * qg + q;
+    const uint32_t two = *(const uint16_t*)&ct[r * 64 + 2 * kq];
+    const float amax = at[r][kq >> 4];
+    w[q][0] = lut[(two >> 4) & 0xFu] * amax;
+    w[q][1] = lut[two & 0xFu] * amax;
+    w[q][2] = lut[(two >> 12) & 0xFu] * amax;
+    w[q][3] = lut[(two >> 8) & 0xFu] * amax;
+  }
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(w[2 * e][f], w[2 * e + 1][f]);
+    *(u32x4_t*)(out + (k0 + 4 * kq + f) * ld_out + col_ofs + n0 + 8 * qg) = o;
   }
 }
 
@@ -129,7 +128,7 @@ hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, const float* absma
                                         int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
                                         hipStream_t stream) {
   if (n == 0 || k == 0) return hipSuccess;
-  dim3 grid((unsigned)(k / 64), (unsigned)(n / 64));
+  dim3 grid((unsigned)((k + 127) / 128), (unsigned)(n / 64));
   nf4_dequant_transpose_kernel<<<grid, dim3(256), 0, stream>>>(codes, absmax, n, k, out, ld_out,
                                                               col_ofs);
   return hipGetLastError();
