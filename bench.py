@@ -37,7 +37,25 @@ def parse():
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="token sample of the CPU oracle baseline (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 3 times (counter calibration)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch.
+
+    Profiled with the same rocprofv3 counters as the benchmark, it gives the
+    factor between what FETCH_SIZE / WRITE_SIZE report and true HBM bytes.
+    """
+    import torch
+    n = 1 << 29                      # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": 2 * n, "launches": 3}))
 
 
 def mlp_flops(m, d, h, r):
@@ -92,6 +110,9 @@ def cpu_baseline(cfg, d, tokens):
 
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration()
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); "
               "the multi-GPU data-parallel design is described, not built.", file=sys.stderr)
