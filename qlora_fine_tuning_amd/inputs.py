@@ -18,10 +18,12 @@ nearest even).
 
 Synthetic NF4 weights (``synthetic_nf4``) stand in for quantized N(0, sigma)
 weights when a workload is too large to quantize on the host: each 64-block's
-absmax is the bf16 max of |N(0, sigma)| over 64 draws, codes are uniform on
-0..15 (NF4 levels are equal-probability quantiles of the normal, so codes of
-normal weights are close to uniform) and one element per block carries the
-+-1 code (0 or 15), as the block's largest weight does after quantization.
+absmax is the bf16 max of |N(0, sigma)| over 64 draws, and the packed code
+bytes are uniform on 0..255, i.e. two independent codes uniform on 0..15 per
+byte. NF4 levels are equal-probability quantiles of the normal, so codes of
+quantized normal weights are close to uniform; a block of 64 uniform codes
+holds an end code (0 or 15, the +-1 levels) with probability 1 - (14/16)^64,
+as the block's largest weight does after quantization.
 """
 from __future__ import annotations
 
@@ -72,12 +74,7 @@ def synthetic_nf4(name, n, k, std=0.02, seed=SEED):
         draws = g.standard_normal((min(rows, n - r0), nb, 64), dtype=np.float32) * np.float32(std)
         amax[r0:r0 + rows] = np.abs(draws).max(axis=2)
     absmax = to_bf16(amax).to(torch.float32)
-    codes = g.integers(0, 16, size=(n, k), dtype=np.uint8)
-    pos = g.integers(0, 64, size=(n, nb))
-    sign = g.integers(0, 2, size=(n, nb)).astype(np.uint8) * 15
-    cv = codes.reshape(n, nb, 64)
-    np.put_along_axis(cv, pos[..., None], sign[..., None], axis=2)
-    packed = ((codes[:, 0::2] << 4) | codes[:, 1::2]).astype(np.uint8)
+    packed = g.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
     return torch.from_numpy(packed), absmax
 
 
