@@ -65,15 +65,17 @@ def mlp_flops(m, d, h, r):
     return 6 * 2 * m * d * h + 3 * 3 * 2 * m * r * (d + h)
 
 
-def gemm_traffic(lib_src_dir):
+def gemm_traffic(lib_src_dir, workload, mode):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
+    or None when it was taken on another workload or dequant mode, or the
+    kernel source changed since."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256(open(os.path.join(lib_src_dir, "gemm.hip"), "rb").read()).hexdigest()
-    if rec.get("gemm_hip_sha256") != h:
+    if (rec.get("gemm_hip_sha256") != h or rec.get("workload_name") != workload
+            or rec.get("dequant_mode") != mode):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -160,7 +162,8 @@ def main():
     flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
-    traffic = gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"))
+    traffic = gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"), cfg.name,
+                           "staged" if a.mode == "auto" else a.mode)
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
