@@ -28,8 +28,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
-// Logistic function; saturates cleanly for large |x|.
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + fast_exp(-x)); }
+// Logistic function with the hardware reciprocal (v_rcp_f32, ~1 ulp), which
+// the bf16 outputs cannot resolve; saturates cleanly: exp(-x) -> inf gives
+// rcp(inf) = 0, exp(-x) -> 0 gives 1.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
 // Activations of the gated MLP and their derivatives (fp32).
 //   act 0: silu(g) = g * sigmoid(g);  silu'(g) = sig * (1 + g * (1 - sig))

@@ -36,6 +36,8 @@
 #include "kernels.hpp"
 #include "nf4_table.hpp"
 
+#include <type_traits>
+
 namespace qlora {
 
 namespace {
@@ -491,6 +493,321 @@ void gemm_nt_kernel(GemmArgs p) {
   }
 }
 
+
+// ===========================================================================
+// bf16-B GEMM: one 256 x 256 tile per workgroup of 4 waves (1 per SIMD), each
+// wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles, its 256 fp32 accumulators in
+// AGPRs. This is the kernel of the staged path (B = pre-dequantized weight).
+//
+// Operand feed: buffer loads straight into LDS (buffer_load_dwordx4 ... lds),
+// through a buffer resource per tile whose size ends at the matrix end, so
+// rows past M (N) read as zeros without per-row clamps. One load instruction
+// moves 8 rows x 128 B in global order (full 128-byte lines); consecutive
+// 1 KB blocks sit at a 1040-byte pitch, and the MFMA lanes read rows in the
+// order below, which makes every 16-lane phase of a ds_read_b128 hit 16
+// different bank groups:
+//   MFMA row i (0..31) of tile t of wave w reads tile row
+//   8 * (16 * w + (i & 15)) + 2 * t + (i >> 4)          (A; B likewise).
+// The epilogue undoes this permutation.
+//
+// Pipeline per 64-wide k-step (2 LDS stages): the loads of step k+1 are
+// issued during the first half of step k, interleaved with its MFMAs; one
+// 4-byte touch per tile row pulls the lines of step k+2 into L2 so that the
+// step-(k+1) loads mostly hit; one barrier per step.
+// ===========================================================================
+namespace {
+constexpr int G_PITCH = 1040;           // bytes per 8-row DMA block
+constexpr int G_OPB = 32 * G_PITCH;     // one operand (256 rows x 64) per stage
+constexpr int G_STAGE = 2 * G_OPB;
+constexpr int G_PF = 2;                 // L2 prefetch distance (k-steps)
+
+// buffer load of `size` bytes per lane into LDS at lds + size*lane; the
+// resource is rebuilt from uniform integers at each use (it stays in SGPRs)
+template <int SIZE>
+__device__ __forceinline__ void bload_lds(uint64_t base, int nrec, void* lds, uint32_t voff, int soff) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(((uint64_t)hi << 32) | lo), (short)0, __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, so, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, so, 0, 0);
+}
+
+// offset that no buffer covers: the load returns zeros
+constexpr uint32_t OOB = 0x80000000u;
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(256)
+void gemm_bf16_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G_STAGE + 256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, ntm * ntn);
+  const int GM = 8;
+  const int per_group = GM * ntn;
+  const int group = pid / per_group;
+  const int first_m = group * GM;
+  const int gsz = min(ntm - first_m, GM);
+  const int tm = first_m + (pid % per_group) % gsz;
+  const int tn = (pid % per_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = p.K / BK;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // ---- operand sources: wave w, load j (0..7) fills DMA block 8w + j ----
+  const int64_t rowsA = min(BM, p.M - m0), rowsB = min(BN, p.N - n0);
+  const uint64_t bA = (uint64_t)(p.A + (int64_t)m0 * p.lda), bB = (uint64_t)(p.B + (int64_t)n0 * p.ldb);
+  const int nA = (int)min<int64_t>(rowsA * p.lda * 2, 0x7fffffff);
+  const int nB = (int)min<int64_t>(rowsB * p.ldb * 2, 0x7fffffff);
+  const int lrow = 64 * wave + (lane >> 3);                      // + 8 j
+  const uint32_t voA = (uint32_t)(lrow * p.lda + (lane & 7) * 8) * 2u;
+  const uint32_t voB = (uint32_t)(lrow * p.ldb + (lane & 7) * 8) * 2u;
+  const uint32_t stA = (uint32_t)(8 * p.lda * 2), stB = (uint32_t)(8 * p.ldb * 2);
+  auto stage_ptr = [&](int kt) { return smem + (kt & 1) * G_STAGE; };
+  auto issue1 = [&](int kt, int q) {   // even q: A load q/2, odd q: B load q/2
+    uint8_t* st = stage_ptr(kt);
+    const int j = q >> 1, kb = kt * BK * 2;
+    if ((q & 1) == 0) bload_lds<16>(bA, nA, st + (8 * wave + j) * G_PITCH, voA + j * stA, kb);
+    else bload_lds<16>(bB, nB, st + G_OPB + (8 * wave + j) * G_PITCH, voB + j * stB, kb);
+  };
+  const uint32_t pfA = (uint32_t)(tid * p.lda * 2), pfB = (uint32_t)(tid * p.ldb * 2);
+  auto prefetch = [&](int kt) {   // tile row tid: touch its 128-B line of step kt (A and B)
+    bload_lds<4>(bA, nA, smem + 2 * G_STAGE, pfA, kt * BK * 2);
+    bload_lds<4>(bB, nB, smem + 2 * G_STAGE, pfB, kt * BK * 2);
+  };
+
+  // ---- fragments ----
+  const int fr = (16 * wm + (lane & 15)) * G_PITCH + ((lane >> 4) & 1) * 128 + (lane >> 5) * 16;
+  const int fc = (16 * wn + (lane & 15)) * G_PITCH + ((lane >> 4) & 1) * 128 + (lane >> 5) * 16;
+  struct Frag {
+    bf16x8_t a[4], b[4];
+  };
+  auto load_frag = [&](Frag& f, const uint8_t* st, int ks) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) f.a[mt] = *(const bf16x8_t*)(st + fr + mt * 256 + ks * 32);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) f.b[nt] = *(const bf16x8_t*)(st + G_OPB + fc + nt * 256 + ks * 32);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
+  };
+  // scheduling hint for one 16-MFMA substep: the fragment reads go with the
+  // first 8 MFMAs, the loads (which write LDS, so they stay after the reads
+  // in program order) with the last 8
+  auto interleave = [&](int nds, int nvm) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+  };
+
+  // ---- main loop ----
+#pragma unroll
+  for (int q = 0; q < 16; ++q) issue1(0, q);
+  for (int s = 1; s < G_PF; ++s)
+    if (s < nk) prefetch(s);
+  wait_vm<0>();
+  ring_barrier();
+  Frag f0, f1;
+  load_frag(f0, stage_ptr(0), 0);
+  // step kt; PRE: step kt+1 exists (issue its loads and the L2 touch of kt+2)
+  auto step = [&](int kt, auto pre_c) {
+    constexpr bool pre = decltype(pre_c)::value;
+    const uint8_t* st = stage_ptr(kt);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      Frag& cur = (ks & 1) ? f1 : f0;
+      Frag& nxt = (ks & 1) ? f0 : f1;
+      load_frag(nxt, st, ks + 1);
+      if (pre && ks < 2) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) issue1(kt + 1, ks * 8 + q);
+      }
+      mma(cur);
+      interleave(8, (pre && ks < 2) ? 8 : 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (pre) prefetch(min(kt + G_PF, nk - 1));   // issued last: vmcnt retires in order
+    if (pre) wait_vm<2>(); else wait_vm<0>();     // step kt+1 landed (the touches may fly)
+    ring_barrier();
+    if (kt + 1 < nk) load_frag(f0, stage_ptr(kt + 1), 0);
+    mma(f1);
+    interleave(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) step(kt, std::integral_constant<bool, true>());
+  step(kt, std::integral_constant<bool, false>());
+  wait_vm<0>();
+  __syncthreads();
+
+  // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be;
+  // columns at or past KE read as zeros ----
+  if (p.KE > 0) {
+    const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
+    const int neA = (int)min<int64_t>(rowsA * p.ldae * 2, 0x7fffffff);
+    const int neB = (int)min<int64_t>(rowsB * p.ldbe * 2, 0x7fffffff);
+    for (int e = 0; e * BK < p.KE; ++e) {
+      const int c = e * BK + (lane & 7) * 8;   // this lane's first column
+      const bool in = c < p.KE;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = lrow + 8 * j;
+        bload_lds<16>(eA, neA, smem + (8 * wave + j) * G_PITCH, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
+        bload_lds<16>(eB, neB, smem + G_OPB + (8 * wave + j) * G_PITCH, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
+      }
+      wait_vm<0>();
+      ring_barrier();
+      const int nsub = (min(BK, p.KE - e * BK) + 15) >> 4;
+      for (int ks = 0; ks < nsub; ++ks) {
+        Frag f;
+        load_frag(f, smem, ks);
+        mma(f);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  // acc[mt][nt][v]: MFMA row r = 8*(v/4) + 4*(lane/32) + v%4, col j = lane%32, i.e.
+  // tile row wm*128 + 8*(r&15) + 2*mt + (r>>4), tile col wn*128 + 8*(j&15) + 2*nt + (j>>4).
+  // Slab mt (32 rows) is staged through LDS as staged row s = 2*(r&15) + (r>>4)
+  // (tile row wm*128 + 8*(s>>1) + 2*mt + (s&1)) by 128 columns in tile order.
+  constexpr int SP = 132;  // floats per staged row
+  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
+  const int col0 = n0 + wn * 128;
+  // one slab per call; mt is a compile-time constant so that acc stays in registers
+  auto slab = [&](auto mt_c) {
+    constexpr int mt = decltype(mt_c)::value;
+    auto grow = [&](int s) { return m0 + wm * 128 + 8 * (s >> 1) + 2 * mt + (s & 1); };
+    // ACT_BWD: fetch this slab's g and u first so that their latency overlaps
+    // the staging (rows past M read nothing)
+    u32x4_t gw[8], uw[8];
+    if (EPI == EPI_ACT_BWD) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = grow(q * 4 + (lane >> 4)), col = col0 + (lane & 15) * 8;
+        gw[q] = u32x4_t{0u, 0u, 0u, 0u};
+        uw[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row < p.M && col < p.N) {
+          const int64_t o = (int64_t)row * p.hdim + col;
+          gw[q] = *(const u32x4_t*)(p.g_in + o);
+          uw[q] = *(const u32x4_t*)(p.u_in + o);
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
+        stage[(2 * (r & 15) + (r >> 4)) * SP + 8 * (j & 15) + 2 * nt + (j >> 4)] = acc[mt][nt][v];
+      }
+    __syncthreads();
+    if (EPI == EPI_STORE || EPI == EPI_ACT_BWD) {
+      // lane: 8 consecutive columns of one staged row; 4 rows per pass
+      const int cc = (lane & 15) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int s = q * 4 + (lane >> 4);
+        const int row = grow(s), col = col0 + cc;
+        if (row < p.M && col < p.N) {
+          const float* x = &stage[s * SP + cc];
+          if (EPI == EPI_STORE) {
+            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
+            u32x4_t o;
+            o[0] = pack_bf16x2(x0[0], x0[1]);
+            o[1] = pack_bf16x2(x0[2], x0[3]);
+            o[2] = pack_bf16x2(x1[0], x1[1]);
+            o[3] = pack_bf16x2(x1[2], x1[3]);
+            *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
+          } else {  // staged values are dH
+            u32x4_t odg, odu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float dg[2], du[2];
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                const float g = bf16_to_f32(t ? (gw[q][e] >> 16) : (gw[q][e] & 0xFFFFu));
+                const float u = bf16_to_f32(t ? (uw[q][e] >> 16) : (uw[q][e] & 0xFFFFu));
+                float a, da;
+                act_fwd_bwd(p.act, g, &a, &da);
+                const float d = x[2 * e + t];
+                dg[t] = d * u * da;
+                du[t] = d * a;
+              }
+              odg[e] = pack_bf16x2(dg[0], dg[1]);
+              odu[e] = pack_bf16x2(du[0], du[1]);
+            }
+            const int64_t od = (int64_t)row * (2 * p.hdim) + col;
+            *(u32x4_t*)(p.dgu + od) = odg;
+            *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
+          }
+        }
+      }
+    } else {  // EPI_GATEUP: staged columns [gate j0..+31 | up j0..+31 | gate j0+32.. | up j0+32..]
+      const int jj = (lane & 7) * 8;                       // 0..56: output index within 64
+      const int gcol = (jj >> 5) * 64 + (jj & 31);         // staged gate column (up = +32)
+      const int64_t j = (int64_t)(col0 >> 1) + jj;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s = q * 8 + (lane >> 3);
+        const int row = grow(s);
+        if (row < p.M && col0 < p.N) {
+          const float* gs = &stage[s * SP + gcol];
+          const float* us = gs + 32;
+          u32x4_t og, ou, oh;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float hv[2];
+            uint32_t gb[2], ub[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              gb[t] = f32_to_bf16(gs[2 * e + t]);
+              ub[t] = f32_to_bf16(us[2 * e + t]);
+              hv[t] = act_fwd(p.act, bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
+            }
+            og[e] = gb[0] | (gb[1] << 16);
+            ou[e] = ub[0] | (ub[1] << 16);
+            oh[e] = pack_bf16x2(hv[0], hv[1]);
+          }
+          const int64_t o = (int64_t)row * p.hdim + j;
+          *(u32x4_t*)(p.g_out + o) = og;
+          *(u32x4_t*)(p.u_out + o) = ou;
+          *(u32x4_t*)(p.h_out + o) = oh;
+        }
+      }
+    }
+    __syncthreads();
+  };
+  slab(std::integral_constant<int, 0>());
+  slab(std::integral_constant<int, 1>());
+  slab(std::integral_constant<int, 2>());
+  slab(std::integral_constant<int, 3>());
+}
+
 template <int BSRC, int EPI>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
@@ -498,8 +815,23 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
+  gemm_bf16_kernel<EPI><<<dim3(ntm * ntn), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int BSRC>
 static hipError_t launch_b(const GemmArgs& a, hipStream_t stream) {
+  if (BSRC == BSRC_BF16) {
+    switch (a.epi) {
+      case EPI_STORE: return launch_bf16<EPI_STORE>(a, stream);
+      case EPI_GATEUP: return launch_bf16<EPI_GATEUP>(a, stream);
+      case EPI_ACT_BWD: return launch_bf16<EPI_ACT_BWD>(a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.epi) {
     case EPI_STORE: return launch_t<BSRC, EPI_STORE>(a, stream);
     case EPI_GATEUP: return launch_t<BSRC, EPI_GATEUP>(a, stream);
