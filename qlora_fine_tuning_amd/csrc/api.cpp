@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -228,6 +229,68 @@ hipError_t run_gemm(const GemmArgs& g, int64_t r_alg, hipStream_t st) {
   g_trace.push_back(t);
   return hipSuccess;
 }
+
+
+// ---- helper stream: independent work of one call overlaps the big GEMMs ----
+// One stream (default priority) and a few events per device, created on first
+// use and kept until the process ends. A call forks work onto it with an event
+// recorded on the caller's stream and joins it back before returning, so to the
+// caller everything stays ordered on its own stream. The per-device mutex is
+// held while a call enqueues, so events are never shared by two calls.
+constexpr int kSideEvents = 6;
+struct SideCtx {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t s = nullptr;
+  hipEvent_t ev[kSideEvents];
+};
+constexpr int kMaxDevices = 64;
+SideCtx g_side[kMaxDevices];
+
+// Locks the device's helper context for the duration of one call.
+class Side {
+ public:
+  explicit Side(hipStream_t main) : main_(main) {}
+  ~Side() {
+    if (ctx_) ctx_->mu.unlock();
+  }
+  hipError_t open() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ctx_ = &g_side[dev];
+    ctx_->mu.lock();
+    if (!ctx_->ready) {
+      e = hipStreamCreateWithFlags(&ctx_->s, hipStreamNonBlocking);
+      if (e != hipSuccess) return e;
+      for (int i = 0; i < kSideEvents; ++i) {
+        e = hipEventCreateWithFlags(&ctx_->ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+      }
+      ctx_->ready = true;
+    }
+    return hipSuccess;
+  }
+  hipStream_t stream() const { return ctx_->s; }
+  // the helper stream waits for everything enqueued so far on the caller's stream
+  hipError_t fork(int i) {
+    hipError_t e = hipEventRecord(ctx_->ev[i], main_);
+    return e != hipSuccess ? e : hipStreamWaitEvent(ctx_->s, ctx_->ev[i], 0);
+  }
+  // event i marks what is enqueued so far on the helper stream ...
+  hipError_t mark(int i) { return hipEventRecord(ctx_->ev[i], ctx_->s); }
+  // ... and the caller's stream waits for it
+  hipError_t wait(int i) { return hipStreamWaitEvent(main_, ctx_->ev[i], 0); }
+  hipError_t join(int i) {
+    hipError_t e = mark(i);
+    return e != hipSuccess ? e : wait(i);
+  }
+
+ private:
+  hipStream_t main_;
+  SideCtx* ctx_ = nullptr;
+};
 
 }  // namespace
 
@@ -456,10 +519,19 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
     J.zero(d, KEd - 2 * r, t.bextd + 2 * r, KEd, 1);
     QL_TRY(launch_prep(J, st), "mlp_fwd: LoRA layouts");
   }
-  if (mode == QLORA_DEQUANT_STAGED) {
-    QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
-    QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
-    QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, st), "mlp_fwd: dequant");
+  // staged: the three dequants run on the helper stream while the caller's
+  // stream does the row products; each GEMM waits for its own weight
+  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  Side side(st);
+  if (staged) {
+    QL_TRY(side.open(), "mlp_fwd: helper stream");
+    QL_TRY(side.fork(0), "mlp_fwd: fork");
+    hipStream_t ss = side.stream();
+    QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, ss), "mlp_fwd: dequant");
+    QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, ss), "mlp_fwd: dequant");
+    QL_TRY(side.mark(1), "mlp_fwd: mark");
+    QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
+    QL_TRY(side.mark(2), "mlp_fwd: mark");
   }
   // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
   QL_TRY(launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
@@ -477,6 +549,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   g.Ae = t.uextgu; g.ldae = KEgu; g.Be = t.bextgu; g.ldbe = KEgu;
   g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
   g.epi = EPI_GATEUP; g.g_out = g_save; g.u_out = u_save; g.h_out = t.H; g.hdim = h; g.act = w->act;
+  if (staged) QL_TRY(side.wait(1), "mlp_fwd: wait");
   QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
   // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
   QL_TRY(launch_rowdot(t.H, h, w->a_down, h, (int)m, (int)h, (int)r, s, Ud, nullptr, (int)r, r,
@@ -489,6 +562,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   g2.Ae = t.uextd; g2.ldae = KEd; g2.Be = t.bextd; g2.ldbe = KEd;
   g2.M = (int)m; g2.N = (int)d; g2.K = (int)h; g2.KE = KEd;
   g2.epi = EPI_STORE; g2.C = Y; g2.ldc = d;
+  if (staged) QL_TRY(side.wait(2), "mlp_fwd: join");
   QL_TRY(run_gemm(g2, r, st), "mlp_fwd: down GEMM");
   return QLORA_OK;
 }
@@ -544,25 +618,42 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
     J.zero(d, KEgu - 4 * r, t.bextdx + 4 * r, KEgu, 1);
     QL_TRY(launch_prep(J, st), "mlp_bwd: LoRA layouts");
   }
-  // staged mode: dequantized transposed weights for the two backward GEMMs
+  // The column reductions (dB, dA) and the transposed dequant of the gate/up
+  // weights run on the helper stream, overlapping the row products and the two
+  // GEMMs on the caller's stream; each waits for exactly the tensors it reads.
+  // All column reductions share t.part, so they stay in order on one stream.
   const bool staged = mode == QLORA_DEQUANT_STAGED;
+  Side side(st);
+  QL_TRY(side.open(), "mlp_bwd: helper stream");
+  hipStream_t ss = side.stream();
+  QL_TRY(side.fork(0), "mlp_bwd: fork");
   if (staged) {
-    QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
-           "mlp_bwd: dequant Wd^T");
-    QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, st),
+    QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, ss),
            "mlp_bwd: dequant Wg^T");
-    QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, st),
+    QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, ss),
            "mlp_bwd: dequant Wu^T");
   }
+  QL_TRY(side.mark(1), "mlp_bwd: mark");
+  // dBd = s dY^T Ud (inputs only)
+  QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, d, (int)m, (int)d, Ud, r, (int)r, t.part, ss),
+         "mlp_bwd: dBd partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, gr->b_down, r, 1, ss),
+         "mlp_bwd: dBd");
 
-  // down projection: Td = dY Bd ; dBd = s dY^T Ud
+  // down projection: Td = dY Bd
+  if (staged)
+    QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
+           "mlp_bwd: dequant Wd^T");
   QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
                        t.textd, KEd, KEd, t.rpart, st),
          "mlp_bwd: Td");
-  QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, d, (int)m, (int)d, Ud, r, (int)r, t.part, st),
-         "mlp_bwd: dBd partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, gr->b_down, r, 1, st),
-         "mlp_bwd: dBd");
+  QL_TRY(side.fork(2), "mlp_bwd: fork");
+  // dAd = s Td^T H, H recomputed from g, u (helper stream, beside the dH GEMM)
+  QL_TRY(launch_colreduce(nullptr, g_save, u_save, w->act, h, (int)m, (int)h, t.td, r, (int)r,
+                          t.part, ss),
+         "mlp_bwd: dAd partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->a_down, 1, h, ss),
+         "mlp_bwd: dAd");
   // dH = dY Wd + s Td Ad, with dg, du in the epilogue
   GemmArgs g = gemm_args();
   g.A = dY; g.lda = d;
@@ -572,26 +663,31 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
   QL_TRY(run_gemm(g, r, st), "mlp_bwd: dH GEMM");
-  // dAd = s Td^T H, H recomputed from g, u
-  QL_TRY(launch_colreduce(nullptr, g_save, u_save, w->act, h, (int)m, (int)h, t.td, r, (int)r,
-                          t.part, st),
-         "mlp_bwd: dAd partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->a_down, 1, h, st),
-         "mlp_bwd: dAd");
+  QL_TRY(side.fork(3), "mlp_bwd: fork");
+  // dBg = s dg^T Ug ; dBu = s du^T Uu (helper stream)
+  QL_TRY(launch_colreduce(t.dgu, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Ug, r, (int)r, t.part, ss),
+         "mlp_bwd: dBg partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_gate, r, 1, ss),
+         "mlp_bwd: dBg");
+  QL_TRY(launch_colreduce(t.dgu + h, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Uu, r, (int)r,
+                          t.part, ss),
+         "mlp_bwd: dBu partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_up, r, 1, ss),
+         "mlp_bwd: dBu");
   // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)
   QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s, t.tgu,
                        nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
          "mlp_bwd: Tg, Tu");
-  // dBg = s dg^T Ug ; dBu = s du^T Uu
-  QL_TRY(launch_colreduce(t.dgu, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Ug, r, (int)r, t.part, st),
-         "mlp_bwd: dBg partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_gate, r, 1, st),
-         "mlp_bwd: dBg");
-  QL_TRY(launch_colreduce(t.dgu + h, nullptr, nullptr, 0, 2 * h, (int)m, (int)h, Uu, r, (int)r,
-                          t.part, st),
-         "mlp_bwd: dBu partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_up, r, 1, st),
-         "mlp_bwd: dBu");
+  QL_TRY(side.fork(4), "mlp_bwd: fork");
+  // dAg = s Tg^T X ; dAu = s Tu^T X (helper stream, beside the dX GEMM)
+  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),
+                          t.part, ss),
+         "mlp_bwd: dAg, dAu partials");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), 0, (int)r, s, gr->a_gate, 1, d, ss),
+         "mlp_bwd: dAg");
+  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), (int)r, (int)r, s, gr->a_up, 1,
+                                 d, ss),
+         "mlp_bwd: dAu");
   // dX = [dg | du] [Wg; Wu] + s [Tg | Tu] [Ag; Au]
   if (dX) {
     GemmArgs g2 = gemm_args();
@@ -606,17 +702,10 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
     g2.Ae = t.textgu; g2.ldae = KEgu; g2.Be = t.bextdx; g2.ldbe = KEgu;
     g2.M = (int)m; g2.N = (int)d; g2.K = (int)(2 * h); g2.KE = KEgu;
     g2.epi = EPI_STORE; g2.C = dX; g2.ldc = d;
+    QL_TRY(side.wait(1), "mlp_bwd: wait");   // transposed gate/up weights
     QL_TRY(run_gemm(g2, 2 * r, st), "mlp_bwd: dX GEMM");
   }
-  // dAg = s Tg^T X ; dAu = s Tu^T X
-  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),
-                          t.part, st),
-         "mlp_bwd: dAg, dAu partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), 0, (int)r, s, gr->a_gate, 1, d, st),
-         "mlp_bwd: dAg");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), (int)r, (int)r, s, gr->a_up, 1,
-                                 d, st),
-         "mlp_bwd: dAu");
+  QL_TRY(side.join(5), "mlp_bwd: join");
   return QLORA_OK;
 }
 
