@@ -175,7 +175,7 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.m / (ms / 1e3), 1),
         "wall_s_timed": round(wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (base GEMMs, LoRA as K-extension)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (base GEMMs, LoRA as K-extension)",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "launches_per_step": launches // a.steps,
