@@ -159,6 +159,8 @@ def main():
     launches, gemm_ms, gemm_flops = Q.trace_read()
     Q.trace_enable(False)
 
+    peak_meas, shader_ghz = Q.probe_mfma_peak(20000)
+
     flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
@@ -180,7 +182,10 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "launches_per_step": launches // a.steps,
                      "avg_launch_ms": round(gemm_ms / launches, 4),
-                     "gemm_share_of_step": round(gemm_ms / a.steps / ms, 4)},
+                     "gemm_share_of_step": round(gemm_ms / a.steps / ms, 4),
+                     "measured_mfma_peak": round(peak_meas, 1),
+                     "frac_of_measured_peak": round(achieved / peak_meas, 4),
+                     "shader_ghz_under_mfma_load": round(shader_ghz, 3)},
     }
     if a.cpu_tokens > 0:
         del X, dY, ws, w

@@ -185,6 +185,16 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X,
 int qlora_trace_enable(int on);
 int qlora_trace_read(int64_t* launches, double* total_ms, double* total_flops);
 
+/* ------------------------------------------------------------ diagnostics --
+ * Measures the sustained dense bf16 matrix-core rate of the current device:
+ * 8 blocks of 4 waves per CU, each wave running 8 independent chains of
+ * 32x32x16 bf16 MFMAs, `iters` rounds, on operands with random bits. Reports
+ * the best of three timed launches (after one warm-up) in TFLOP/s and the
+ * shader clock in GHz read on one wave under that load. Enqueues on `stream`
+ * and waits for it (blocking host call). Allocates nothing.
+ * Errors: QLORA_EINVAL (null outputs, iters < 1), QLORA_EHIP. */
+int qlora_probe_mfma_peak(int iters, double* tflops, double* shader_ghz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

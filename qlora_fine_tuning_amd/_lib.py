@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.qlora_mlp_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                     ctypes.POINTER(MlpWeights), c_vp, ctypes.POINTER(MlpGrads),
                                     ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_probe_mfma_peak.restype = ctypes.c_int
+        L.qlora_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
         L.qlora_trace_enable.restype = ctypes.c_int
         L.qlora_trace_enable.argtypes = [ctypes.c_int]
         L.qlora_trace_read.restype = ctypes.c_int
@@ -101,5 +104,5 @@ EXPORTED = [
     "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
     "qlora_nf4_dequant", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
-    "qlora_trace_enable", "qlora_trace_read",
+    "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",
 ]

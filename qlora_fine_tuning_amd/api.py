@@ -94,6 +94,14 @@ def trace_read():
     return n.value, ms.value, fl.value
 
 
+def probe_mfma_peak(iters: int = 20000):
+    """(sustained dense bf16 MFMA TFLOP/s, shader clock GHz) of the current GPU."""
+    tf, ghz = ctypes.c_double(0), ctypes.c_double(0)
+    _lib.check(_lib.lib().qlora_probe_mfma_peak(int(iters), ctypes.byref(tf), ctypes.byref(ghz), _stream()),
+               "qlora_probe_mfma_peak")
+    return tf.value, ghz.value
+
+
 def nf4_levels() -> torch.Tensor:
     buf = (ctypes.c_float * 16)()
     _lib.lib().qlora_nf4_levels(buf)

@@ -312,6 +312,12 @@ const char* qlora_last_error(void) { return g_last_error.c_str(); }
 
 const char* qlora_version(void) { return "qlora-mi355x 0.1 gfx950"; }
 
+int qlora_probe_mfma_peak(int iters, double* tflops, double* shader_ghz, void* stream) {
+  if (!tflops || !shader_ghz || iters < 1) return QLORA_EINVAL;
+  QL_TRY(probe_mfma_peak(iters, (hipStream_t)stream, tflops, shader_ghz), "probe_mfma_peak");
+  return QLORA_OK;
+}
+
 int qlora_trace_enable(int on) {
   trace_clear();
   g_trace_on = on != 0;

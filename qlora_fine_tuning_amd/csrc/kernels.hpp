@@ -125,4 +125,9 @@ struct PrepJobs {
 hipError_t launch_prep(const PrepJobs& jobs, hipStream_t stream);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t stream);
 
+// ---- diagnostics (probe.hip) ----
+// Sustained dense bf16 MFMA TFLOP/s and the shader clock (GHz) under that
+// load; synchronizes the host.
+hipError_t probe_mfma_peak(int iters, hipStream_t stream, double* tflops, double* ghz);
+
 }  // namespace qlora

@@ -128,3 +128,10 @@ def test_mlp_validation_errors(L):
     assert f(*args(bad)) == -1
     assert f(FAKE, 0, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == 0
     assert f(FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == -1
+
+
+def test_probe_validation_errors(L):
+    d = ctypes.c_double(0)
+    assert L.qlora_probe_mfma_peak(100, None, ctypes.byref(d), None) == -1
+    assert L.qlora_probe_mfma_peak(100, ctypes.byref(d), None, None) == -1
+    assert L.qlora_probe_mfma_peak(0, ctypes.byref(d), ctypes.byref(d), None) == -1
