@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--workload", default="llama7b_mlp",
                    choices=["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"])
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
+    p.add_argument("--base", default="nf4", choices=["nf4", "bf16"],
+                   help="base weights: NF4 (QLoRA, default) or bf16 (16-bit LoRA variant)")
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="token sample of the CPU oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -129,18 +131,27 @@ def main():
     cfg = {"llama7b_mlp": I.LLAMA_MLP, "mistral7b_mlp": I.MISTRAL_MLP,
            "gemma7b_mlp": I.GEMMA_MLP}[a.workload]
     dev = "cuda:0"
-    d = I.mlp_inputs(cfg, dense_w=False)
-    nf = lambda wn: Q.NF4Weight(d[wn + "_codes"].to(dev), d[wn + "_absmax"].to(dev))  # noqa: E731
-    w = Q.MlpWeights(nf("Wg"), nf("Wu"), nf("Wd"),
-                     *(d[k].to(dev) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")),
-                     s=cfg.s, act=cfg.act)
+    w16 = a.base == "bf16"
+    d = I.mlp_inputs(cfg, dense_w=w16)
+    lora = [d[k].to(dev) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")]
+    if w16:
+        w = Q.Mlp16Weights(d["Wg"].to(dev), d["Wu"].to(dev), d["Wd"].to(dev), *lora, s=cfg.s,
+                           act=cfg.act)
+        nbytes = Q.mlp16_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r)
+    else:
+        nf = lambda wn: Q.NF4Weight(d[wn + "_codes"].to(dev), d[wn + "_absmax"].to(dev))  # noqa: E731
+        w = Q.MlpWeights(nf("Wg"), nf("Wu"), nf("Wd"), *lora, s=cfg.s, act=cfg.act)
+        nbytes = Q.mlp_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r, a.mode)
     X, dY = d["X"].to(dev), d["dY"].to(dev)
-    ws = torch.empty(Q.mlp_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r, a.mode), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step():
-        _, sv = Q.mlp_fwd(X, w, mode=a.mode, ws=ws)
-        Q.mlp_bwd(dY, X, sv, w, mode=a.mode, ws=ws)
+        if w16:
+            _, sv = Q.mlp16_fwd(X, w, ws=ws)
+            Q.mlp16_bwd(dY, X, sv, w, ws=ws)
+        else:
+            _, sv = Q.mlp_fwd(X, w, mode=a.mode, ws=ws)
+            Q.mlp_bwd(dY, X, sv, w, mode=a.mode, ws=ws)
 
     for _ in range(a.warmup):
         step()
@@ -164,16 +175,17 @@ def main():
     flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
-    traffic = gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"), cfg.name,
-                           "staged" if a.mode == "auto" else a.mode)
+    traffic = None if w16 else gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"),
+                                            cfg.name, "staged" if a.mode == "auto" else a.mode)
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.m, "d": cfg.d, "h": cfg.h, "r": cfg.r,
-                   "s": cfg.s, "act": cfg.act, "weights": "nf4 blocksize 64, fp32 absmax",
-                   "dequant_mode": a.mode, "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
+                   "s": cfg.s, "act": cfg.act,
+                   "weights": "bf16 (16-bit LoRA)" if w16 else "nf4 blocksize 64, fp32 absmax",
+                   "dequant_mode": "none" if w16 else a.mode, "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.m / (ms / 1e3), 1),
         "wall_s_timed": round(wall, 3),
@@ -187,7 +199,7 @@ def main():
                      "frac_of_measured_peak": round(achieved / peak_meas, 4),
                      "shader_ghz_under_mfma_load": round(shader_ghz, 3)},
     }
-    if a.cpu_tokens > 0:
+    if a.cpu_tokens > 0 and not w16:
         del X, dY, ws, w
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(cfg, d, min(a.cpu_tokens, cfg.m))

@@ -34,9 +34,10 @@
  *   - Validation errors return before anything is enqueued. A HIP launch
  *     failure returns QLORA_EHIP; qlora_last_error() then gives the HIP
  *     message (per thread).
- *   - Shape limits: k, n (and d, h) multiples of 64; m >= 0 (m == 0 is a
- *     no-op); 1 <= r <= 64 (1 <= r <= 32 for the MLP). Output buffers must
- *     not alias inputs.
+ *   - Shape limits: k, n (and d, h) multiples of 64; m >= 0; 1 <= r <= 64
+ *     (1 <= r <= 32 for the MLP). m == 0 writes only the LoRA gradients (as
+ *     zeros); the per-token tensors may then be NULL. Output buffers must not
+ *     alias inputs.
  *   - Results are deterministic: two identical calls give identical bits
  *     (no floating-point atomics; fixed reduction order).
  *   - Calls that share one workspace buffer must not overlap in time.
@@ -170,6 +171,59 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X,
                   int64_t m, const qlora_mlp_weights* w,
                   uint16_t* dX, const qlora_mlp_grads* grads, int mode,
                   void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------- 16-bit base weights --
+ * The same linear layer and gated MLP with an unquantized bf16 base weight
+ * (plain LoRA on a 16-bit model, which the pages offer beside QLoRA: Show HN
+ * thread, "QLoRA / LoRA" feature list; "Introducing Unsloth", supported
+ * fine-tuning modes). W [n][k] bf16 replaces the NF4 weight; everything else,
+ * including the saved set, the workspace rules and the results' definition,
+ * is as above. RSLoRA is the caller's choice of s (alpha / sqrt(r)).
+ * The forward reads W as it is (the MLP copies gate/up into an interleaved
+ * layout in the workspace); the backward transposes W into the workspace for
+ * the dX product. */
+size_t qlora_linear16_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r);
+
+int qlora_linear16_fwd(const uint16_t* X, int64_t m, const uint16_t* W, int64_t n, int64_t k,
+                       const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                       uint16_t* Y, float* U_save, void* ws, size_t ws_bytes, void* stream);
+
+int qlora_linear16_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m,
+                       const uint16_t* W, int64_t n, int64_t k,
+                       const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                       uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* MLP with bf16 base weights: gate, up [h][d], down [d][h]. Passed by HOST
+ * pointer. */
+typedef struct qlora_mlp16_weights {
+  const uint16_t* gate;
+  const uint16_t* up;
+  const uint16_t* down;
+  const uint16_t* a_gate; /* [r][d] */
+  const uint16_t* b_gate; /* [h][r] */
+  const uint16_t* a_up;   /* [r][d] */
+  const uint16_t* b_up;   /* [h][r] */
+  const uint16_t* a_down; /* [r][h] */
+  const uint16_t* b_down; /* [d][r] */
+  int64_t d, h, r;
+  float s;
+  int act;   /* qlora_act */
+} qlora_mlp16_weights;
+
+size_t qlora_mlp16_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r);
+
+int qlora_mlp16_fwd(const uint16_t* X, int64_t m, const qlora_mlp16_weights* w,
+                    uint16_t* Y, uint16_t* g_save, uint16_t* u_save,
+                    float* Ug, float* Uu, float* Ud,
+                    void* ws, size_t ws_bytes, void* stream);
+
+int qlora_mlp16_bwd(const uint16_t* dY, const uint16_t* X,
+                    const uint16_t* g_save, const uint16_t* u_save,
+                    const float* Ug, const float* Uu, const float* Ud,
+                    int64_t m, const qlora_mlp16_weights* w,
+                    uint16_t* dX, const qlora_mlp_grads* grads,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- tracing --
  * Kernel timing aid for benchmarks and profiling. While enabled, every

@@ -10,6 +10,8 @@ __all__ = [
     "NF4Weight", "MlpWeights", "version", "nf4_levels", "nf4_dequant",
     "linear_workspace_bytes", "linear_fwd", "linear_bwd",
     "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read", "probe_mfma_peak",
+    "linear16_workspace_bytes", "linear16_fwd", "linear16_bwd",
+    "Mlp16Weights", "mlp16_workspace_bytes", "mlp16_fwd", "mlp16_bwd",
 ]
 
 

@@ -35,6 +35,13 @@ class MlpWeights(ctypes.Structure):
                 ("d", c_i64), ("h", c_i64), ("r", c_i64), ("s", ctypes.c_float), ("act", ctypes.c_int)]
 
 
+class Mlp16Weights(ctypes.Structure):
+    _fields_ = [("gate", c_vp), ("up", c_vp), ("down", c_vp),
+                ("a_gate", c_vp), ("b_gate", c_vp), ("a_up", c_vp), ("b_up", c_vp),
+                ("a_down", c_vp), ("b_down", c_vp),
+                ("d", c_i64), ("h", c_i64), ("r", c_i64), ("s", ctypes.c_float), ("act", ctypes.c_int)]
+
+
 class MlpGrads(ctypes.Structure):
     _fields_ = [("a_gate", c_vp), ("b_gate", c_vp), ("a_up", c_vp), ("b_up", c_vp),
                 ("a_down", c_vp), ("b_down", c_vp)]
@@ -80,6 +87,24 @@ def lib() -> ctypes.CDLL:
         L.qlora_mlp_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                     ctypes.POINTER(MlpWeights), c_vp, ctypes.POINTER(MlpGrads),
                                     ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_linear16_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_linear16_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64]
+        L.qlora_linear16_fwd.restype = ctypes.c_int
+        L.qlora_linear16_fwd.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64,
+                                         ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_linear16_bwd.restype = ctypes.c_int
+        L.qlora_linear16_bwd.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp,
+                                         c_i64, ctypes.c_float, c_vp, c_vp, c_vp, c_vp,
+                                         ctypes.c_size_t, c_vp]
+        L.qlora_mlp16_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_mlp16_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64]
+        L.qlora_mlp16_fwd.restype = ctypes.c_int
+        L.qlora_mlp16_fwd.argtypes = [c_vp, c_i64, ctypes.POINTER(Mlp16Weights), c_vp, c_vp, c_vp,
+                                      c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_mlp16_bwd.restype = ctypes.c_int
+        L.qlora_mlp16_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                      ctypes.POINTER(Mlp16Weights), c_vp, ctypes.POINTER(MlpGrads),
+                                      c_vp, ctypes.c_size_t, c_vp]
         L.qlora_probe_mfma_peak.restype = ctypes.c_int
         L.qlora_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
@@ -105,4 +130,6 @@ EXPORTED = [
     "qlora_nf4_dequant", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",
+    "qlora_linear16_workspace_bytes", "qlora_linear16_fwd", "qlora_linear16_bwd",
+    "qlora_mlp16_workspace_bytes", "qlora_mlp16_fwd", "qlora_mlp16_bwd",
 ]

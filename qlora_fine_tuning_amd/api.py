@@ -243,3 +243,138 @@ def mlp_bwd(dY, X, saved, w: MlpWeights, need_dx=True, mode="auto", ws=None):
                                   _lib.MODE[mode], _ptr(ws), ws.numel(), _stream())
     _lib.check(st, "qlora_mlp_bwd")
     return out
+
+
+# ------------------------------------------------------ 16-bit base weights --
+def linear16_workspace_bytes(m, k, n, r) -> int:
+    return int(_lib.lib().qlora_linear16_workspace_bytes(m, k, n, r))
+
+
+def linear16_fwd(X, W, A, B, s: float, ws=None):
+    """bf16 base weight W [n][k]. Returns (Y [m][n] bf16, U [m][r] fp32)."""
+    m, k, n, r = X.shape[0], W.shape[1], W.shape[0], A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(W, "W", torch.bfloat16, (n, k))
+    _need(A, "A", torch.bfloat16, (r, k))
+    _need(B, "B", torch.bfloat16, (n, r))
+    Y = torch.empty((m, n), dtype=torch.bfloat16, device=X.device)
+    U = torch.empty((m, r), dtype=torch.float32, device=X.device)
+    nb = linear16_workspace_bytes(m, k, n, r)
+    ws = workspace(nb, X.device) if ws is None else ws
+    st = _lib.lib().qlora_linear16_fwd(_ptr(X), m, _ptr(W), n, k, _ptr(A), _ptr(B), r, float(s),
+                                       _ptr(Y), _ptr(U), _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_linear16_fwd")
+    return Y, U
+
+
+def linear16_bwd(dY, X, U, W, A, B, s: float, need_dx=True, ws=None):
+    """Returns (dX [m][k] or None, dA [r][k], dB [n][r]), all bf16."""
+    m, k, n, r = X.shape[0], W.shape[1], W.shape[0], A.shape[0]
+    _need(dY, "dY", torch.bfloat16, (m, n))
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(U, "U", torch.float32, (m, r))
+    _need(W, "W", torch.bfloat16, (n, k))
+    _need(A, "A", torch.bfloat16, (r, k))
+    _need(B, "B", torch.bfloat16, (n, r))
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=X.device) if need_dx else None
+    dA = torch.empty((r, k), dtype=torch.bfloat16, device=X.device)
+    dB = torch.empty((n, r), dtype=torch.bfloat16, device=X.device)
+    nb = linear16_workspace_bytes(m, k, n, r)
+    ws = workspace(nb, X.device) if ws is None else ws
+    st = _lib.lib().qlora_linear16_bwd(_ptr(dY), _ptr(X), _ptr(U), m, _ptr(W), n, k, _ptr(A),
+                                       _ptr(B), r, float(s), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                       ws.numel(), _stream())
+    _lib.check(st, "qlora_linear16_bwd")
+    return dX, dA, dB
+
+
+@dataclasses.dataclass
+class Mlp16Weights:
+    """Gated MLP with bf16 base weights: gate, up [h][d], down [d][h]."""
+    gate: torch.Tensor
+    up: torch.Tensor
+    down: torch.Tensor
+    a_gate: torch.Tensor
+    b_gate: torch.Tensor
+    a_up: torch.Tensor
+    b_up: torch.Tensor
+    a_down: torch.Tensor
+    b_down: torch.Tensor
+    s: float
+    act: str = "swiglu"
+
+    @property
+    def d(self):
+        return self.gate.shape[1]
+
+    @property
+    def h(self):
+        return self.gate.shape[0]
+
+    @property
+    def r(self):
+        return self.a_gate.shape[0]
+
+    def c_struct(self) -> _lib.Mlp16Weights:
+        d, h, r = self.d, self.h, self.r
+        for name, t, shape in (("gate", self.gate, (h, d)), ("up", self.up, (h, d)),
+                               ("down", self.down, (d, h)),
+                               ("a_gate", self.a_gate, (r, d)), ("a_up", self.a_up, (r, d)),
+                               ("a_down", self.a_down, (r, h)), ("b_gate", self.b_gate, (h, r)),
+                               ("b_up", self.b_up, (h, r)), ("b_down", self.b_down, (d, r))):
+            _need(t, name, torch.bfloat16, shape)
+        return _lib.Mlp16Weights(self.gate.data_ptr(), self.up.data_ptr(), self.down.data_ptr(),
+                                 self.a_gate.data_ptr(), self.b_gate.data_ptr(), self.a_up.data_ptr(),
+                                 self.b_up.data_ptr(), self.a_down.data_ptr(), self.b_down.data_ptr(),
+                                 d, h, r, float(self.s), _lib.ACT[self.act])
+
+
+def mlp16_workspace_bytes(m, d, h, r) -> int:
+    return int(_lib.lib().qlora_mlp16_workspace_bytes(m, d, h, r))
+
+
+def mlp16_fwd(X, w: Mlp16Weights, ws=None):
+    """Returns (Y [m][d] bf16, saved) with saved = dict(g, u, Ug, Uu, Ud)."""
+    m, d, h, r = X.shape[0], w.d, w.h, w.r
+    _need(X, "X", torch.bfloat16, (m, d))
+    dev = X.device
+    Y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    saved = dict(g=torch.empty((m, h), dtype=torch.bfloat16, device=dev),
+                 u=torch.empty((m, h), dtype=torch.bfloat16, device=dev),
+                 Ug=torch.empty((m, r), dtype=torch.float32, device=dev),
+                 Uu=torch.empty((m, r), dtype=torch.float32, device=dev),
+                 Ud=torch.empty((m, r), dtype=torch.float32, device=dev))
+    nb = mlp16_workspace_bytes(m, d, h, r)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = _lib.lib().qlora_mlp16_fwd(_ptr(X), m, ctypes.byref(cw), _ptr(Y), _ptr(saved["g"]),
+                                    _ptr(saved["u"]), _ptr(saved["Ug"]), _ptr(saved["Uu"]),
+                                    _ptr(saved["Ud"]), _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_mlp16_fwd")
+    return Y, saved
+
+
+def mlp16_bwd(dY, X, saved, w: Mlp16Weights, need_dx=True, ws=None):
+    """Returns dict(dX, dAg, dBg, dAu, dBu, dAd, dBd), all bf16."""
+    m, d, h, r = X.shape[0], w.d, w.h, w.r
+    _need(dY, "dY", torch.bfloat16, (m, d))
+    _need(X, "X", torch.bfloat16, (m, d))
+    for k_, sh, dt in (("g", (m, h), torch.bfloat16), ("u", (m, h), torch.bfloat16),
+                       ("Ug", (m, r), torch.float32), ("Uu", (m, r), torch.float32),
+                       ("Ud", (m, r), torch.float32)):
+        _need(saved[k_], k_, dt, sh)
+    dev = X.device
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    out = dict(dX=e(m, d) if need_dx else None, dAg=e(r, d), dBg=e(h, r), dAu=e(r, d),
+               dBu=e(h, r), dAd=e(r, h), dBd=e(d, r))
+    grads = _lib.MlpGrads(out["dAg"].data_ptr(), out["dBg"].data_ptr(), out["dAu"].data_ptr(),
+                          out["dBu"].data_ptr(), out["dAd"].data_ptr(), out["dBd"].data_ptr())
+    nb = mlp16_workspace_bytes(m, d, h, r)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = _lib.lib().qlora_mlp16_bwd(_ptr(dY), _ptr(X), _ptr(saved["g"]), _ptr(saved["u"]),
+                                    _ptr(saved["Ug"]), _ptr(saved["Uu"]), _ptr(saved["Ud"]), m,
+                                    ctypes.byref(cw), _ptr(out["dX"]), ctypes.byref(grads),
+                                    _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, "qlora_mlp16_bwd")
+    return out

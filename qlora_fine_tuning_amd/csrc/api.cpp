@@ -59,6 +59,30 @@ inline int64_t ceil16(int64_t x) { return (x + 15) / 16 * 16; }
 
 bool bad_nf4(const qlora_nf4& w) { return !w.codes || !w.absmax; }
 
+// Base-weight source: NF4 (codes + absmax) or, in MODE_BF16, a bf16 matrix
+// used as it is (16-bit LoRA: the dequantization step becomes nothing, a copy
+// or a transpose).
+constexpr int MODE_BF16 = 3;
+struct WSrc {
+  const uint8_t* codes = nullptr;
+  const float* absmax = nullptr;
+  const uint16_t* w16 = nullptr;
+  int64_t n = 0, k = 0;
+};
+WSrc src_nf4(const qlora_nf4& w) {
+  WSrc s;
+  s.codes = w.codes; s.absmax = w.absmax; s.n = w.n; s.k = w.k;
+  return s;
+}
+WSrc src_w16(const uint16_t* w, int64_t n, int64_t k) {
+  WSrc s;
+  s.w16 = w; s.n = n; s.k = k;
+  return s;
+}
+bool bad_src(const WSrc& w, int mode) { return mode == MODE_BF16 ? !w.w16 : (!w.codes || !w.absmax); }
+// a bf16 copy of the weight (or of its transpose) lives in the workspace
+bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE_BF16; }
+
 int resolve_mode(int mode) {
   if (mode == QLORA_DEQUANT_AUTO) return QLORA_DEQUANT_STAGED;
   return mode;
@@ -104,7 +128,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.t = c.take<float>(m * r);
   t.text = c.take<uint16_t>(m * KE);
   t.part = c.take<float>(chunks * std::max(n, k) * r);
-  t.wt = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(k * n) : nullptr;
+  t.wt = staged_like(mode) ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
   if (w) *w = t;
   return c.off;
@@ -132,9 +156,8 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.uextgu = c.take<uint16_t>(m * KEgu);
   t.uextd = c.take<uint16_t>(m * KEd);
   t.H = c.take<uint16_t>(m * h);
-  const bool staged = mode == QLORA_DEQUANT_STAGED;
-  t.wgu = staged ? c.take<uint16_t>(2 * h * d) : nullptr;
-  t.wd = staged ? c.take<uint16_t>(d * h) : nullptr;
+  t.wgu = staged_like(mode) ? c.take<uint16_t>(2 * h * d) : nullptr;
+  t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
   t.rpart = c.take<float>(16 * m * 2 * r);
   if (w) *w = t;
   return c.off;
@@ -170,9 +193,8 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.tgu = c.take<float>(m * 2 * r);
   t.textgu = c.take<uint16_t>(m * KEgu);
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
-  const bool staged = mode == QLORA_DEQUANT_STAGED;
-  t.wdt = staged ? c.take<uint16_t>(h * d) : nullptr;
-  t.wgut = staged ? c.take<uint16_t>(d * 2 * h) : nullptr;
+  t.wdt = staged_like(mode) ? c.take<uint16_t>(h * d) : nullptr;
+  t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
   t.rpart = c.take<float>(16 * m * 2 * r);
   if (w) *w = t;
   return c.off;
@@ -351,22 +373,31 @@ int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream) {
 }
 
 // ------------------------------------------------------------ linear layer --
-size_t qlora_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
-  if (!dims_ok(m, k, n) || r < 1 || r > 64 || !valid_mode(mode)) return 0;
-  mode = resolve_mode(mode);
+static size_t linear_ws(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
   Carver a(nullptr), b(nullptr);
   return std::max(plan_linear_fwd(a, m, k, n, r, mode, nullptr), plan_linear_bwd(b, m, k, n, r, mode, nullptr));
 }
 
-int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* A,
-                     const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save, int mode,
-                     void* ws, size_t ws_bytes, void* stream) {
-  if (!X || !A || !B || !Y || bad_nf4(w)) return QLORA_EINVAL;
-  if (r < 1 || r > 64 || !std::isfinite(s) || !valid_mode(mode)) return QLORA_EINVAL;
+size_t qlora_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
+  if (!dims_ok(m, k, n) || r < 1 || r > 64 || !valid_mode(mode)) return 0;
+  return linear_ws(m, k, n, r, resolve_mode(mode));
+}
+
+size_t qlora_linear16_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r) {
+  if (!dims_ok(m, k, n) || r < 1 || r > 64) return 0;
+  return linear_ws(m, k, n, r, MODE_BF16);
+}
+
+// mode: QLORA_DEQUANT_STAGED, QLORA_DEQUANT_FUSED or MODE_BF16 (resolved)
+static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const uint16_t* A,
+                           const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save,
+                           int mode, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !B || bad_src(w, mode)) return QLORA_EINVAL;
+  if (m > 0 && (!X || !Y)) return QLORA_EINVAL;   // per-token tensors may be NULL when m == 0
+  if (r < 1 || r > 64 || !std::isfinite(s)) return QLORA_EINVAL;
   const int64_t k = w.k, n = w.n;
   if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
-  mode = resolve_mode(mode);
-  const size_t need = qlora_linear_workspace_bytes(m, k, n, r, mode);
+  const size_t need = linear_ws(m, k, n, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   if (m == 0) return QLORA_OK;
   hipStream_t st = (hipStream_t)stream;
@@ -390,6 +421,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* 
   GemmArgs g = gemm_args();
   g.A = X; g.lda = k;
   if (mode == QLORA_DEQUANT_STAGED) { g.bsrc = BSRC_BF16; g.B = t.wbf; g.ldb = k; }
+  else if (mode == MODE_BF16) { g.bsrc = BSRC_BF16; g.B = w.w16; g.ldb = k; }
   else { g.bsrc = BSRC_NF4; g.codes0 = w.codes; g.absmax0 = w.absmax; }
   g.Ae = t.uext; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
   g.M = (int)m; g.N = (int)n; g.K = (int)k; g.KE = KE;
@@ -398,16 +430,16 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* 
   return QLORA_OK;
 }
 
-int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m, qlora_nf4 w,
-                     const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* dX,
-                     uint16_t* dA, uint16_t* dB, int mode, void* ws, size_t ws_bytes,
-                     void* stream) {
-  if (!dY || !X || !U || !A || !B || !dA || !dB || bad_nf4(w)) return QLORA_EINVAL;
-  if (r < 1 || r > 64 || !std::isfinite(s) || !valid_mode(mode)) return QLORA_EINVAL;
+static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m,
+                           const WSrc& w, const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                           uint16_t* dX, uint16_t* dA, uint16_t* dB, int mode, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!A || !B || !dA || !dB || bad_src(w, mode)) return QLORA_EINVAL;
+  if (m > 0 && (!dY || !X || !U)) return QLORA_EINVAL;   // may be NULL when m == 0
+  if (r < 1 || r > 64 || !std::isfinite(s)) return QLORA_EINVAL;
   const int64_t k = w.k, n = w.n;
   if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
-  mode = resolve_mode(mode);
-  const size_t need = qlora_linear_workspace_bytes(m, k, n, r, mode);
+  const size_t need = linear_ws(m, k, n, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (m == 0) {  // empty batch: zero weight gradients
@@ -444,9 +476,12 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   if (dX) {
     GemmArgs g = gemm_args();
     g.A = dY; g.lda = n;
-    if (mode == QLORA_DEQUANT_STAGED) {
-      QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
-             "linear_bwd: dequant W^T");
+    if (staged_like(mode)) {
+      if (mode == MODE_BF16)
+        QL_TRY(launch_w16_transpose(w.w16, n, k, t.wt, n, 0, st), "linear_bwd: W^T");
+      else
+        QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
+               "linear_bwd: dequant W^T");
       g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = n;
     } else {
       g.bsrc = BSRC_NF4_T; g.codes0 = w.codes; g.absmax0 = w.absmax;
@@ -464,38 +499,102 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int6
   return QLORA_OK;
 }
 
-// --------------------------------------------------------------- gated MLP --
-static int check_mlp(const qlora_mlp_weights* w, int mode) {
-  if (!w) return QLORA_EINVAL;
-  if (bad_nf4(w->gate) || bad_nf4(w->up) || bad_nf4(w->down)) return QLORA_EINVAL;
-  if (!w->a_gate || !w->b_gate || !w->a_up || !w->b_up || !w->a_down || !w->b_down) return QLORA_EINVAL;
-  if (w->r < 1 || w->r > 32 || !std::isfinite(w->s)) return QLORA_EINVAL;
-  if (w->act != QLORA_ACT_SWIGLU && w->act != QLORA_ACT_GEGLU_TANH) return QLORA_EINVAL;
+int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* A,
+                     const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save, int mode,
+                     void* ws, size_t ws_bytes, void* stream) {
   if (!valid_mode(mode)) return QLORA_EINVAL;
-  const int64_t d = w->d, h = w->h;
+  return linear_fwd_impl(X, m, src_nf4(w), A, B, r, s, Y, U_save, resolve_mode(mode), ws, ws_bytes,
+                         stream);
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m, qlora_nf4 w,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* dX,
+                     uint16_t* dA, uint16_t* dB, int mode, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!valid_mode(mode)) return QLORA_EINVAL;
+  return linear_bwd_impl(dY, X, U, m, src_nf4(w), A, B, r, s, dX, dA, dB, resolve_mode(mode), ws,
+                         ws_bytes, stream);
+}
+
+int qlora_linear16_fwd(const uint16_t* X, int64_t m, const uint16_t* W, int64_t n, int64_t k,
+                       const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* Y,
+                       float* U_save, void* ws, size_t ws_bytes, void* stream) {
+  return linear_fwd_impl(X, m, src_w16(W, n, k), A, B, r, s, Y, U_save, MODE_BF16, ws, ws_bytes,
+                         stream);
+}
+
+int qlora_linear16_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m,
+                       const uint16_t* W, int64_t n, int64_t k, const uint16_t* A,
+                       const uint16_t* B, int64_t r, float s, uint16_t* dX, uint16_t* dA,
+                       uint16_t* dB, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(dY, X, U, m, src_w16(W, n, k), A, B, r, s, dX, dA, dB, MODE_BF16, ws,
+                         ws_bytes, stream);
+}
+
+// --------------------------------------------------------------- gated MLP --
+// MLP weights with their base-weight sources (NF4 or bf16)
+struct MlpSrc {
+  WSrc gate, up, down;
+  const uint16_t *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;
+  int64_t d, h, r;
+  float s;
+  int act;
+};
+
+static MlpSrc mlp_src(const qlora_mlp_weights* w) {
+  MlpSrc m;
+  m.gate = src_nf4(w->gate); m.up = src_nf4(w->up); m.down = src_nf4(w->down);
+  m.a_gate = w->a_gate; m.b_gate = w->b_gate; m.a_up = w->a_up; m.b_up = w->b_up;
+  m.a_down = w->a_down; m.b_down = w->b_down;
+  m.d = w->d; m.h = w->h; m.r = w->r; m.s = w->s; m.act = w->act;
+  return m;
+}
+
+static MlpSrc mlp_src16(const qlora_mlp16_weights* w) {
+  MlpSrc m;
+  m.gate = src_w16(w->gate, w->h, w->d); m.up = src_w16(w->up, w->h, w->d);
+  m.down = src_w16(w->down, w->d, w->h);
+  m.a_gate = w->a_gate; m.b_gate = w->b_gate; m.a_up = w->a_up; m.b_up = w->b_up;
+  m.a_down = w->a_down; m.b_down = w->b_down;
+  m.d = w->d; m.h = w->h; m.r = w->r; m.s = w->s; m.act = w->act;
+  return m;
+}
+
+static int check_mlp(const MlpSrc& w, int mode) {
+  if (bad_src(w.gate, mode) || bad_src(w.up, mode) || bad_src(w.down, mode)) return QLORA_EINVAL;
+  if (!w.a_gate || !w.b_gate || !w.a_up || !w.b_up || !w.a_down || !w.b_down) return QLORA_EINVAL;
+  if (w.r < 1 || w.r > 32 || !std::isfinite(w.s)) return QLORA_EINVAL;
+  if (w.act != QLORA_ACT_SWIGLU && w.act != QLORA_ACT_GEGLU_TANH) return QLORA_EINVAL;
+  const int64_t d = w.d, h = w.h;
   if (!dims_ok(0, d, h)) return QLORA_ESHAPE;
-  if (w->gate.n != h || w->gate.k != d || w->up.n != h || w->up.k != d || w->down.n != d ||
-      w->down.k != h)
+  if (w.gate.n != h || w.gate.k != d || w.up.n != h || w.up.k != d || w.down.n != d || w.down.k != h)
     return QLORA_ESHAPE;
   return QLORA_OK;
 }
 
-size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
-  if (!dims_ok(m, d, h) || r < 1 || r > 32 || !valid_mode(mode)) return 0;
-  mode = resolve_mode(mode);
+static size_t mlp_ws(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
   Carver a(nullptr), b(nullptr);
   return std::max(plan_mlp_fwd(a, m, d, h, r, mode, nullptr), plan_mlp_bwd(b, m, d, h, r, mode, nullptr));
 }
 
-int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint16_t* Y,
-                  uint16_t* g_save, uint16_t* u_save, float* Ug, float* Uu, float* Ud, int mode,
-                  void* ws, size_t ws_bytes, void* stream) {
-  if (int e = check_mlp(w, mode)) return e;
-  if (!X || !Y || !g_save || !u_save || !Ug || !Uu || !Ud) return QLORA_EINVAL;
+size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
+  if (!dims_ok(m, d, h) || r < 1 || r > 32 || !valid_mode(mode)) return 0;
+  return mlp_ws(m, d, h, r, resolve_mode(mode));
+}
+
+size_t qlora_mlp16_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r) {
+  if (!dims_ok(m, d, h) || r < 1 || r > 32) return 0;
+  return mlp_ws(m, d, h, r, MODE_BF16);
+}
+
+static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t* Y,
+                        uint16_t* g_save, uint16_t* u_save, float* Ug, float* Uu, float* Ud, int mode,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_mlp(*w, mode)) return e;
+  if (m > 0 && (!X || !Y || !g_save || !u_save || !Ug || !Uu || !Ud)) return QLORA_EINVAL;
   const int64_t d = w->d, h = w->h, r = w->r;
   if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
-  mode = resolve_mode(mode);
-  const size_t need = qlora_mlp_workspace_bytes(m, d, h, r, mode);
+  const size_t need = mlp_ws(m, d, h, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   if (m == 0) return QLORA_OK;
   hipStream_t st = (hipStream_t)stream;
@@ -527,16 +626,23 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   }
   // staged: the three dequants run on the helper stream while the caller's
   // stream does the row products; each GEMM waits for its own weight
-  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  const bool staged = staged_like(mode);
+  const bool w16 = mode == MODE_BF16;
   Side side(st);
   if (staged) {
     QL_TRY(side.open(), "mlp_fwd: helper stream");
     QL_TRY(side.fork(0), "mlp_fwd: fork");
     hipStream_t ss = side.stream();
-    QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, ss), "mlp_fwd: dequant");
-    QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, ss), "mlp_fwd: dequant");
-    QL_TRY(side.mark(1), "mlp_fwd: mark");
-    QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
+    if (w16) {   // 16-bit base: interleave copy of gate/up; down is used as it is
+      QL_TRY(launch_w16_rows(w->gate.w16, h, d, t.wgu, d, 1, ss), "mlp_fwd: gate/up copy");
+      QL_TRY(launch_w16_rows(w->up.w16, h, d, t.wgu, d, 2, ss), "mlp_fwd: gate/up copy");
+      QL_TRY(side.mark(1), "mlp_fwd: mark");
+    } else {
+      QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, ss), "mlp_fwd: dequant");
+      QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, ss), "mlp_fwd: dequant");
+      QL_TRY(side.mark(1), "mlp_fwd: mark");
+      QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
+    }
     QL_TRY(side.mark(2), "mlp_fwd: mark");
   }
   // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
@@ -546,7 +652,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   // gate || up GEMM with the activation epilogue
   GemmArgs g = gemm_args();
   g.A = X; g.lda = d;
-  if (mode == QLORA_DEQUANT_STAGED) { g.bsrc = BSRC_BF16; g.B = t.wgu; g.ldb = d; }
+  if (staged) { g.bsrc = BSRC_BF16; g.B = t.wgu; g.ldb = d; }
   else {
     g.bsrc = BSRC_NF4_PAIR;
     g.codes0 = w->gate.codes; g.absmax0 = w->gate.absmax;
@@ -563,7 +669,8 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
          "mlp_fwd: Ud");
   GemmArgs g2 = gemm_args();
   g2.A = t.H; g2.lda = h;
-  if (mode == QLORA_DEQUANT_STAGED) { g2.bsrc = BSRC_BF16; g2.B = t.wd; g2.ldb = h; }
+  if (w16) { g2.bsrc = BSRC_BF16; g2.B = w->down.w16; g2.ldb = h; }
+  else if (staged) { g2.bsrc = BSRC_BF16; g2.B = t.wd; g2.ldb = h; }
   else { g2.bsrc = BSRC_NF4; g2.codes0 = w->down.codes; g2.absmax0 = w->down.absmax; }
   g2.Ae = t.uextd; g2.ldae = KEd; g2.Be = t.bextd; g2.ldbe = KEd;
   g2.M = (int)m; g2.N = (int)d; g2.K = (int)h; g2.KE = KEd;
@@ -573,18 +680,18 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint
   return QLORA_OK;
 }
 
-int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
-                  const uint16_t* u_save, const float* Ug, const float* Uu, const float* Ud,
-                  int64_t m, const qlora_mlp_weights* w, uint16_t* dX,
-                  const qlora_mlp_grads* gr, int mode, void* ws, size_t ws_bytes, void* stream) {
-  if (int e = check_mlp(w, mode)) return e;
-  if (!dY || !X || !g_save || !u_save || !Ug || !Uu || !Ud || !gr) return QLORA_EINVAL;
+static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
+                        const uint16_t* u_save, const float* Ug, const float* Uu, const float* Ud,
+                        int64_t m, const MlpSrc* w, uint16_t* dX,
+                        const qlora_mlp_grads* gr, int mode, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_mlp(*w, mode)) return e;
+  if (!gr) return QLORA_EINVAL;
+  if (m > 0 && (!dY || !X || !g_save || !u_save || !Ug || !Uu || !Ud)) return QLORA_EINVAL;
   if (!gr->a_gate || !gr->b_gate || !gr->a_up || !gr->b_up || !gr->a_down || !gr->b_down)
     return QLORA_EINVAL;
   const int64_t d = w->d, h = w->h, r = w->r;
   if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
-  mode = resolve_mode(mode);
-  const size_t need = qlora_mlp_workspace_bytes(m, d, h, r, mode);
+  const size_t need = mlp_ws(m, d, h, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (m == 0) {
@@ -628,12 +735,16 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   // weights run on the helper stream, overlapping the row products and the two
   // GEMMs on the caller's stream; each waits for exactly the tensors it reads.
   // All column reductions share t.part, so they stay in order on one stream.
-  const bool staged = mode == QLORA_DEQUANT_STAGED;
+  const bool staged = staged_like(mode);
+  const bool w16 = mode == MODE_BF16;
   Side side(st);
   QL_TRY(side.open(), "mlp_bwd: helper stream");
   hipStream_t ss = side.stream();
   QL_TRY(side.fork(0), "mlp_bwd: fork");
-  if (staged) {
+  if (w16) {
+    QL_TRY(launch_w16_transpose(w->gate.w16, h, d, t.wgut, 2 * h, 0, ss), "mlp_bwd: Wg^T");
+    QL_TRY(launch_w16_transpose(w->up.w16, h, d, t.wgut, 2 * h, h, ss), "mlp_bwd: Wu^T");
+  } else if (staged) {
     QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, ss),
            "mlp_bwd: dequant Wg^T");
     QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, ss),
@@ -647,7 +758,9 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
          "mlp_bwd: dBd");
 
   // down projection: Td = dY Bd
-  if (staged)
+  if (w16)
+    QL_TRY(launch_w16_transpose(w->down.w16, d, h, t.wdt, d, 0, st), "mlp_bwd: Wd^T");
+  else if (staged)
     QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
            "mlp_bwd: dequant Wd^T");
   QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
@@ -713,6 +826,43 @@ int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
   }
   QL_TRY(side.join(5), "mlp_bwd: join");
   return QLORA_OK;
+}
+
+int qlora_mlp_fwd(const uint16_t* X, int64_t m, const qlora_mlp_weights* w, uint16_t* Y,
+                  uint16_t* g_save, uint16_t* u_save, float* Ug, float* Uu, float* Ud, int mode,
+                  void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !valid_mode(mode)) return QLORA_EINVAL;
+  const MlpSrc src = mlp_src(w);
+  return mlp_fwd_impl(X, m, &src, Y, g_save, u_save, Ug, Uu, Ud, resolve_mode(mode), ws, ws_bytes,
+                      stream);
+}
+
+int qlora_mlp_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
+                  const uint16_t* u_save, const float* Ug, const float* Uu, const float* Ud,
+                  int64_t m, const qlora_mlp_weights* w, uint16_t* dX,
+                  const qlora_mlp_grads* gr, int mode, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !valid_mode(mode)) return QLORA_EINVAL;
+  const MlpSrc src = mlp_src(w);
+  return mlp_bwd_impl(dY, X, g_save, u_save, Ug, Uu, Ud, m, &src, dX, gr, resolve_mode(mode), ws,
+                      ws_bytes, stream);
+}
+
+int qlora_mlp16_fwd(const uint16_t* X, int64_t m, const qlora_mlp16_weights* w, uint16_t* Y,
+                    uint16_t* g_save, uint16_t* u_save, float* Ug, float* Uu, float* Ud,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  const MlpSrc src = mlp_src16(w);
+  return mlp_fwd_impl(X, m, &src, Y, g_save, u_save, Ug, Uu, Ud, MODE_BF16, ws, ws_bytes, stream);
+}
+
+int qlora_mlp16_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_save,
+                    const uint16_t* u_save, const float* Ug, const float* Uu, const float* Ud,
+                    int64_t m, const qlora_mlp16_weights* w, uint16_t* dX,
+                    const qlora_mlp_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  const MlpSrc src = mlp_src16(w);
+  return mlp_bwd_impl(dY, X, g_save, u_save, Ug, Uu, Ud, m, &src, dX, gr, MODE_BF16, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"

@@ -135,3 +135,30 @@ def test_probe_validation_errors(L):
     assert L.qlora_probe_mfma_peak(100, None, ctypes.byref(d), None) == -1
     assert L.qlora_probe_mfma_peak(100, ctypes.byref(d), None, None) == -1
     assert L.qlora_probe_mfma_peak(0, ctypes.byref(d), ctypes.byref(d), None) == -1
+
+
+def test_w16_validation_errors(L):
+    FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    ws = L.qlora_linear16_workspace_bytes(64, 128, 192, 8)
+    assert ws > 0
+    assert L.qlora_linear16_workspace_bytes(64, 100, 192, 8) == 0        # k not a multiple of 64
+    assert L.qlora_linear16_workspace_bytes(64, 128, 192, 65) == 0       # r > 64
+    # null weight
+    assert L.qlora_linear16_fwd(FAKE, 64, None, 192, 128, FAKE, FAKE, 8, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, ws, None) == -1
+    # bad shape
+    assert L.qlora_linear16_fwd(FAKE, 64, FAKE, 192, 100, FAKE, FAKE, 8, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, ws, None) == -2
+    # workspace too small
+    assert L.qlora_linear16_fwd(FAKE, 64, FAKE, 192, 128, FAKE, FAKE, 8, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, 256, None) == -3
+    assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 8) > 0
+    assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 33) == 0          # MLP rank limit
+    w = _lib.Mlp16Weights(None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                          128, 192, 8, 1.0, 0)
+    assert L.qlora_mlp16_fwd(FAKE, 64, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 30, None) == -1
+    w.gate = 0x1000
+    w.act = 7
+    assert L.qlora_mlp16_fwd(FAKE, 64, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 30, None) == -1

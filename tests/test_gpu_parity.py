@@ -253,3 +253,25 @@ def test_mlp_b_zero_gives_zero_a_grads():
     _check(got, _oracle_mlp(cfg, d), keys=["Y", "dX", "dBg", "dBu", "dBd"])
     for k in ("dAg", "dAu", "dAd"):
         assert torch.count_nonzero(got[k]).item() == 0, k
+
+
+def test_empty_batch_writes_zero_lora_grads():
+    # m == 0: no token contributes, so every LoRA gradient is zero; the
+    # per-token tensors are empty (null device pointers)
+    cfg, d = _linear_case(4, 128, 192, 8, 2.0)
+    w = Q.NF4Weight(d["codes"].to(DEV), d["absmax"].to(DEV))
+    A, B = d["A"].to(DEV), d["B"].to(DEV)
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=DEV)  # noqa: E731
+    dA = torch.full((8, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    dB = torch.full((192, 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    U0 = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    _, dA2, dB2 = Q.linear_bwd(e(0, 192), e(0, 128), U0, w, A, B, 2.0)
+    mc = I.MlpCfg("empty", 4, 64, 128, 4, 1.0, "swiglu", 1.0)
+    md = _mlp_case(mc, dense=True)
+    mw = _weights(mc, md)
+    sv = dict(g=e(0, 128), u=e(0, 128), **{k: torch.empty((0, 4), dtype=torch.float32, device=DEV)
+                                           for k in ("Ug", "Uu", "Ud")})
+    gr = Q.mlp_bwd(e(0, 64), e(0, 64), sv, mw)
+    torch.cuda.synchronize()
+    for t in (dA2, dB2, *(gr[k] for k in ("dAg", "dBg", "dAu", "dBu", "dAd", "dBd"))):
+        assert torch.count_nonzero(t).item() == 0
