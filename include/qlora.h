@@ -128,6 +128,20 @@ void qlora_nf4_levels(float out_host[16]);
  * contract: bf16_rne(fp32_rne(level[code] * absmax)). */
 int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);
 
+/* Quantizer: bf16 W [n][k] (k a multiple of 64, finite values) -> NF4 codes
+ * [n][k/2] and absmax [n][k/64], the inverse direction of the dequant above
+ * (needed to turn 16-bit weights into the 4-bit base of the method). Per
+ * 64-block: absmax = max |w| (exact); each weight takes the nearest level to
+ * x = w / absmax, x and the distances formed in fp64, ties to the lower
+ * code; an all-zero block gets absmax 0 and code 7 (the level 0) throughout.
+ * The absmax values stay fp32 (no second-level quantization). Layout and
+ * ownership as for qlora_nf4_dequant (device pointers owned by the caller).
+ * Errors: QLORA_ESHAPE if k % 64 != 0 or a size is negative or >= 2^31;
+ * n*k == 0 returns QLORA_OK and touches nothing (pointers may be NULL);
+ * otherwise QLORA_EINVAL for a NULL pointer. Asynchronous on `stream`. */
+int qlora_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
+                       void* stream);
+
 /* ---------------------------------------------------------- linear layer --
  * Forward:  U = X A^T (saved, fp32 [m][r]);  Y = X W^T + s U B^T.
  * Backward: T = dY B;  dX = dY W + s T A;  dA = s T^T X;  dB = s dY^T U.

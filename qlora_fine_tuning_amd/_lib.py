@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.qlora_nf4_dequant.restype = ctypes.c_int
         L.qlora_nf4_dequant.argtypes = [Nf4, c_vp, c_vp]
+        L.qlora_nf4_quantize.restype = ctypes.c_int
+        L.qlora_nf4_quantize.argtypes = [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]
         L.qlora_linear_workspace_bytes.restype = ctypes.c_size_t
         L.qlora_linear_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
         L.qlora_linear_fwd.restype = ctypes.c_int
@@ -127,7 +129,7 @@ def check(status: int, what: str) -> None:
 
 EXPORTED = [
     "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
-    "qlora_nf4_dequant", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_nf4_dequant", "qlora_nf4_quantize", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",
     "qlora_linear16_workspace_bytes", "qlora_linear16_fwd", "qlora_linear16_bwd",

@@ -114,6 +114,19 @@ def nf4_dequant(w: NF4Weight) -> torch.Tensor:
     return out
 
 
+def nf4_quantize(W: torch.Tensor) -> NF4Weight:
+    """bf16 W [n][k] (k % 64 == 0) -> NF4Weight (codes, absmax) on W's device."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    n, k = W.shape
+    _need(W, "W", torch.bfloat16, (n, k))
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
+    absmax = torch.empty((n, k // 64), dtype=torch.float32, device=W.device)
+    _lib.check(_lib.lib().qlora_nf4_quantize(_ptr(W), n, k, _ptr(codes), _ptr(absmax), _stream()),
+               "qlora_nf4_quantize")
+    return NF4Weight(codes, absmax)
+
+
 # ------------------------------------------------------------- linear layer --
 def linear_workspace_bytes(m, k, n, r, mode="auto") -> int:
     return int(_lib.lib().qlora_linear_workspace_bytes(m, k, n, r, _lib.MODE[mode]))

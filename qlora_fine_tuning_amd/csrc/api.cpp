@@ -334,6 +334,16 @@ const char* qlora_last_error(void) { return g_last_error.c_str(); }
 
 const char* qlora_version(void) { return "qlora-mi355x 0.1 gfx950"; }
 
+int qlora_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
+                       void* stream) {
+  if (n < 0 || k < 0 || k % 64 || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
+    return QLORA_ESHAPE;
+  if (n * k == 0) return QLORA_OK;
+  if (!w || !codes || !absmax) return QLORA_EINVAL;
+  QL_TRY(launch_nf4_quantize(w, n, k, codes, absmax, (hipStream_t)stream), "nf4_quantize");
+  return QLORA_OK;
+}
+
 int qlora_probe_mfma_peak(int iters, double* tflops, double* shader_ghz, void* stream) {
   if (!tflops || !shader_ghz || iters < 1) return QLORA_EINVAL;
   QL_TRY(probe_mfma_peak(iters, (hipStream_t)stream, tflops, shader_ghz), "probe_mfma_peak");

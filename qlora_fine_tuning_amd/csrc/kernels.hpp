@@ -19,6 +19,10 @@ hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, const float* absma
                                         int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
                                         hipStream_t stream);
 
+// NF4 quantizer: codes [n][k/2] and absmax [n][k/64] from bf16 W [n][k]
+hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                               float* absmax, hipStream_t stream);
+
 // ---- bf16 base-weight staging (w16.hip); n, k multiples of 64 ----
 // out[dest_row(i)][j] = W[i][j] (dest_row as for the NF4 dequant)
 hipError_t launch_w16_rows(const uint16_t* src, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,

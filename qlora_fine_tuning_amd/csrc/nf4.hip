@@ -112,6 +112,73 @@ __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
   }
 }
 
+// Quantizer (bf16 weights -> NF4), one thread per 64-weight block. For
+// every block: absmax = max |w| (exact: a bf16 value, stored as fp32); each
+// weight gets the level nearest to x = w / absmax, with x and the distances
+// |x - level| formed in fp64 and ties going to the lower code; an all-zero
+// block gets absmax 0 and code 7 (the exact zero) everywhere. Weights must be
+// finite. Packing as for the dequant: element 2j in the high nibble of byte j.
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t* __restrict__ w,
+                                                           int64_t nblocks,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax) {
+  double lv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lv[i] = (double)__uint_as_float(c_nf4_levels[i]);
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = *(const u32x4_t*)(w + b * 64 + q * 8);
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        amax = fmaxf(amax, fabsf(bf16_to_f32(v[q][e] & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(bf16_to_f32(v[q][e] >> 16)));
+      }
+    const double a = (double)amax;
+    u32x4_t out[2];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {   // t = 0: element 2j (high nibble), t = 1: 2j + 1
+          const float wf = bf16_to_f32(t ? (v[q][e] >> 16) : (v[q][e] & 0xFFFFu));
+          const double x = amax == 0.0f ? 0.0 : (double)wf / a;
+          int best = 0;
+          double bd = fabs(x - lv[0]);
+#pragma unroll
+          for (int i = 1; i < 16; ++i) {
+            const double di = fabs(x - lv[i]);
+            if (di < bd) { bd = di; best = i; }
+          }
+          byte |= (uint32_t)best << (t ? 0 : 4);
+        }
+        word |= byte << (8 * e);
+      }
+      out[q >> 2][q & 3] = word;
+    }
+    *(u32x4_t*)(codes + b * 32) = out[0];
+    *(u32x4_t*)(codes + b * 32 + 16) = out[1];
+    absmax[b] = amax;
+  }
+}
+
+hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                               float* absmax, hipStream_t stream) {
+  const int64_t nblocks = n * (k / 64);
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  if (grid > 256 * 64) grid = 256 * 64;
+  nf4_quantize_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(w, nblocks, codes, absmax);
+  return hipGetLastError();
+}
+
 hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, int64_t n, int64_t k,
                                    uint16_t* out, int64_t ld_out, int interleave,
                                    hipStream_t stream) {

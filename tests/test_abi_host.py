@@ -162,3 +162,12 @@ def test_w16_validation_errors(L):
     w.act = 7
     assert L.qlora_mlp16_fwd(FAKE, 64, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              FAKE, 1 << 30, None) == -1
+
+
+def test_quantize_validation_errors(L):
+    FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    assert L.qlora_nf4_quantize(None, 4, 64, FAKE, FAKE, None) == -1      # null weights
+    assert L.qlora_nf4_quantize(FAKE, 4, 64, FAKE, None, None) == -1      # null absmax
+    assert L.qlora_nf4_quantize(FAKE, 4, 96, FAKE, FAKE, None) == -2      # k % 64 != 0
+    assert L.qlora_nf4_quantize(FAKE, -1, 64, FAKE, FAKE, None) == -2     # negative rows
+    assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == 0       # empty: no work

@@ -1,0 +1,85 @@
+"""GPU NF4 quantizer (qlora_nf4_quantize) against the oracle quantizer: codes
+and absmax must match bit for bit (an integer decision per weight, taken in
+fp64 on both sides).
+
+Cases: normal weights of the workload's distribution at several shapes, and
+crafted blocks that stress the decision: all-zero blocks, a single nonzero,
+signed zeros, bf16 values just below and just above every midpoint between
+neighbouring levels, and extreme and subnormal magnitudes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import qlora_fine_tuning_amd as Q
+from oracle import nf4 as onf4
+from qlora_fine_tuning_amd import inputs as I
+
+from _util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(W: torch.Tensor):
+    say(f"quantize {tuple(W.shape)}")
+    got = Q.nf4_quantize(W.to(DEV))
+    torch.cuda.synchronize()
+    codes, absmax = onf4.quantize(_bits(W))
+    assert np.array_equal(got.codes.cpu().numpy(), codes)
+    assert np.array_equal(got.absmax.cpu().numpy().view(np.uint32), absmax.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(64, 64), (512, 256), (1024, 4096), (96, 1088)])
+def test_quantize_matches_oracle(n, k):
+    _check(I.normal_bf16("W", (n, k), 0.02, seed=n + k))
+
+
+def _bf16_neighbours(x: float):
+    """The bf16 values just below and just above x (x not representable)."""
+    f = np.array([x], dtype=np.float32).view(np.uint32)[0]
+    b = f >> 16
+    lo = np.array([b << 16], dtype=np.uint32).view(np.float32)[0]
+    hi = np.array([(b + 1) << 16], dtype=np.uint32).view(np.float32)[0]
+    if x < 0:
+        lo, hi = hi, lo
+    return [float(v) for v in (lo, hi)]
+
+
+def test_quantize_decision_boundaries_and_special_blocks():
+    L = onf4.nf4_levels().astype(np.float64)
+    rows = []
+    for amax in (1.0, 0.0234375, 3.0e38, 1.0e-38):
+        vals = []
+        for i in range(15):
+            mid = 0.5 * (L[i] + L[i + 1]) * amax
+            vals += _bf16_neighbours(mid) if mid != 0.0 else [0.0, -0.0]
+        vals = [amax] + vals + [-0.0, 0.0]
+        vals = (vals + [0.25 * amax] * 64)[:64]
+        rows.append(vals)
+    rows.append([0.0] * 64)                       # all-zero block
+    rows.append([-0.0] * 63 + [0.0])              # signed zeros only
+    rows.append([0.0] * 37 + [-1.5] + [0.0] * 26)  # a single nonzero
+    rows.append([1e-40] * 32 + [-3e-40] * 32)     # subnormals
+    W = torch.tensor(np.array(rows, dtype=np.float32)).to(torch.bfloat16)
+    _check(W)
+
+
+def test_quantize_then_dequant_round_trip():
+    # quantize(dequant(c, a)) == (c, a) when a is the absmax of the dequantized block
+    W = I.normal_bf16("W", (256, 512), 0.02, seed=3)
+    q = Q.nf4_quantize(W.to(DEV))
+    Wq = Q.nf4_dequant(q)
+    q2 = Q.nf4_quantize(Wq)
+    torch.cuda.synchronize()
+    assert torch.equal(q.codes, q2.codes)
+    assert torch.equal(q.absmax, q2.absmax)
