@@ -133,6 +133,42 @@ def mlp_rows(rows, X, dY, Wg, Wu, Wd, Ag, Bg, Au, Bu, Ad, Bd, s, act="swiglu"):
     return dict(Y=Y, dX=gr["dX"], **sv)
 
 
+# ---------------------------------------- q, k, v on one shared input --
+def qkv_fwd(X, Ws, As, Bs, s):
+    """The q, k, v projections of one input (Mistral benchmark page, breakdown
+    row "Manual Autograd QKV"; Show HN thread, the author's list of savings).
+
+    Ws, As, Bs: the three base weights W_p [N_p][d] and LoRA factors A_p
+    [r][d], B_p [N_p][r]. Each output is the linear layer's Y_p; returns
+    (list of Y_p, list of U_p = X A_p^T).
+    """
+    outs = [linear_fwd(X, W, A, B, s) for W, A, B in zip(Ws, As, Bs)]
+    return [o[0] for o in outs], [o[1] for o in outs]
+
+
+def qkv_bwd(dYs, X, Us, Ws, As, Bs, s):
+    """Manual backward of the three projections: X feeds all three, so its
+    gradient is the sum dX = sum_p (dY_p W_p + s T_p A_p) with T_p = dY_p B_p;
+    each projection has its own dA_p = s T_p^T X and dB_p = s dY_p^T U_p.
+
+    Returns (dX, list of dA_p, list of dB_p).
+    """
+    dX = np.zeros_like(X)
+    dA, dB = [], []
+    for dY, U, W, A, B in zip(dYs, Us, Ws, As, Bs):
+        dXp, dAp, dBp, _ = linear_bwd(dY, X, U, W, A, B, s)
+        dX = dX + dXp
+        dA.append(dAp)
+        dB.append(dBp)
+    return dX, dA, dB
+
+
+def qkv_algorithmic_flops(m, d, ns, r):
+    """FLOPs for the q, k, v forward + backward: each projection counts as one
+    linear layer (the shared input adds no work)."""
+    return sum(linear_algorithmic_flops(m, d, n, r) for n in ns)
+
+
 # ------------------------------------------------- chained-matmul FLOPs --
 def chain_macs(shapes, order):
     """Multiply-accumulates of a matrix chain evaluated in a given bracketing.
