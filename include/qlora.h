@@ -239,6 +239,89 @@ int qlora_mlp16_bwd(const uint16_t* dY, const uint16_t* X,
                     uint16_t* dX, const qlora_mlp_grads* grads,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* -------------------------------------------- q, k, v on one shared input --
+ * The attention projections of a layer as one call: for p in {q, k, v},
+ *   Y_p = X W_p^T + s (X A_p^T) B_p^T,   W_p [n_p][d], A_p [r][d], B_p [n_p][r],
+ * X [m][d] shared (with grouped-query attention n_k, n_v < n_q). Forward: one
+ * GEMM over the concatenated width n_q + n_k + n_v and one read of X for the
+ * three rank-r products; saved for the backward: U fp32 [m][3r] =
+ * [X A_q^T | X A_k^T | X A_v^T] (caller-owned).
+ * Backward: T_p = dY_p B_p; dX = sum_p (dY_p W_p + s T_p A_p), formed as ONE
+ * GEMM whose contraction runs over the three dY_p in place; dA_p = s T_p^T X;
+ * dB_p = s dY_p^T U_p. dX may be NULL (not wanted).
+ * (Mistral benchmark page, breakdown row "Manual Autograd QKV"; Show HN
+ * thread, the author's list of savings, manual QKV autograd.)
+ *   - Q, K, V (forward outputs) and dQ, dK, dV (backward inputs) each take a
+ *     row pitch in elements: pitch >= n_p, a multiple of 8, pointer 16-byte
+ *     aligned. They may be separate tensors or column slices of one
+ *     [m][n_q + n_k + n_v] buffer; outputs must not overlap.
+ *   - d, n_q, n_k, n_v: positive multiples of 64; 1 <= r <= 64.
+ *   - The base weights are always dequantized (or copied, 16-bit variant)
+ *     into the workspace as one bf16 [n_q + n_k + n_v][d] matrix (forward) or
+ *     its transpose (backward); one workspace query serves both formats.
+ *   - Errors: QLORA_EINVAL (null pointer, r, s), QLORA_ESHAPE (dimensions,
+ *     mismatched d, pitch or alignment of a per-token tensor),
+ *     QLORA_EWORKSPACE, QLORA_EHIP. m == 0 writes only the six LoRA
+ *     gradients, as zeros; per-token pointers may then be NULL. */
+typedef struct qlora_qkv_weights {
+  qlora_nf4 q, k, v;      /* [n_q][d], [n_k][d], [n_v][d] */
+  const uint16_t* a_q;    /* [r][d] */
+  const uint16_t* b_q;    /* [n_q][r] */
+  const uint16_t* a_k;    /* [r][d] */
+  const uint16_t* b_k;    /* [n_k][r] */
+  const uint16_t* a_v;    /* [r][d] */
+  const uint16_t* b_v;    /* [n_v][r] */
+  int64_t r;
+  float s;
+} qlora_qkv_weights;
+
+/* The same with bf16 base weights (16-bit LoRA). */
+typedef struct qlora_qkv16_weights {
+  const uint16_t* q;      /* [n_q][d] */
+  const uint16_t* k;      /* [n_k][d] */
+  const uint16_t* v;      /* [n_v][d] */
+  int64_t d, n_q, n_k, n_v;
+  const uint16_t* a_q;
+  const uint16_t* b_q;
+  const uint16_t* a_k;
+  const uint16_t* b_k;
+  const uint16_t* a_v;
+  const uint16_t* b_v;
+  int64_t r;
+  float s;
+} qlora_qkv16_weights;
+
+/* LoRA weight gradients (device pointers, bf16, shapes of the factors). */
+typedef struct qlora_qkv_grads {
+  uint16_t* a_q;
+  uint16_t* b_q;
+  uint16_t* a_k;
+  uint16_t* b_k;
+  uint16_t* a_v;
+  uint16_t* b_v;
+} qlora_qkv_grads;
+
+size_t qlora_qkv_workspace_bytes(int64_t m, int64_t d, int64_t n_q, int64_t n_k, int64_t n_v,
+                                 int64_t r);
+
+int qlora_qkv_fwd(const uint16_t* X, int64_t m, const qlora_qkv_weights* w,
+                  uint16_t* Q, int64_t ld_q, uint16_t* K, int64_t ld_k, uint16_t* V, int64_t ld_v,
+                  float* U_save, void* ws, size_t ws_bytes, void* stream);
+
+int qlora_qkv_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64_t ld_dk,
+                  const uint16_t* dV, int64_t ld_dv, const uint16_t* X, const float* U,
+                  int64_t m, const qlora_qkv_weights* w, uint16_t* dX,
+                  const qlora_qkv_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+int qlora_qkv16_fwd(const uint16_t* X, int64_t m, const qlora_qkv16_weights* w,
+                    uint16_t* Q, int64_t ld_q, uint16_t* K, int64_t ld_k, uint16_t* V,
+                    int64_t ld_v, float* U_save, void* ws, size_t ws_bytes, void* stream);
+
+int qlora_qkv16_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64_t ld_dk,
+                    const uint16_t* dV, int64_t ld_dv, const uint16_t* X, const float* U,
+                    int64_t m, const qlora_qkv16_weights* w, uint16_t* dX,
+                    const qlora_qkv_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- tracing --
  * Kernel timing aid for benchmarks and profiling. While enabled, every
  * dense-contraction (base GEMM) launch made by the entry points above is

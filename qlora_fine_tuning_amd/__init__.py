@@ -12,6 +12,8 @@ __all__ = [
     "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read", "probe_mfma_peak",
     "linear16_workspace_bytes", "linear16_fwd", "linear16_bwd",
     "Mlp16Weights", "mlp16_workspace_bytes", "mlp16_fwd", "mlp16_bwd",
+    "QkvWeights", "Qkv16Weights", "qkv_workspace_bytes", "qkv_fwd", "qkv_bwd", "qkv16_fwd",
+    "qkv16_bwd",
 ]
 
 

@@ -42,6 +42,24 @@ class Mlp16Weights(ctypes.Structure):
                 ("d", c_i64), ("h", c_i64), ("r", c_i64), ("s", ctypes.c_float), ("act", ctypes.c_int)]
 
 
+class QkvWeights(ctypes.Structure):
+    _fields_ = [("q", Nf4), ("k", Nf4), ("v", Nf4),
+                ("a_q", c_vp), ("b_q", c_vp), ("a_k", c_vp), ("b_k", c_vp), ("a_v", c_vp),
+                ("b_v", c_vp), ("r", c_i64), ("s", ctypes.c_float)]
+
+
+class Qkv16Weights(ctypes.Structure):
+    _fields_ = [("q", c_vp), ("k", c_vp), ("v", c_vp),
+                ("d", c_i64), ("n_q", c_i64), ("n_k", c_i64), ("n_v", c_i64),
+                ("a_q", c_vp), ("b_q", c_vp), ("a_k", c_vp), ("b_k", c_vp), ("a_v", c_vp),
+                ("b_v", c_vp), ("r", c_i64), ("s", ctypes.c_float)]
+
+
+class QkvGrads(ctypes.Structure):
+    _fields_ = [("a_q", c_vp), ("b_q", c_vp), ("a_k", c_vp), ("b_k", c_vp), ("a_v", c_vp),
+                ("b_v", c_vp)]
+
+
 class MlpGrads(ctypes.Structure):
     _fields_ = [("a_gate", c_vp), ("b_gate", c_vp), ("a_up", c_vp), ("b_up", c_vp),
                 ("a_down", c_vp), ("b_down", c_vp)]
@@ -107,6 +125,19 @@ def lib() -> ctypes.CDLL:
         L.qlora_mlp16_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                       ctypes.POINTER(Mlp16Weights), c_vp, ctypes.POINTER(MlpGrads),
                                       c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_qkv_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_qkv_workspace_bytes.argtypes = [c_i64] * 6
+        for name, wt in (("qlora_qkv_fwd", QkvWeights), ("qlora_qkv16_fwd", Qkv16Weights)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [c_vp, c_i64, ctypes.POINTER(wt), c_vp, c_i64, c_vp, c_i64, c_vp, c_i64,
+                          c_vp, c_vp, ctypes.c_size_t, c_vp]
+        for name, wt in (("qlora_qkv_bwd", QkvWeights), ("qlora_qkv16_bwd", Qkv16Weights)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64,
+                          ctypes.POINTER(wt), c_vp, ctypes.POINTER(QkvGrads), c_vp,
+                          ctypes.c_size_t, c_vp]
         L.qlora_probe_mfma_peak.restype = ctypes.c_int
         L.qlora_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
@@ -134,4 +165,6 @@ EXPORTED = [
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",
     "qlora_linear16_workspace_bytes", "qlora_linear16_fwd", "qlora_linear16_bwd",
     "qlora_mlp16_workspace_bytes", "qlora_mlp16_fwd", "qlora_mlp16_bwd",
+    "qlora_qkv_workspace_bytes", "qlora_qkv_fwd", "qlora_qkv_bwd", "qlora_qkv16_fwd",
+    "qlora_qkv16_bwd",
 ]

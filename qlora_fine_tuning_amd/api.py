@@ -391,3 +391,143 @@ def mlp16_bwd(dY, X, saved, w: Mlp16Weights, need_dx=True, ws=None):
                                     _ptr(ws), ws.numel(), _stream())
     _lib.check(st, "qlora_mlp16_bwd")
     return out
+
+
+# ---------------------------------------------- q, k, v on one shared input --
+def _need_rows(t: torch.Tensor, name: str, shape):
+    """A bf16 [rows][cols] tensor whose rows may be strided (a column slice of
+    a wider buffer); returns its row pitch in elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if shape[0] > 1 else max(t.stride(0), shape[1])
+
+
+@dataclasses.dataclass
+class QkvWeights:
+    """q, k, v projections of one input: NF4 base weights W_p [n_p][d],
+    LoRA A_p [r][d], B_p [n_p][r]."""
+    q: NF4Weight
+    k: NF4Weight
+    v: NF4Weight
+    a_q: torch.Tensor
+    b_q: torch.Tensor
+    a_k: torch.Tensor
+    b_k: torch.Tensor
+    a_v: torch.Tensor
+    b_v: torch.Tensor
+    s: float
+
+    @property
+    def d(self):
+        return self.q.k
+
+    @property
+    def ns(self):
+        return (self.q.n, self.k.n, self.v.n)
+
+    @property
+    def r(self):
+        return self.a_q.shape[0]
+
+    def _lora_check(self):
+        d, r = self.d, self.r
+        for name, t, shape in (("a_q", self.a_q, (r, d)), ("a_k", self.a_k, (r, d)),
+                               ("a_v", self.a_v, (r, d)), ("b_q", self.b_q, (self.ns[0], r)),
+                               ("b_k", self.b_k, (self.ns[1], r)), ("b_v", self.b_v, (self.ns[2], r))):
+            _need(t, name, torch.bfloat16, shape)
+        return [t.data_ptr() for t in (self.a_q, self.b_q, self.a_k, self.b_k, self.a_v, self.b_v)]
+
+    def c_struct(self):
+        return _lib.QkvWeights(self.q.c_struct(), self.k.c_struct(), self.v.c_struct(),
+                               *self._lora_check(), self.r, float(self.s))
+
+
+@dataclasses.dataclass
+class Qkv16Weights(QkvWeights):
+    """The same with bf16 base weights q, k, v [n_p][d] (16-bit LoRA)."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+
+    @property
+    def d(self):
+        return self.q.shape[1]
+
+    @property
+    def ns(self):
+        return (self.q.shape[0], self.k.shape[0], self.v.shape[0])
+
+    def c_struct(self):
+        d = self.d
+        for name, t, n in (("q", self.q, self.ns[0]), ("k", self.k, self.ns[1]),
+                           ("v", self.v, self.ns[2])):
+            _need(t, name, torch.bfloat16, (n, d))
+        return _lib.Qkv16Weights(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), d,
+                                 *self.ns, *self._lora_check(), self.r, float(self.s))
+
+
+def qkv_workspace_bytes(m, d, n_q, n_k, n_v, r) -> int:
+    return int(_lib.lib().qlora_qkv_workspace_bytes(m, d, n_q, n_k, n_v, r))
+
+
+def _qkv_fwd(fn, X, w, out, ws):
+    m, d, r, ns = X.shape[0], w.d, w.r, w.ns
+    _need(X, "X", torch.bfloat16, (m, d))
+    dev = X.device
+    if out is None:
+        out = tuple(torch.empty((m, n), dtype=torch.bfloat16, device=dev) for n in ns)
+    lds = [_need_rows(t, nm, (m, n)) for t, nm, n in zip(out, ("Q", "K", "V"), ns)]
+    U = torch.empty((m, 3 * r), dtype=torch.float32, device=dev)
+    nb = qkv_workspace_bytes(m, d, *ns, r)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = getattr(_lib.lib(), fn)(_ptr(X), m, ctypes.byref(cw), _ptr(out[0]), lds[0], _ptr(out[1]),
+                                 lds[1], _ptr(out[2]), lds[2], _ptr(U), _ptr(ws), ws.numel(),
+                                 _stream())
+    _lib.check(st, fn)
+    return out[0], out[1], out[2], U
+
+
+def _qkv_bwd(fn, dQ, dK, dV, X, U, w, need_dx, ws):
+    m, d, r, ns = X.shape[0], w.d, w.r, w.ns
+    _need(X, "X", torch.bfloat16, (m, d))
+    _need(U, "U", torch.float32, (m, 3 * r))
+    lds = [_need_rows(t, nm, (m, n)) for t, nm, n in zip((dQ, dK, dV), ("dQ", "dK", "dV"), ns)]
+    dev = X.device
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    out = dict(dX=e(m, d) if need_dx else None, dAq=e(r, d), dBq=e(ns[0], r), dAk=e(r, d),
+               dBk=e(ns[1], r), dAv=e(r, d), dBv=e(ns[2], r))
+    grads = _lib.QkvGrads(*[out[k].data_ptr() for k in ("dAq", "dBq", "dAk", "dBk", "dAv", "dBv")])
+    nb = qkv_workspace_bytes(m, d, *ns, r)
+    ws = workspace(nb, dev) if ws is None else ws
+    cw = w.c_struct()
+    st = getattr(_lib.lib(), fn)(_ptr(dQ), lds[0], _ptr(dK), lds[1], _ptr(dV), lds[2], _ptr(X),
+                                 _ptr(U), m, ctypes.byref(cw), _ptr(out["dX"]),
+                                 ctypes.byref(grads), _ptr(ws), ws.numel(), _stream())
+    _lib.check(st, fn)
+    return out
+
+
+def qkv_fwd(X, w: QkvWeights, out=None, ws=None):
+    """Returns (Q, K, V, U): Q/K/V bf16 [m][n_p] (into `out`, three tensors
+    that may be column slices of one buffer, if given), U fp32 [m][3r]."""
+    return _qkv_fwd("qlora_qkv_fwd", X, w, out, ws)
+
+
+def qkv_bwd(dQ, dK, dV, X, U, w: QkvWeights, need_dx=True, ws=None):
+    """Returns dict(dX, dAq, dBq, dAk, dBk, dAv, dBv), all bf16."""
+    return _qkv_bwd("qlora_qkv_bwd", dQ, dK, dV, X, U, w, need_dx, ws)
+
+
+def qkv16_fwd(X, w: Qkv16Weights, out=None, ws=None):
+    return _qkv_fwd("qlora_qkv16_fwd", X, w, out, ws)
+
+
+def qkv16_bwd(dQ, dK, dV, X, U, w: Qkv16Weights, need_dx=True, ws=None):
+    return _qkv_bwd("qlora_qkv16_bwd", dQ, dK, dV, X, U, w, need_dx, ws)

@@ -875,4 +875,359 @@ int qlora_mlp16_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g_sav
                       stream);
 }
 
+// ------------------------------------------- q, k, v on one shared input --
+// Projection p in {q, k, v} = {0, 1, 2}: Y_p = X W_p^T + s (X A_p^T) B_p^T.
+// Forward: one GEMM over the concatenated output width nt = n_q + n_k + n_v
+// (B = [W_q; W_k; W_v] in the workspace), the three LoRA terms as one
+// K-extension, and an epilogue that writes each column range to its output.
+// Backward: dX = sum_p dY_p W_p + s T_p A_p as one GEMM whose K runs over the
+// three dY_p (read in place, each with its own pitch).
+struct QkvSrc {
+  WSrc w[3];
+  const uint16_t* a[3];
+  const uint16_t* b[3];
+  int64_t r;
+  float s;
+};
+
+static QkvSrc qkv_src(const qlora_qkv_weights* w) {
+  QkvSrc q;
+  q.w[0] = src_nf4(w->q); q.w[1] = src_nf4(w->k); q.w[2] = src_nf4(w->v);
+  q.a[0] = w->a_q; q.a[1] = w->a_k; q.a[2] = w->a_v;
+  q.b[0] = w->b_q; q.b[1] = w->b_k; q.b[2] = w->b_v;
+  q.r = w->r; q.s = w->s;
+  return q;
+}
+
+static QkvSrc qkv_src16(const qlora_qkv16_weights* w) {
+  QkvSrc q;
+  q.w[0] = src_w16(w->q, w->n_q, w->d); q.w[1] = src_w16(w->k, w->n_k, w->d);
+  q.w[2] = src_w16(w->v, w->n_v, w->d);
+  q.a[0] = w->a_q; q.a[1] = w->a_k; q.a[2] = w->a_v;
+  q.b[0] = w->b_q; q.b[1] = w->b_k; q.b[2] = w->b_v;
+  q.r = w->r; q.s = w->s;
+  return q;
+}
+
+static bool qkv_dims_ok(int64_t m, int64_t d, const int64_t n[3]) {
+  const int64_t lim = (int64_t)1 << 30;
+  if (!dims_ok(m, d, n[0]) || !dims_ok(m, d, n[1]) || !dims_ok(m, d, n[2])) return false;
+  return n[0] + n[1] + n[2] < lim;
+}
+
+static int check_qkv(const QkvSrc& w, int mode) {
+  for (int p = 0; p < 3; ++p)
+    if (bad_src(w.w[p], mode) || !w.a[p] || !w.b[p]) return QLORA_EINVAL;
+  if (w.r < 1 || w.r > 64 || !std::isfinite(w.s)) return QLORA_EINVAL;
+  const int64_t n[3] = {w.w[0].n, w.w[1].n, w.w[2].n};
+  const int64_t d = w.w[0].k;
+  if (w.w[1].k != d || w.w[2].k != d || !qkv_dims_ok(0, d, n)) return QLORA_ESHAPE;
+  return QLORA_OK;
+}
+
+// a per-token tensor with a row pitch: pitch >= width, 16-byte rows
+static bool pitch_ok(const void* p, int64_t ld, int64_t width) {
+  return ld >= width && ld % 8 == 0 && ((uintptr_t)p & 15) == 0;
+}
+
+// K-extension layout of the forward: with 3r <= 64 one row product forms
+// [U_q | U_k | U_v] and the columns are [hi(sU) | lo(sU)] over all three;
+// otherwise each projection has its own row product and the columns are
+// [hi(sU_q) lo(sU_q) | hi(sU_k) lo(sU_k) | hi(sU_v) lo(sU_v)]. The backward
+// always uses the second form (its T_p come from three different dY_p).
+struct QkvExt {
+  bool one;
+  int64_t r;
+  int64_t hi(int p) const { return one ? p * r : 2 * r * p; }
+  int64_t lo(int p) const { return one ? 3 * r + p * r : 2 * r * p + r; }
+};
+
+struct QkvFwdWs {
+  uint16_t* lqkv;   // [3r][d]   [A_q; A_k; A_v] (one row product)
+  uint16_t* bext;   // [nt][KE]  B_p at its hi and lo columns
+  uint16_t* uext;   // [m][KE]
+  uint16_t* wcat;   // [nt][d]   [W_q; W_k; W_v] in bf16
+  float* rpart;     // row-product split partials
+};
+
+static size_t plan_qkv_fwd(Carver& c, int64_t m, int64_t d, int64_t nt, int64_t r, QkvFwdWs* w) {
+  const int64_t KE = ceil16(6 * r);
+  QkvFwdWs t;
+  t.lqkv = c.take<uint16_t>(3 * r * d);
+  t.bext = c.take<uint16_t>(nt * KE);
+  t.uext = c.take<uint16_t>(m * KE);
+  t.wcat = c.take<uint16_t>(nt * d);
+  t.rpart = c.take<float>(16 * m * 3 * r);
+  if (w) *w = t;
+  return c.off;
+}
+
+struct QkvBwdWs {
+  uint16_t* lt;     // [r][nt]   [B_q^T | B_k^T | B_v^T]
+  uint16_t* bext;   // [d][KE]   A_p^T at columns 2rp and 2rp + r
+  float* t;         // [m][3r]   [T_q | T_k | T_v]
+  uint16_t* text;   // [m][KE]
+  float* part;      // column-reduction partials
+  uint16_t* wt;     // [d][nt]   [W_q^T | W_k^T | W_v^T] in bf16
+  float* rpart;     // row-product split partials
+};
+
+static size_t plan_qkv_bwd(Carver& c, int64_t m, int64_t d, const int64_t n[3], int64_t r,
+                           QkvBwdWs* w) {
+  const int64_t KE = ceil16(6 * r), nt = n[0] + n[1] + n[2];
+  const int64_t nmax = std::max(n[0], std::max(n[1], n[2]));
+  const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
+  const int64_t ra = 3 * r <= 64 ? 3 * r : r;   // columns of the dA reduction
+  QkvBwdWs t;
+  t.lt = c.take<uint16_t>(r * nt);
+  t.bext = c.take<uint16_t>(d * KE);
+  t.t = c.take<float>(m * 3 * r);
+  t.text = c.take<uint16_t>(m * KE);
+  t.part = c.take<float>(chunks * std::max(nmax * r, d * ra));
+  t.wt = c.take<uint16_t>(d * nt);
+  t.rpart = c.take<float>(16 * m * r);
+  if (w) *w = t;
+  return c.off;
+}
+
+static size_t qkv_ws(int64_t m, int64_t d, const int64_t n[3], int64_t r) {
+  Carver a(nullptr), b(nullptr);
+  return std::max(plan_qkv_fwd(a, m, d, n[0] + n[1] + n[2], r, nullptr),
+                  plan_qkv_bwd(b, m, d, n, r, nullptr));
+}
+
+size_t qlora_qkv_workspace_bytes(int64_t m, int64_t d, int64_t n_q, int64_t n_k, int64_t n_v,
+                                 int64_t r) {
+  const int64_t n[3] = {n_q, n_k, n_v};
+  if (!qkv_dims_ok(m, d, n) || r < 1 || r > 64) return 0;
+  return qkv_ws(m, d, n, r);
+}
+
+static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t* const out[3],
+                        const int64_t ld[3], float* U, int mode, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (int e = check_qkv(w, mode)) return e;
+  const int64_t d = w.w[0].k, r = w.r;
+  const int64_t n[3] = {w.w[0].n, w.w[1].n, w.w[2].n};
+  const int64_t off[3] = {0, n[0], n[0] + n[1]}, nt = n[0] + n[1] + n[2];
+  if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (m > 0) {
+    if (!X || !U || !out[0] || !out[1] || !out[2]) return QLORA_EINVAL;
+    for (int p = 0; p < 3; ++p)
+      if (!pitch_ok(out[p], ld[p], n[p])) return QLORA_ESHAPE;
+  }
+  if (int e = check_ws(ws, ws_bytes, qkv_ws(m, d, n, r))) return e;
+  if (m == 0) return QLORA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  QkvFwdWs t;
+  plan_qkv_fwd(c, m, d, nt, r, &t);
+  const int64_t KE = ceil16(6 * r);
+  const QkvExt ex{3 * r <= 64, r};
+  const float s = w.s;
+
+  // LoRA operand layouts (Bext starts as zeros: each row block holds only its
+  // own projection's B)
+  QL_TRY(launch_zero(t.bext, (size_t)(nt * KE) * 2, st), "qkv_fwd: LoRA layouts");
+  {
+    PrepJobs J;
+    for (int p = 0; p < 3; ++p) {
+      if (ex.one) J.copy(w.a[p], d, 1, r, d, t.lqkv + p * r * d, d, 1);
+      J.copy(w.b[p], r, 1, n[p], r, t.bext + off[p] * KE + ex.hi(p), KE, 1);
+      J.copy(w.b[p], r, 1, n[p], r, t.bext + off[p] * KE + ex.lo(p), KE, 1);
+    }
+    if (!ex.one) J.zero(m, KE - 6 * r, t.uext + 6 * r, KE, 1);
+    QL_TRY(launch_prep(J, st), "qkv_fwd: LoRA layouts");
+  }
+  // the bf16 copy of [W_q; W_k; W_v] is made on the helper stream while the
+  // caller's stream forms the row products
+  const bool w16 = mode == MODE_BF16;
+  Side side(st);
+  QL_TRY(side.open(), "qkv_fwd: helper stream");
+  QL_TRY(side.fork(0), "qkv_fwd: fork");
+  hipStream_t ss = side.stream();
+  for (int p = 0; p < 3; ++p) {
+    uint16_t* dst = t.wcat + off[p] * d;
+    if (w16)
+      QL_TRY(launch_w16_rows(w.w[p].w16, n[p], d, dst, d, 0, ss), "qkv_fwd: weight copy");
+    else
+      QL_TRY(launch_nf4_dequant_rows(w.w[p].codes, w.w[p].absmax, n[p], d, dst, d, 0, ss),
+             "qkv_fwd: dequant");
+  }
+  QL_TRY(side.mark(1), "qkv_fwd: mark");
+  if (ex.one) {   // [U_q | U_k | U_v] = X [A_q; A_k; A_v]^T, one read of X
+    QL_TRY(launch_rowdot(X, d, t.lqkv, d, (int)m, (int)d, (int)(3 * r), s, U, nullptr,
+                         (int)(3 * r), 3 * r, t.uext, KE, (int)KE, t.rpart, st),
+           "qkv_fwd: U");
+  } else {
+    for (int p = 0; p < 3; ++p)
+      QL_TRY(launch_rowdot(X, d, w.a[p], d, (int)m, (int)d, (int)r, s, U + p * r, nullptr, (int)r,
+                           3 * r, t.uext + ex.hi(p), KE, (int)(2 * r), t.rpart, st),
+             "qkv_fwd: U");
+  }
+  GemmArgs g = gemm_args();
+  g.A = X; g.lda = d;
+  g.bsrc = BSRC_BF16; g.B = t.wcat; g.ldb = d;
+  g.Ae = t.uext; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
+  g.M = (int)m; g.N = (int)nt; g.K = (int)d; g.KE = (int)KE;
+  g.epi = EPI_STORE3;
+  g.C = out[0]; g.ldc = ld[0]; g.C1 = out[1]; g.ldc1 = ld[1]; g.C2 = out[2]; g.ldc2 = ld[2];
+  g.nc1 = (int)off[1]; g.nc2 = (int)off[2];
+  QL_TRY(side.wait(1), "qkv_fwd: wait");
+  QL_TRY(run_gemm(g, r, st), "qkv_fwd: GEMM");
+  return QLORA_OK;
+}
+
+static int qkv_bwd_impl(const uint16_t* const dy[3], const int64_t lddy[3], const uint16_t* X,
+                        const float* U, int64_t m, const QkvSrc& w, uint16_t* dX,
+                        const qlora_qkv_grads* gr, int mode, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (int e = check_qkv(w, mode)) return e;
+  if (!gr || !gr->a_q || !gr->b_q || !gr->a_k || !gr->b_k || !gr->a_v || !gr->b_v)
+    return QLORA_EINVAL;
+  uint16_t* const ga[3] = {gr->a_q, gr->a_k, gr->a_v};
+  uint16_t* const gb[3] = {gr->b_q, gr->b_k, gr->b_v};
+  const int64_t d = w.w[0].k, r = w.r;
+  const int64_t n[3] = {w.w[0].n, w.w[1].n, w.w[2].n};
+  const int64_t off[3] = {0, n[0], n[0] + n[1]}, nt = n[0] + n[1] + n[2];
+  if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (m > 0) {
+    if (!X || !U || !dy[0] || !dy[1] || !dy[2]) return QLORA_EINVAL;
+    for (int p = 0; p < 3; ++p)
+      if (!pitch_ok(dy[p], lddy[p], n[p])) return QLORA_ESHAPE;
+  }
+  if (int e = check_ws(ws, ws_bytes, qkv_ws(m, d, n, r))) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (m == 0) {
+    PrepJobs J;
+    for (int p = 0; p < 3; ++p) {
+      J.zero(r, d, ga[p], d, 1);
+      J.zero(n[p], r, gb[p], r, 1);
+    }
+    QL_TRY(launch_prep(J, st), "qkv_bwd: zero grads");
+    return QLORA_OK;
+  }
+  Carver c(ws);
+  QkvBwdWs t;
+  plan_qkv_bwd(c, m, d, n, r, &t);
+  const int64_t KE = ceil16(6 * r);
+  const int chunks = colreduce_chunks((int)m);
+  const bool one_a = 3 * r <= 64;
+  const float s = w.s;
+
+  {  // lt = [B_q^T | B_k^T | B_v^T]; bext rows: A_p^T at columns 2rp and 2rp + r
+    PrepJobs J;
+    for (int p = 0; p < 3; ++p) {
+      J.copy(w.b[p], 1, r, r, n[p], t.lt + off[p], nt, 1);
+      J.copy(w.a[p], 1, d, d, r, t.bext + 2 * r * p, KE, 1);
+      J.copy(w.a[p], 1, d, d, r, t.bext + 2 * r * p + r, KE, 1);
+    }
+    J.zero(d, KE - 6 * r, t.bext + 6 * r, KE, 1);
+    J.zero(m, KE - 6 * r, t.text + 6 * r, KE, 1);
+    QL_TRY(launch_prep(J, st), "qkv_bwd: LoRA layouts");
+  }
+  // helper stream: the transposed bf16 weights, then dB_p (inputs only), then
+  // dA_p once the T_p exist; the caller's stream: T_p, then the dX GEMM
+  const bool w16 = mode == MODE_BF16;
+  Side side(st);
+  QL_TRY(side.open(), "qkv_bwd: helper stream");
+  hipStream_t ss = side.stream();
+  QL_TRY(side.fork(0), "qkv_bwd: fork");
+  if (dX) {
+    for (int p = 0; p < 3; ++p) {
+      if (w16)
+        QL_TRY(launch_w16_transpose(w.w[p].w16, n[p], d, t.wt, nt, off[p], ss), "qkv_bwd: W^T");
+      else
+        QL_TRY(launch_nf4_dequant_transpose(w.w[p].codes, w.w[p].absmax, n[p], d, t.wt, nt, off[p],
+                                            ss),
+               "qkv_bwd: dequant W^T");
+    }
+  }
+  QL_TRY(side.mark(1), "qkv_bwd: mark");
+  for (int p = 0; p < 3; ++p) {   // dB_p = s dY_p^T U_p
+    QL_TRY(launch_colreduce(dy[p], nullptr, nullptr, 0, lddy[p], (int)m, (int)n[p], U + p * r,
+                            3 * r, (int)r, t.part, ss),
+           "qkv_bwd: dB partials");
+    QL_TRY(launch_colreduce_finish(t.part, chunks, (int)n[p], (int)r, 0, (int)r, s, gb[p], r, 1, ss),
+           "qkv_bwd: dB");
+  }
+  for (int p = 0; p < 3; ++p)     // T_p = dY_p B_p, and [hi(sT_p) | lo(sT_p)]
+    QL_TRY(launch_rowdot(dy[p], lddy[p], t.lt + off[p], nt, (int)m, (int)n[p], (int)r, s,
+                         t.t + p * r, nullptr, (int)r, 3 * r, t.text + 2 * r * p, KE, (int)(2 * r),
+                         t.rpart, st),
+           "qkv_bwd: T");
+  QL_TRY(side.fork(2), "qkv_bwd: fork");
+  if (one_a) {   // dA_p = s T_p^T X, one read of X for all three
+    QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.t, 3 * r, (int)(3 * r),
+                            t.part, ss),
+           "qkv_bwd: dA partials");
+    for (int p = 0; p < 3; ++p)
+      QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(3 * r), (int)(p * r), (int)r, s,
+                                     ga[p], 1, d, ss),
+             "qkv_bwd: dA");
+  } else {
+    for (int p = 0; p < 3; ++p) {
+      QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.t + p * r, 3 * r, (int)r,
+                              t.part, ss),
+             "qkv_bwd: dA partials");
+      QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, ga[p], 1, d, ss),
+             "qkv_bwd: dA");
+    }
+  }
+  if (dX) {   // dX = [dY_q | dY_k | dY_v] [W_q; W_k; W_v] + s [T_q | T_k | T_v] [A_q; A_k; A_v]
+    GemmArgs g = gemm_args();
+    g.A = dy[0]; g.lda = lddy[0];
+    g.A1 = dy[1]; g.lda1 = lddy[1];
+    g.A2 = dy[2]; g.lda2 = lddy[2];
+    g.ka1 = (int)off[1]; g.ka2 = (int)off[2];
+    g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = nt;
+    g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
+    g.M = (int)m; g.N = (int)d; g.K = (int)nt; g.KE = (int)KE;
+    g.epi = EPI_STORE; g.C = dX; g.ldc = d;
+    QL_TRY(side.wait(1), "qkv_bwd: wait");
+    QL_TRY(run_gemm(g, 3 * r, st), "qkv_bwd: dX GEMM");
+  }
+  QL_TRY(side.join(3), "qkv_bwd: join");
+  return QLORA_OK;
+}
+
+int qlora_qkv_fwd(const uint16_t* X, int64_t m, const qlora_qkv_weights* w, uint16_t* Q,
+                  int64_t ld_q, uint16_t* K, int64_t ld_k, uint16_t* V, int64_t ld_v, float* U_save,
+                  void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  uint16_t* const out[3] = {Q, K, V};
+  const int64_t ld[3] = {ld_q, ld_k, ld_v};
+  return qkv_fwd_impl(X, m, qkv_src(w), out, ld, U_save, QLORA_DEQUANT_STAGED, ws, ws_bytes, stream);
+}
+
+int qlora_qkv_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64_t ld_dk,
+                  const uint16_t* dV, int64_t ld_dv, const uint16_t* X, const float* U, int64_t m,
+                  const qlora_qkv_weights* w, uint16_t* dX, const qlora_qkv_grads* grads, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  const uint16_t* const dy[3] = {dQ, dK, dV};
+  const int64_t ld[3] = {ld_dq, ld_dk, ld_dv};
+  return qkv_bwd_impl(dy, ld, X, U, m, qkv_src(w), dX, grads, QLORA_DEQUANT_STAGED, ws, ws_bytes,
+                      stream);
+}
+
+int qlora_qkv16_fwd(const uint16_t* X, int64_t m, const qlora_qkv16_weights* w, uint16_t* Q,
+                    int64_t ld_q, uint16_t* K, int64_t ld_k, uint16_t* V, int64_t ld_v,
+                    float* U_save, void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  uint16_t* const out[3] = {Q, K, V};
+  const int64_t ld[3] = {ld_q, ld_k, ld_v};
+  return qkv_fwd_impl(X, m, qkv_src16(w), out, ld, U_save, MODE_BF16, ws, ws_bytes, stream);
+}
+
+int qlora_qkv16_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64_t ld_dk,
+                    const uint16_t* dV, int64_t ld_dv, const uint16_t* X, const float* U, int64_t m,
+                    const qlora_qkv16_weights* w, uint16_t* dX, const qlora_qkv_grads* grads,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return QLORA_EINVAL;
+  const uint16_t* const dy[3] = {dQ, dK, dV};
+  const int64_t ld[3] = {ld_dq, ld_dk, ld_dv};
+  return qkv_bwd_impl(dy, ld, X, U, m, qkv_src16(w), dX, grads, MODE_BF16, ws, ws_bytes, stream);
+}
+
 }  // extern "C"

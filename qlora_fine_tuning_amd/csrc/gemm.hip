@@ -9,25 +9,36 @@
 // hi/lo is a two-term bf16 split of the fp32 product, which keeps the LoRA
 // term accurate to ~2^-17 relative on bf16 matrix cores.
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 waves (2 per SIMD) laid
-// out 2 x 4, each wave 128 x 64 = 4 x 2 MFMA 32x32x16 tiles (128 fp32
-// accumulators per lane). K is walked in 64-wide steps through a 2-deep LDS
-// ring filled by direct-to-LDS loads (global_load_lds_dwordx4): operands
-// never pass through VGPRs and every row request covers a full 128-byte
-// line. LDS rows are 128 B; the 16-byte chunk index is XOR-swizzled with
-// (row >> 1) & 7 so each 16-lane phase of a ds_read_b128 fragment load hits
-// 16 different bank groups. Fragments of the next substep are read while the
-// matrix cores work on the current one, across the stage barrier too.
+// Two kernels share the arguments (GemmArgs) and the epilogues.
 //
-// A 256 x 256 tile with bf16 operands needs 64 KB of operands per 64-wide
-// k-step, which at full matrix rate exceeds what L2 can feed a CU. With NF4
-// weights (B) the feed carries the 4-bit codes and the fp32 absmax instead
-// (8 KB + 1 KB per step instead of 32 KB); the block dequantizes the next
-// step's codes in LDS, bf16_rne(fp32_rne(level[code] * absmax)) exactly as
-// the standalone dequant, while its matrix cores work on the current step.
-// BSRC_NF4_T reads the weight transposed (the backward dX = dY W): the tile's
-// rows are input features, its K runs over output features, and the dequant
-// writes the transposed bf16 tile.
+// gemm_bf16_kernel (B in bf16: a staged dequant, or 16-bit base weights):
+// 256 x 256 output tile per workgroup of 4 waves (one per SIMD) laid out
+// 2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32
+// accumulators per lane). K is walked in 64-wide steps through a 2-deep LDS
+// ring filled by buffer loads straight into LDS (one buffer resource per
+// operand tile, so rows past M or N read as zeros). Each 8-row, 1 KB load
+// block sits at a 1040-byte pitch, which makes the ds_read_b128 fragment
+// reads conflict-free; the MFMA row order is permuted to match and undone in
+// the epilogue. Fragments of the next substep are read while the matrix
+// cores work on the current one, and sched_group_barrier hints interleave
+// the LDS reads and load issues with the MFMAs. Each step also touches the
+// tile's lines two steps ahead with 4-byte loads, so the next DMA hits L2.
+// Optional extras: A split along K into up to three matrices (dX = sum of
+// dY_p W_p over separately stored dY_p), and an epilogue that writes column
+// ranges to three outputs (q, k, v from one GEMM).
+//
+// gemm_nt_kernel (B as NF4 codes, dequantized in the tile): 256 x 256 tile
+// per workgroup of 8 waves (2 per SIMD) laid out 2 x 4, each wave 128 x 64 =
+// 4 x 2 MFMA 32x32x16 tiles. K is walked in 64-wide steps through a 2-deep
+// LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4); LDS rows
+// are 128 B with the 16-byte chunk index XOR-swizzled by (row >> 1) & 7.
+// The feed carries the 4-bit codes and the fp32 absmax (8 KB + 1 KB per step
+// instead of 32 KB of bf16); the block dequantizes the next step's codes in
+// LDS, bf16_rne(fp32_rne(level[code] * absmax)) exactly as the standalone
+// dequant, while its matrix cores work on the current step. BSRC_NF4_T reads
+// the weight transposed (the backward dX = dY W): the tile's rows are input
+// features, its K runs over output features, and the dequant writes the
+// transposed bf16 tile.
 //
 // Tile order: workgroup ids are dealt to the 8 XCDs round-robin; ids are
 // remapped so that each XCD walks a contiguous range of tiles, grouped 8
@@ -534,11 +545,18 @@ __device__ __forceinline__ void bload_lds(uint64_t base, int nrec, void* lds, ui
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, so, 0, 0);
 }
 
+// bytes a buffer resource covers for `rows` rows of pitch `ld` bf16, capped
+// at the 31-bit record limit (integer arithmetic throughout)
+__device__ __forceinline__ int rec_bytes(int64_t rows, int64_t ld) {
+  const int64_t b = rows * ld * 2;
+  return b < 0x7fffffff ? (int)b : 0x7fffffff;
+}
+
 // offset that no buffer covers: the load returns zeros
 constexpr uint32_t OOB = 0x80000000u;
 }  // namespace
 
-template <int EPI>
+template <int EPI, bool SEGA>
 __global__ __launch_bounds__(256)
 void gemm_bf16_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G_STAGE + 256];
@@ -569,22 +587,70 @@ void gemm_bf16_kernel(GemmArgs p) {
   // ---- operand sources: wave w, load j (0..7) fills DMA block 8w + j ----
   const int64_t rowsA = min(BM, p.M - m0), rowsB = min(BN, p.N - n0);
   const uint64_t bA = (uint64_t)(p.A + (int64_t)m0 * p.lda), bB = (uint64_t)(p.B + (int64_t)n0 * p.ldb);
-  const int nA = (int)min<int64_t>(rowsA * p.lda * 2, 0x7fffffff);
-  const int nB = (int)min<int64_t>(rowsB * p.ldb * 2, 0x7fffffff);
+  const int nA = rec_bytes(rowsA, p.lda);
+  const int nB = rec_bytes(rowsB, p.ldb);
   const int lrow = 64 * wave + (lane >> 3);                      // + 8 j
   const uint32_t voA = (uint32_t)(lrow * p.lda + (lane & 7) * 8) * 2u;
   const uint32_t voB = (uint32_t)(lrow * p.ldb + (lane & 7) * 8) * 2u;
   const uint32_t stA = (uint32_t)(8 * p.lda * 2), stB = (uint32_t)(8 * p.ldb * 2);
+  const uint32_t pfA = (uint32_t)(tid * p.lda * 2), pfB = (uint32_t)(tid * p.ldb * 2);
+  // A operand of k-step kt. SEGA: K is split into up to three segments, each
+  // its own matrix with its own row pitch (segment starts are multiples of
+  // BK, so a step never straddles two). The per-lane offsets are formed from
+  // the segment's pitch at each use (sk: the segment's first byte along K).
+  // Plain scalars, not a struct, so that everything stays in SGPRs.
+  uint64_t sb0 = 0, sb1 = 0, sb2 = 0;
+  int sn0 = 0, sn1 = 0, sn2 = 0, sk1 = 0, sk2 = 0;
+  uint32_t sl0 = 0, sl1 = 0, sl2 = 0;
+  int ks1 = nk, ks2 = nk;
+  if constexpr (SEGA) {
+    ks1 = p.ka1 / BK;
+    ks2 = p.ka2 / BK;
+    sb0 = bA; sn0 = nA; sl0 = (uint32_t)(p.lda * 2);
+    sb1 = (uint64_t)(p.A1 + (int64_t)m0 * p.lda1);
+    sn1 = rec_bytes(rowsA, p.lda1);
+    sl1 = (uint32_t)(p.lda1 * 2);
+    sk1 = ks1 * BK * 2;
+    sb2 = (uint64_t)(p.A2 + (int64_t)m0 * p.lda2);
+    sn2 = rec_bytes(rowsA, p.lda2);
+    sl2 = (uint32_t)(p.lda2 * 2);
+    sk2 = ks2 * BK * 2;
+  }
+  // (base, records, pitch, first K byte) of step kt's segment, as sums of
+  // 0/1 flags times differences (a select chain here was lowered to an
+  // indexed stack array)
+  auto aseg = [&](int kt, uint64_t& b, int& n, uint32_t& l, int& k) {
+    const int f1 = kt >= ks1, f2 = kt >= ks2;
+    b = sb0 + (uint64_t)f1 * (sb1 - sb0) + (uint64_t)f2 * (sb2 - sb1);
+    n = sn0 + f1 * (sn1 - sn0) + f2 * (sn2 - sn1);
+    l = sl0 + (uint32_t)f1 * (sl1 - sl0) + (uint32_t)f2 * (sl2 - sl1);
+    k = f1 * sk1 + f2 * (sk2 - sk1);
+  };
+  const uint32_t lcol = (uint32_t)(lane & 7) * 16u;
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * G_STAGE; };
   auto issue1 = [&](int kt, int q) {   // even q: A load q/2, odd q: B load q/2
     uint8_t* st = stage_ptr(kt);
     const int j = q >> 1, kb = kt * BK * 2;
-    if ((q & 1) == 0) bload_lds<16>(bA, nA, st + (8 * wave + j) * G_PITCH, voA + j * stA, kb);
-    else bload_lds<16>(bB, nB, st + G_OPB + (8 * wave + j) * G_PITCH, voB + j * stB, kb);
+    if ((q & 1) == 0) {
+      if constexpr (SEGA) {
+        uint64_t b; int n; uint32_t l; int k;
+        aseg(kt, b, n, l, k);
+        bload_lds<16>(b, n, st + (8 * wave + j) * G_PITCH, (uint32_t)(lrow + 8 * j) * l + lcol, kb - k);
+      } else {
+        bload_lds<16>(bA, nA, st + (8 * wave + j) * G_PITCH, voA + j * stA, kb);
+      }
+    } else {
+      bload_lds<16>(bB, nB, st + G_OPB + (8 * wave + j) * G_PITCH, voB + j * stB, kb);
+    }
   };
-  const uint32_t pfA = (uint32_t)(tid * p.lda * 2), pfB = (uint32_t)(tid * p.ldb * 2);
   auto prefetch = [&](int kt) {   // tile row tid: touch its 128-B line of step kt (A and B)
-    bload_lds<4>(bA, nA, smem + 2 * G_STAGE, pfA, kt * BK * 2);
+    if constexpr (SEGA) {
+      uint64_t b; int n; uint32_t l; int k;
+      aseg(kt, b, n, l, k);
+      bload_lds<4>(b, n, smem + 2 * G_STAGE, (uint32_t)tid * l, kt * BK * 2 - k);
+    } else {
+      bload_lds<4>(bA, nA, smem + 2 * G_STAGE, pfA, kt * BK * 2);
+    }
     bload_lds<4>(bB, nB, smem + 2 * G_STAGE, pfB, kt * BK * 2);
   };
 
@@ -667,8 +733,8 @@ void gemm_bf16_kernel(GemmArgs p) {
   // columns at or past KE read as zeros ----
   if (p.KE > 0) {
     const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
-    const int neA = (int)min<int64_t>(rowsA * p.ldae * 2, 0x7fffffff);
-    const int neB = (int)min<int64_t>(rowsB * p.ldbe * 2, 0x7fffffff);
+    const int neA = rec_bytes(rowsA, p.ldae);
+    const int neB = rec_bytes(rowsB, p.ldbe);
     for (int e = 0; e * BK < p.KE; ++e) {
       const int c = e * BK + (lane & 7) * 8;   // this lane's first column
       const bool in = c < p.KE;
@@ -726,7 +792,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         stage[(2 * (r & 15) + (r >> 4)) * SP + 8 * (j & 15) + 2 * nt + (j >> 4)] = acc[mt][nt][v];
       }
     __syncthreads();
-    if (EPI == EPI_STORE || EPI == EPI_ACT_BWD) {
+    if (EPI == EPI_STORE || EPI == EPI_STORE3 || EPI == EPI_ACT_BWD) {
       // lane: 8 consecutive columns of one staged row; 4 rows per pass
       const int cc = (lane & 15) * 8;
 #pragma unroll
@@ -735,14 +801,21 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int row = grow(s), col = col0 + cc;
         if (row < p.M && col < p.N) {
           const float* x = &stage[s * SP + cc];
-          if (EPI == EPI_STORE) {
+          if (EPI == EPI_STORE || EPI == EPI_STORE3) {
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             u32x4_t o;
             o[0] = pack_bf16x2(x0[0], x0[1]);
             o[1] = pack_bf16x2(x0[2], x0[3]);
             o[2] = pack_bf16x2(x1[0], x1[1]);
             o[3] = pack_bf16x2(x1[2], x1[3]);
-            *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
+            uint16_t* dst;
+            if (EPI == EPI_STORE3)   // the 8 columns lie in one output (nc1, nc2 multiples of 8)
+              dst = col < p.nc1   ? p.C + (int64_t)row * p.ldc + col
+                    : col < p.nc2 ? p.C1 + (int64_t)row * p.ldc1 + (col - p.nc1)
+                                  : p.C2 + (int64_t)row * p.ldc2 + (col - p.nc2);
+            else
+              dst = p.C + (int64_t)row * p.ldc + col;
+            *(u32x4_t*)dst = o;
           } else {  // staged values are dH
             u32x4_t odg, odu;
 #pragma unroll
@@ -815,23 +888,32 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool SEGA>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
-  gemm_bf16_kernel<EPI><<<dim3(ntm * ntn), dim3(256), 0, stream>>>(a);
+  gemm_bf16_kernel<EPI, SEGA><<<dim3(ntm * ntn), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int BSRC>
 static hipError_t launch_b(const GemmArgs& a, hipStream_t stream) {
   if (BSRC == BSRC_BF16) {
+    if (a.A1) {   // K-segmented A: only the plain store is instantiated
+      if (a.epi != EPI_STORE || !a.A2 || a.ka1 % BK || a.ka2 % BK || a.ka1 > a.ka2 || a.ka2 > a.K)
+        return hipErrorInvalidValue;
+      return launch_bf16<EPI_STORE, true>(a, stream);
+    }
     switch (a.epi) {
-      case EPI_STORE: return launch_bf16<EPI_STORE>(a, stream);
-      case EPI_GATEUP: return launch_bf16<EPI_GATEUP>(a, stream);
-      case EPI_ACT_BWD: return launch_bf16<EPI_ACT_BWD>(a, stream);
+      case EPI_STORE: return launch_bf16<EPI_STORE, false>(a, stream);
+      case EPI_GATEUP: return launch_bf16<EPI_GATEUP, false>(a, stream);
+      case EPI_ACT_BWD: return launch_bf16<EPI_ACT_BWD, false>(a, stream);
+      case EPI_STORE3:
+        if (a.nc1 % 8 || a.nc2 % 8 || a.nc1 > a.nc2 || !a.C1 || !a.C2) return hipErrorInvalidValue;
+        return launch_bf16<EPI_STORE3, false>(a, stream);
     }
     return hipErrorInvalidValue;
   }
+  if (a.A1) return hipErrorInvalidValue;
   switch (a.epi) {
     case EPI_STORE: return launch_t<BSRC, EPI_STORE>(a, stream);
     case EPI_GATEUP: return launch_t<BSRC, EPI_GATEUP>(a, stream);

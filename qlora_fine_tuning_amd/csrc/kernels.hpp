@@ -36,6 +36,8 @@ enum GemmEpilogue {
   EPI_STORE = 0,     // C bf16 [M][N]
   EPI_GATEUP = 1,    // columns interleaved by 32 (gate, up); writes g, u, H = act(g) * u
   EPI_ACT_BWD = 2,   // C = dH [M][h]; reads g, u; writes dgu = [dg | du] [M][2h]
+  EPI_STORE3 = 3,    // bf16 columns [0, nc1) to C, [nc1, nc2) to C1, [nc2, N) to C2
+                     // (bf16 B source only; nc1, nc2 multiples of 8)
 };
 
 // How the B operand ([N][K] weight, K contiguous) reaches the tile:
@@ -52,6 +54,14 @@ struct GemmArgs {
   // main operands: A [M][K] bf16 (lda); B [N][K] bf16 (ldb) or NF4
   const uint16_t* A;
   int64_t lda;
+  // bf16 B source only: A split along K into segments, K columns [0, ka1) from
+  // A, [ka1, ka2) from A1 (lda1), [ka2, K) from A2 (lda2); ka1 <= ka2 <= K,
+  // multiples of 64. A1 == nullptr: one segment.
+  const uint16_t* A1;
+  int64_t lda1;
+  const uint16_t* A2;
+  int64_t lda2;
+  int ka1, ka2;
   const uint16_t* B;
   int64_t ldb;
   int bsrc;
@@ -70,6 +80,11 @@ struct GemmArgs {
   int epi;
   uint16_t* C;
   int64_t ldc;
+  uint16_t* C1;   // EPI_STORE3
+  int64_t ldc1;
+  uint16_t* C2;
+  int64_t ldc2;
+  int nc1, nc2;
   uint16_t* g_out;
   uint16_t* u_out;
   uint16_t* h_out;

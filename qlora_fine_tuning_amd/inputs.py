@@ -101,12 +101,27 @@ class MlpCfg:
     dy_std: float = 0.01
 
 
+@dataclasses.dataclass(frozen=True)
+class QkvCfg:
+    name: str
+    m: int
+    d: int
+    n_q: int
+    n_k: int
+    n_v: int
+    r: int
+    s: float
+    dy_std: float = 0.01
+
+
 TINY_LINEAR = LinearCfg("tiny_linear", 256, 256, 512, 8, 2.0, 1.0)
 QPROJ = LinearCfg("llama7b_q_proj", 8192, 4096, 4096, 16, 1.0, 0.01)
 LLAMA_MLP = MlpCfg("llama7b_mlp", 8192, 4096, 11008, 16, 1.0, "swiglu")
 MISTRAL_KV = LinearCfg("mistral7b_kv_proj", 8192, 4096, 1024, 16, 1.0, 0.01)
 MISTRAL_MLP = MlpCfg("mistral7b_mlp", 8192, 4096, 14336, 16, 1.0, "swiglu")
 GEMMA_MLP = MlpCfg("gemma7b_mlp", 40960, 3072, 24576, 16, 1.0, "geglu_tanh")
+MISTRAL_QKV = QkvCfg("mistral7b_qkv", 8192, 4096, 4096, 1024, 1024, 16, 1.0)
+LLAMA_QKV = QkvCfg("llama7b_qkv", 8192, 4096, 4096, 4096, 4096, 16, 1.0)
 
 
 def linear_inputs(cfg: LinearCfg, dense_w: bool, seed=SEED, role=""):
@@ -150,4 +165,26 @@ def mlp_inputs(cfg: MlpCfg, dense_w: bool, seed=SEED, m=None):
             out[wn] = normal_bf16(wn, (nn, kk), 0.02, seed)
         else:
             out[wn + "_codes"], out[wn + "_absmax"] = synthetic_nf4(wn, nn, kk, 0.02, seed)
+    return out
+
+
+def qkv_inputs(cfg: QkvCfg, dense_w: bool, seed=SEED, m=None):
+    """Inputs of the q, k, v projections of one input (CPU tensors).
+
+    Projection q draws from the plain linear layer's streams (W, A, B, dY), k
+    and v from their own (Wk, Ak, Bk, dYk; Wv, ...); X is shared. dense_w=True
+    gives bf16 base weights "Wq", "Wk", "Wv"; otherwise synthetic NF4 under
+    "<name>_codes" / "<name>_absmax".
+    """
+    m = cfg.m if m is None else m
+    d, r = cfg.d, cfg.r
+    out = dict(X=normal_bf16("X", (m, d), 1.0, seed))
+    for p, role, n in (("q", "", cfg.n_q), ("k", "k", cfg.n_k), ("v", "v", cfg.n_v)):
+        out["A" + p] = kaiming_uniform_bf16("A" + role, (r, d), d, seed)
+        out["B" + p] = normal_bf16("B" + role, (n, r), 0.01, seed)
+        out["dY" + p] = normal_bf16("dY" + role, (m, n), cfg.dy_std, seed)
+        if dense_w:
+            out["W" + p] = normal_bf16("W" + role, (n, d), 0.02, seed)
+        else:
+            out["W" + p + "_codes"], out["W" + p + "_absmax"] = synthetic_nf4("W" + role, n, d, 0.02, seed)
     return out

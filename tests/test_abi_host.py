@@ -171,3 +171,36 @@ def test_quantize_validation_errors(L):
     assert L.qlora_nf4_quantize(FAKE, 4, 96, FAKE, FAKE, None) == -2      # k % 64 != 0
     assert L.qlora_nf4_quantize(FAKE, -1, 64, FAKE, FAKE, None) == -2     # negative rows
     assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == 0       # empty: no work
+
+
+def test_qkv_validation_errors(L):
+    FAKE = 0x1000   # never dereferenced: validation fails first
+    F = ctypes.c_void_p(FAKE)
+    assert L.qlora_qkv_workspace_bytes(64, 128, 128, 64, 64, 16) > 0
+    assert L.qlora_qkv_workspace_bytes(64, 128, 128, 64, 100, 16) == 0   # n_v % 64
+    assert L.qlora_qkv_workspace_bytes(64, 128, 128, 64, 64, 65) == 0    # r > 64
+    nf = lambda n, k: _lib.Nf4(FAKE, FAKE, n, k)  # noqa: E731
+    w = _lib.QkvWeights(nf(128, 128), nf(64, 128), nf(64, 128), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        8, 1.0)
+    ws = L.qlora_qkv_workspace_bytes(64, 128, 128, 64, 64, 8)
+    args = lambda ldq=128, ldk=64, ldv=64, q=F, wsb=ws: (  # noqa: E731
+        F, 64, ctypes.byref(w), q, ldq, F, ldk, F, ldv, F, F, wsb, None)
+    assert L.qlora_qkv_fwd(*args(ldq=120)) == -2                # pitch below the width
+    assert L.qlora_qkv_fwd(*args(ldq=132)) == -2                # pitch not a multiple of 8
+    assert L.qlora_qkv_fwd(*args(q=ctypes.c_void_p(FAKE + 8))) == -2   # misaligned rows
+    assert L.qlora_qkv_fwd(*args(wsb=256)) == -3                # workspace too small
+    w.v = nf(64, 192)                                           # d mismatch
+    assert L.qlora_qkv_fwd(*args()) == -2
+    w.v = nf(64, 128)
+    w.r = 0
+    assert L.qlora_qkv_fwd(*args()) == -1
+    w.r = 8
+    w.b_k = None
+    assert L.qlora_qkv_fwd(*args()) == -1
+    w.b_k = FAKE
+    g = _lib.QkvGrads(FAKE, FAKE, FAKE, None, FAKE, FAKE)
+    assert L.qlora_qkv_bwd(F, 128, F, 64, F, 64, F, F, 64, ctypes.byref(w), F, ctypes.byref(g),
+                           F, ws, None) == -1                   # null gradient
+    w16 = _lib.Qkv16Weights(FAKE, None, FAKE, 128, 128, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            8, 1.0)
+    assert L.qlora_qkv16_fwd(*(lambda a: (a[0], a[1], ctypes.byref(w16)) + a[3:])(args())) == -1

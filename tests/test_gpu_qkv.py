@@ -1,0 +1,190 @@
+"""GPU parity of the q, k, v projections on one shared input (qlora_qkv_* and
+qlora_qkv16_*, through the C ABI) against the fp64 oracle.
+
+Bar: max|gpu - oracle| / max|oracle| <= 2e-2 per output tensor. Small cases
+compare every element; they cover the one-row-product K-extension (3r <= 64)
+and the per-projection one (3r > 64), ranks whose extension width is padded,
+ragged token counts and unequal projection widths. Full-size Mistral-7B
+(4096 -> 4096 / 1024 / 1024) and Llama-7B (3 x 4096) shapes compare sampled
+token rows of Q, K, V, U and dX and the full LoRA gradients. Outputs written
+into column slices of one buffer, and upstream gradients read from slices or
+from padded rows, must give the same bits as separate dense tensors.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import qlora_fine_tuning_amd as Q
+from oracle import qlora as OQ
+from qlora_fine_tuning_amd import inputs as I
+
+from _util import TOL, dequant_oracle, f64, need_gpu, quantize_dense, rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+P = ("q", "k", "v")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _case(cfg, m=None, dense=True, w16=False, seed=3407):
+    d = I.qkv_inputs(cfg, dense_w=dense or w16, seed=seed, m=m)
+    if dense and not w16:
+        for p in P:
+            d["W" + p + "_codes"], d["W" + p + "_absmax"] = quantize_dense(d.pop("W" + p))
+    return d
+
+
+def _weights(cfg, d, w16):
+    lora = [d[k + p].to(DEV) for p in P for k in ("A", "B")]
+    if w16:
+        return Q.Qkv16Weights(*(d["W" + p].to(DEV) for p in P), *lora, s=cfg.s)
+    nf = lambda p: Q.NF4Weight(d["W" + p + "_codes"].to(DEV), d["W" + p + "_absmax"].to(DEV))  # noqa: E731
+    return Q.QkvWeights(nf("q"), nf("k"), nf("v"), *lora, s=cfg.s)
+
+
+def _run(cfg, d, w16=False, out=None, dys=None, need_dx=True):
+    w = _weights(cfg, d, w16)
+    X = d["X"].to(DEV)
+    if dys is None:
+        dys = [d["dY" + p].to(DEV) for p in P]
+    say(f"qkv m={X.shape[0]} d={cfg.d} n=({cfg.n_q},{cfg.n_k},{cfg.n_v}) r={cfg.r} "
+        f"w16={w16} slices={out is not None}")
+    fwd, bwd = (Q.qkv16_fwd, Q.qkv16_bwd) if w16 else (Q.qkv_fwd, Q.qkv_bwd)
+    Yq, Yk, Yv, U = fwd(X, w, out=out)
+    gr = bwd(*dys, X, U, w, need_dx=need_dx)
+    torch.cuda.synchronize()
+    return dict(Yq=Yq, Yk=Yk, Yv=Yv, U=U, **gr)
+
+
+def _oracle(cfg, d, w16=False, rows=None):
+    Ws = [f64(d["W" + p]) if w16 else dequant_oracle(d["W" + p + "_codes"], d["W" + p + "_absmax"])
+          for p in P]
+    As = [f64(d["A" + p]) for p in P]
+    Bs = [f64(d["B" + p]) for p in P]
+    X = f64(d["X"])
+    dYs = [f64(d["dY" + p]) for p in P]
+    Us = [X @ A.T for A in As]
+    _, dA, dB = OQ.qkv_bwd(dYs, X, Us, Ws, As, Bs, cfg.s)   # LoRA grads: always all tokens
+    out = {"dA" + p: dA[i] for i, p in enumerate(P)}
+    out.update({"dB" + p: dB[i] for i, p in enumerate(P)})
+    if rows is not None:
+        X, dYs, Us = X[rows], [t[rows] for t in dYs], [u[rows] for u in Us]
+    Ys, _ = OQ.qkv_fwd(X, Ws, As, Bs, cfg.s)
+    dX, _, _ = OQ.qkv_bwd(dYs, X, Us, Ws, As, Bs, cfg.s)
+    out.update(Yq=Ys[0], Yk=Ys[1], Yv=Ys[2], U=np.concatenate(Us, axis=1), dX=dX)
+    return out
+
+
+def _check(got, want, rows=None):
+    errs = {}
+    for k, ref in want.items():
+        g = got[k]
+        if rows is not None and k in ("Yq", "Yk", "Yv", "U", "dX"):
+            g = g[torch.as_tensor(rows, device=g.device)]
+        errs[k] = rel_err(g, ref)
+    say(f"  rel errors: {errs}")
+    for k, e in errs.items():
+        assert e <= TOL, (k, e)
+
+
+def _rows(m, n=32, seed=7):
+    g = np.random.default_rng(seed)
+    extra = g.choice(m, size=min(n, m), replace=False).tolist()
+    return np.array(sorted(set([0, 1, m // 2, m - 1] + extra)))
+
+
+SMALL = [I.QkvCfg("one_ext", 300, 192, 256, 128, 64, 8, 2.0, 1.0),      # 3r <= 64
+         I.QkvCfg("per_proj", 129, 128, 64, 128, 192, 32, 0.5, 1.0),   # 3r > 64
+         I.QkvCfg("padded_r22", 77, 64, 64, 64, 64, 22, 1.0, 1.0),    # KE 144 > 6r
+         I.QkvCfg("padded_r4", 65, 128, 128, 64, 64, 4, 4.0, 1.0),     # KE 32 > 6r
+         I.QkvCfg("r64", 40, 64, 64, 64, 128, 64, 0.25, 1.0),
+         I.QkvCfg("one_token", 1, 64, 64, 64, 64, 1, 1.0, 1.0)]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_qkv_small(cfg):
+    d = _case(cfg, seed=21)
+    _check(_run(cfg, d), _oracle(cfg, d))
+
+
+@pytest.mark.parametrize("cfg", SMALL[:3], ids=lambda c: c.name)
+def test_qkv16_small(cfg):
+    d = _case(cfg, w16=True, seed=22)
+    _check(_run(cfg, d, w16=True), _oracle(cfg, d, w16=True))
+
+
+def test_qkv_slices_and_pitches_give_identical_bits():
+    cfg = SMALL[0]
+    d = _case(cfg, seed=23)
+    m, ns = cfg.m, (cfg.n_q, cfg.n_k, cfg.n_v)
+    ref = _run(cfg, d)
+    # outputs into column slices of one [m][nq + nk + nv] buffer
+    buf = torch.full((m, sum(ns)), float("nan"), dtype=torch.bfloat16, device=DEV)
+    offs = np.cumsum((0,) + ns)
+    out = tuple(buf[:, offs[i]:offs[i + 1]] for i in range(3))
+    # upstream gradients: one concatenated buffer (slices), then padded rows
+    cat = torch.cat([d["dY" + p] for p in P], dim=1).to(DEV)
+    slices = [cat[:, offs[i]:offs[i + 1]] for i in range(3)]
+    got = _run(cfg, d, out=out, dys=slices)
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), k
+    assert torch.equal(buf[:, :ns[0]], ref["Yq"]) and torch.equal(buf[:, offs[2]:], ref["Yv"])
+    padded = []
+    for p, n in zip(P, ns):
+        t = torch.zeros((m, n + 72), dtype=torch.bfloat16, device=DEV)
+        t[:, :n] = d["dY" + p].to(DEV)
+        padded.append(t[:, :n])
+    got2 = _run(cfg, d, dys=padded)
+    for k in ref:
+        assert torch.equal(ref[k], got2[k]), k
+
+
+def test_qkv_without_dx_and_deterministic():
+    cfg = SMALL[1]
+    d = _case(cfg, seed=24)
+    a = _run(cfg, d)
+    b = _run(cfg, d, need_dx=False)
+    assert b["dX"] is None
+    for k in a:
+        if k != "dX":
+            assert torch.equal(a[k], b[k]), k
+    c = _run(cfg, d)
+    for k in a:
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_qkv_empty_batch_zero_grads():
+    cfg = dataclasses.replace(SMALL[0], m=0)
+    d = _case(cfg, seed=25)
+    say("qkv empty batch")
+    w = _weights(cfg, d, False)
+    X = torch.empty((0, cfg.d), dtype=torch.bfloat16, device=DEV)
+    Yq, Yk, Yv, U = Q.qkv_fwd(X, w)
+    dys = [torch.empty((0, n), dtype=torch.bfloat16, device=DEV) for n in (cfg.n_q, cfg.n_k, cfg.n_v)]
+    gr = Q.qkv_bwd(*dys, X, U, w)
+    torch.cuda.synchronize()
+    for k in ("dAq", "dBq", "dAk", "dBk", "dAv", "dBv"):
+        assert torch.count_nonzero(gr[k]).item() == 0, k
+    assert gr["dX"].shape == (0, cfg.d) and Yq.shape == (0, cfg.n_q) and U.shape == (0, 3 * cfg.r)
+
+
+@pytest.mark.parametrize("cfg", [I.MISTRAL_QKV, I.LLAMA_QKV], ids=lambda c: c.name)
+def test_qkv_full_size_sampled_rows(cfg):
+    d = _case(cfg, dense=False)
+    got = _run(cfg, d)
+    rows = _rows(cfg.m)
+    _check(got, _oracle(cfg, d, rows=rows), rows=rows)
+
+
+def test_qkv16_full_size_sampled_rows():
+    cfg = I.MISTRAL_QKV
+    d = _case(cfg, w16=True)
+    got = _run(cfg, d, w16=True)
+    rows = _rows(cfg.m, seed=8)
+    _check(got, _oracle(cfg, d, w16=True, rows=rows), rows=rows)
