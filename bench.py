@@ -1,4 +1,4 @@
-"""Benchmark: QLoRA gated-MLP forward + backward on one MI355X.
+"""Benchmark: QLoRA gated-MLP (or q/k/v) forward + backward on one MI355X.
 
 Workload (default): Llama-7B MLP block, 8192 tokens (4 x 2048) x 4096 ->
 11008 -> 4096, NF4 (blocksize 64) gate/up/down, LoRA rank 16, s = 1, SwiGLU,
@@ -6,6 +6,11 @@ synthetic seeded inputs already resident in HBM. One step = qlora_mlp_fwd +
 qlora_mlp_bwd (every kernel of the path). The metric counts algorithmic
 FLOPs only: six base products 2*m*d*h plus the LoRA products (recompute,
 dequant and elementwise work are not counted).
+
+Other workloads: the Mistral-7B / Gemma-7B MLP shapes, and the q/k/v
+projections of one input at the Mistral-7B (4096 -> 4096 / 1024 / 1024) and
+Llama-7B (3 x 4096) shapes, 8192 tokens; one step = qlora_qkv_fwd +
+qlora_qkv_bwd, FLOPs 4*m*d*n + 6*m*r*(d + n) per projection.
 
 Prints ONE JSON line. Extra fields: roofline (the base-GEMM kernel, timed
 live with HIP events on its launch stream) and cpu_baseline (the fp64 CPU
@@ -25,6 +30,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
 METRIC = "QLoRA MLP fwd+bwd TFLOP/s + % bf16 MFMA peak, Llama-7B shape, 8192 tok"
+METRIC_QKV = "QLoRA q/k/v fwd+bwd TFLOP/s + % bf16 MFMA peak, {model} shape, 8192 tok"
+MLP_WORKLOADS = ["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"]
+QKV_WORKLOADS = ["mistral7b_qkv", "llama7b_qkv"]
+QUANT_WORKLOAD = "llama7b_mlp_quantize"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+QUANT_BYTES_PER_WEIGHT = 2 + 0.5 + 4 / 64   # bf16 in; codes + fp32 absmax out
 
 
 def parse():
@@ -33,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama7b_mlp",
-                   choices=["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"])
+                   choices=MLP_WORKLOADS + QKV_WORKLOADS + [QUANT_WORKLOAD])
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--base", default="nf4", choices=["nf4", "bf16"],
                    help="base weights: NF4 (QLoRA, default) or bf16 (16-bit LoRA variant)")
@@ -67,6 +78,12 @@ def mlp_flops(m, d, h, r):
     return 6 * 2 * m * d * h + 3 * 3 * 2 * m * r * (d + h)
 
 
+def qkv_flops(m, d, ns, r):
+    """Algorithmic FLOPs of the q/k/v forward + backward: per projection two
+    base products 2*m*d*n and 2*m*r*(d+n) of LoRA forward, twice that backward."""
+    return sum(4 * m * d * n + 6 * m * r * (d + n) for n in ns)
+
+
 def gemm_traffic(lib_src_dir, workload, mode):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
     or None when it was taken on another workload or dequant mode, or the
@@ -74,12 +91,12 @@ def gemm_traffic(lib_src_dir, workload, mode):
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
     h = hashlib.sha256(open(os.path.join(lib_src_dir, "gemm.hip"), "rb").read()).hexdigest()
-    if (rec.get("gemm_hip_sha256") != h or rec.get("workload_name") != workload
-            or rec.get("dequant_mode") != mode):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for rec in json.load(open(path)):
+        if (rec.get("gemm_hip_sha256") == h and rec.get("workload_name") == workload
+                and rec.get("dequant_mode") == mode):
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(cfg, d, tokens):
@@ -112,6 +129,98 @@ def cpu_baseline(cfg, d, tokens):
             "tokens_per_s": round(tokens / t, 3), "seconds": round(t, 3)}
 
 
+def cpu_baseline_qkv(cfg, d, tokens):
+    """fp64 oracle (as it stands) on the first `tokens` tokens of the q/k/v workload."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import nf4 as onf4
+    from oracle import qlora as oq
+
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    t0 = time.perf_counter()
+    Ws = [onf4.dequant_f64(d["W" + p + "_codes"].numpy(), d["W" + p + "_absmax"].numpy())
+          for p in "qkv"]
+    t_dq = time.perf_counter() - t0
+    As = [f64(d["A" + p]) for p in "qkv"]
+    Bs = [f64(d["B" + p]) for p in "qkv"]
+    X = f64(d["X"][:tokens])
+    dYs = [f64(d["dY" + p][:tokens]) for p in "qkv"]
+    t0 = time.perf_counter()
+    _, Us = oq.qkv_fwd(X, Ws, As, Bs, cfg.s)
+    oq.qkv_bwd(dYs, X, Us, Ws, As, Bs, cfg.s)
+    t = time.perf_counter() - t0 + t_dq
+    flops = oq.qkv_algorithmic_flops(tokens, cfg.d, (cfg.n_q, cfg.n_k, cfg.n_v), cfg.r)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{tokens} of {cfg.m} tokens with the full {cfg.name} weights, fp64 numpy: "
+                      f"weight dequant {t_dq:.2f} s + fwd/bwd {t - t_dq:.2f} s",
+            "tokens_per_s": round(tokens / t, 3), "seconds": round(t, 3)}
+
+
+def bench_quantize(a):
+    """NF4 quantization of the three Llama-7B MLP weights (gate, up [11008][4096],
+    down [4096][11008]) from bf16, one step = the three qlora_nf4_quantize calls.
+    HBM-bound: 2 B read and 0.5 + 4/64 B written per weight."""
+    import torch
+
+    import qlora_fine_tuning_amd as Q
+    from qlora_fine_tuning_amd import inputs as I
+
+    dev = "cuda:0"
+    cfg = I.LLAMA_MLP
+    shapes = {"Wg": (cfg.h, cfg.d), "Wu": (cfg.h, cfg.d), "Wd": (cfg.d, cfg.h)}
+    Ws = {wn: I.normal_bf16(wn, sh, 0.02) for wn, sh in shapes.items()}
+    Wd = {wn: w.to(dev) for wn, w in Ws.items()}
+    outs = {wn: Q.nf4_quantize(w) for wn, w in Wd.items()}
+
+    def step():
+        for wn, w in Wd.items():
+            Q.nf4_quantize(w, out=outs[wn])
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / a.steps
+    nw = sum(n * k for n, k in shapes.values())
+    gbs = nw * QUANT_BYTES_PER_WEIGHT / (ms / 1e3) / 1e9
+    out = {
+        "metric": "NF4 quantize (bf16 -> codes + fp32 absmax) GB/s, Llama-7B MLP weights",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->nf4", "data": "synthetic",
+        "config": {"workload": QUANT_WORKLOAD, "weights": [list(v) for v in shapes.values()],
+                   "blocksize": 64, "global_batch": None, "parallelism": "none (1 GPU)"},
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "kernel": "nf4_quantize_kernel", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_weight": QUANT_BYTES_PER_WEIGHT,
+                     "launches_per_step": 3, "avg_launch_ms": round(ms / 3, 4)},
+    }
+    if a.cpu_tokens > 0:   # oracle quantizer on a bounded sample of gate rows
+        from oracle import nf4 as onf4
+        rows = 4096
+        bits = Ws["Wg"][:rows].contiguous().view(torch.int16).numpy().view("uint16")
+        t0 = time.perf_counter()
+        onf4.quantize(bits)
+        t = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(rows * cfg.d * QUANT_BYTES_PER_WEIGHT / t / 1e9, 4),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {cfg.h} gate rows ({rows * cfg.d} weights), fp64 numpy",
+                               "seconds": round(t, 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -122,31 +231,57 @@ def main():
               "the multi-GPU data-parallel design is described, not built.", file=sys.stderr)
         sys.exit(2)
 
+    if a.workload == QUANT_WORKLOAD:
+        bench_quantize(a)
+        return
+
     import torch
 
     import qlora_fine_tuning_amd as Q
     from qlora_fine_tuning_amd import _lib
     from qlora_fine_tuning_amd import inputs as I
 
+    qkv = a.workload in QKV_WORKLOADS
     cfg = {"llama7b_mlp": I.LLAMA_MLP, "mistral7b_mlp": I.MISTRAL_MLP,
-           "gemma7b_mlp": I.GEMMA_MLP}[a.workload]
+           "gemma7b_mlp": I.GEMMA_MLP, "mistral7b_qkv": I.MISTRAL_QKV,
+           "llama7b_qkv": I.LLAMA_QKV}[a.workload]
     dev = "cuda:0"
     w16 = a.base == "bf16"
-    d = I.mlp_inputs(cfg, dense_w=w16)
-    lora = [d[k].to(dev) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")]
-    if w16:
-        w = Q.Mlp16Weights(d["Wg"].to(dev), d["Wu"].to(dev), d["Wd"].to(dev), *lora, s=cfg.s,
-                           act=cfg.act)
-        nbytes = Q.mlp16_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r)
+    if qkv:
+        if a.mode == "fused":
+            sys.exit("the q/k/v path always stages its bf16 weights (no fused mode)")
+        d = I.qkv_inputs(cfg, dense_w=w16)
+        lora = [d[k + p].to(dev) for p in "qkv" for k in ("A", "B")]
+        if w16:
+            w = Q.Qkv16Weights(*(d["W" + p].to(dev) for p in "qkv"), *lora, s=cfg.s)
+        else:
+            nf = lambda p: Q.NF4Weight(d["W" + p + "_codes"].to(dev), d["W" + p + "_absmax"].to(dev))  # noqa: E731
+            w = Q.QkvWeights(nf("q"), nf("k"), nf("v"), *lora, s=cfg.s)
+        ns = (cfg.n_q, cfg.n_k, cfg.n_v)
+        nbytes = Q.qkv_workspace_bytes(cfg.m, cfg.d, *ns, cfg.r)
+        X = d["X"].to(dev)
+        dYs = [d["dY" + p].to(dev) for p in "qkv"]
+        dY = None
     else:
-        nf = lambda wn: Q.NF4Weight(d[wn + "_codes"].to(dev), d[wn + "_absmax"].to(dev))  # noqa: E731
-        w = Q.MlpWeights(nf("Wg"), nf("Wu"), nf("Wd"), *lora, s=cfg.s, act=cfg.act)
-        nbytes = Q.mlp_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r, a.mode)
-    X, dY = d["X"].to(dev), d["dY"].to(dev)
+        d = I.mlp_inputs(cfg, dense_w=w16)
+        lora = [d[k].to(dev) for k in ("Ag", "Bg", "Au", "Bu", "Ad", "Bd")]
+        if w16:
+            w = Q.Mlp16Weights(d["Wg"].to(dev), d["Wu"].to(dev), d["Wd"].to(dev), *lora, s=cfg.s,
+                               act=cfg.act)
+            nbytes = Q.mlp16_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r)
+        else:
+            nf = lambda wn: Q.NF4Weight(d[wn + "_codes"].to(dev), d[wn + "_absmax"].to(dev))  # noqa: E731
+            w = Q.MlpWeights(nf("Wg"), nf("Wu"), nf("Wd"), *lora, s=cfg.s, act=cfg.act)
+            nbytes = Q.mlp_workspace_bytes(cfg.m, cfg.d, cfg.h, cfg.r, a.mode)
+        X, dY = d["X"].to(dev), d["dY"].to(dev)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step():
-        if w16:
+        if qkv:
+            fwd, bwd = (Q.qkv16_fwd, Q.qkv16_bwd) if w16 else (Q.qkv_fwd, Q.qkv_bwd)
+            _, _, _, U = fwd(X, w, ws=ws)
+            bwd(*dYs, X, U, w, ws=ws)
+        elif w16:
             _, sv = Q.mlp16_fwd(X, w, ws=ws)
             Q.mlp16_bwd(dY, X, sv, w, ws=ws)
         else:
@@ -172,20 +307,26 @@ def main():
 
     peak_meas, shader_ghz = Q.probe_mfma_peak(20000)
 
-    flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
+    flops = qkv_flops(cfg.m, cfg.d, ns, cfg.r) if qkv else mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
     traffic = None if w16 else gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"),
-                                            cfg.name, "staged" if a.mode == "auto" else a.mode)
+                                            cfg.name, "staged" if (qkv or a.mode == "auto") else a.mode)
+    if qkv:
+        metric = METRIC_QKV.format(model="Mistral-7B" if cfg is I.MISTRAL_QKV else "Llama-7B")
+        shape = {"d": cfg.d, "n_q": cfg.n_q, "n_k": cfg.n_k, "n_v": cfg.n_v}
+    else:
+        metric = METRIC
+        shape = {"d": cfg.d, "h": cfg.h, "act": cfg.act}
     out = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": cfg.m, "d": cfg.d, "h": cfg.h, "r": cfg.r,
-                   "s": cfg.s, "act": cfg.act,
+        "config": {"workload": cfg.name, "tokens": cfg.m, **shape, "r": cfg.r, "s": cfg.s,
                    "weights": "bf16 (16-bit LoRA)" if w16 else "nf4 blocksize 64, fp32 absmax",
-                   "dequant_mode": "none" if w16 else a.mode, "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
+                   "dequant_mode": "none" if w16 else ("staged" if qkv else a.mode),
+                   "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.m / (ms / 1e3), 1),
         "wall_s_timed": round(wall, 3),
@@ -202,7 +343,8 @@ def main():
     if a.cpu_tokens > 0 and not w16:
         del X, dY, ws, w
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, d, min(a.cpu_tokens, cfg.m))
+        base = cpu_baseline_qkv if qkv else cpu_baseline
+        out["cpu_baseline"] = base(cfg, d, min(a.cpu_tokens, cfg.m))
     print(json.dumps(out), flush=True)
 
 

@@ -138,7 +138,8 @@ int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);
  * ownership as for qlora_nf4_dequant (device pointers owned by the caller).
  * Errors: QLORA_ESHAPE if k % 64 != 0 or a size is negative or >= 2^31;
  * n*k == 0 returns QLORA_OK and touches nothing (pointers may be NULL);
- * otherwise QLORA_EINVAL for a NULL pointer. Asynchronous on `stream`. */
+ * otherwise QLORA_EINVAL for a NULL pointer, QLORA_ESHAPE unless w is
+ * 16-byte and codes, absmax 4-byte aligned. Asynchronous on `stream`. */
 int qlora_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
                        void* stream);
 

@@ -114,14 +114,20 @@ def nf4_dequant(w: NF4Weight) -> torch.Tensor:
     return out
 
 
-def nf4_quantize(W: torch.Tensor) -> NF4Weight:
-    """bf16 W [n][k] (k % 64 == 0) -> NF4Weight (codes, absmax) on W's device."""
+def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None) -> NF4Weight:
+    """bf16 W [n][k] (k % 64 == 0) -> NF4Weight (codes, absmax) on W's device
+    (written into `out` if given)."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D")
     n, k = W.shape
     _need(W, "W", torch.bfloat16, (n, k))
-    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
-    absmax = torch.empty((n, k // 64), dtype=torch.float32, device=W.device)
+    if out is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
+        absmax = torch.empty((n, k // 64), dtype=torch.float32, device=W.device)
+    else:
+        codes, absmax = out.codes, out.absmax
+        _need(codes, "codes", torch.uint8, (n, k // 2))
+        _need(absmax, "absmax", torch.float32, (n, k // 64))
     _lib.check(_lib.lib().qlora_nf4_quantize(_ptr(W), n, k, _ptr(codes), _ptr(absmax), _stream()),
                "qlora_nf4_quantize")
     return NF4Weight(codes, absmax)

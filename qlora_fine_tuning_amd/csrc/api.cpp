@@ -340,6 +340,7 @@ int qlora_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, 
     return QLORA_ESHAPE;
   if (n * k == 0) return QLORA_OK;
   if (!w || !codes || !absmax) return QLORA_EINVAL;
+  if (((uintptr_t)w & 15) || ((uintptr_t)codes & 3) || ((uintptr_t)absmax & 3)) return QLORA_ESHAPE;
   QL_TRY(launch_nf4_quantize(w, n, k, codes, absmax, (hipStream_t)stream), "nf4_quantize");
   return QLORA_OK;
 }

@@ -112,60 +112,67 @@ __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
   }
 }
 
-// Quantizer (bf16 weights -> NF4), one thread per 64-weight block. For
-// every block: absmax = max |w| (exact: a bf16 value, stored as fp32); each
-// weight gets the level nearest to x = w / absmax, with x and the distances
-// |x - level| formed in fp64 and ties going to the lower code; an all-zero
-// block gets absmax 0 and code 7 (the exact zero) everywhere. Weights must be
-// finite. Packing as for the dequant: element 2j in the high nibble of byte j.
+// Quantizer (bf16 weights -> NF4). A lane takes 8 consecutive weights (16 B)
+// and 8 lanes a 64-weight block, so a wave reads 1 KB contiguously. Per
+// block: absmax = max |w| (exact: a bf16 value, stored as fp32), reduced over
+// the block's 8 lanes. The code of w is the level nearest to w / absmax with
+// ties to the lower code, found as the number of level midpoints
+// mu_i = (L_i + L_{i+1}) / 2 with w > mu_i * absmax, compared in fp64: both
+// mu_i and the product are exact there (24 + 8 significant bits), so the
+// comparison is the exact one. A quotient of two bf16 values is either on a
+// midpoint or at least 2^-34 (relative) away from it, so a nearest-level search
+// on the fp64 quotient gives the same codes. An all-zero block gets absmax 0
+// and code 7 (the exact zero) everywhere. Weights must be finite. Packing as
+// for the dequant: element 2j in the high nibble of byte j.
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t* __restrict__ w,
                                                            int64_t nblocks,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax) {
-  double lv[16];
+  double mu[15];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = (double)__uint_as_float(c_nf4_levels[i]);
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
-       b += (int64_t)gridDim.x * blockDim.x) {
-    u32x4_t v[8];
+  for (int i = 0; i < 15; ++i)
+    mu[i] = 0.5 * ((double)__uint_as_float(c_nf4_levels[i]) + (double)__uint_as_float(c_nf4_levels[i + 1]));
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = nblocks * 8;   // 8-weight groups
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // base is wave-aligned, so the loop condition is uniform across the wave and
+  // a block's 8 lanes are either all in range or all out of it
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63); base < groups;
+       base += stride) {
+    const int64_t g = base + lane;
+    const bool in = g < groups;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (in) v = *(const u32x4_t*)(w + g * 8);
+    float wf[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = *(const u32x4_t*)(w + b * 64 + q * 8);
+    for (int e = 0; e < 4; ++e) {
+      wf[2 * e] = bf16_to_f32(v[e] & 0xFFFFu);
+      wf[2 * e + 1] = bf16_to_f32(v[e] >> 16);
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(wf[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    double t[15];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32(v[q][e] & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(v[q][e] >> 16)));
-      }
-    const double a = (double)amax;
-    u32x4_t out[2];
+    for (int i = 0; i < 15; ++i) t[i] = mu[i] * (double)amax;
+    uint32_t word = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t word = 0;
+    for (int e = 0; e < 8; ++e) {
+      const double x = (double)wf[e];
+      uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t byte = 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {   // t = 0: element 2j (high nibble), t = 1: 2j + 1
-          const float wf = bf16_to_f32(t ? (v[q][e] >> 16) : (v[q][e] & 0xFFFFu));
-          const double x = amax == 0.0f ? 0.0 : (double)wf / a;
-          int best = 0;
-          double bd = fabs(x - lv[0]);
-#pragma unroll
-          for (int i = 1; i < 16; ++i) {
-            const double di = fabs(x - lv[i]);
-            if (di < bd) { bd = di; best = i; }
-          }
-          byte |= (uint32_t)best << (t ? 0 : 4);
-        }
-        word |= byte << (8 * e);
-      }
-      out[q >> 2][q & 3] = word;
+      for (int i = 0; i < 15; ++i) c += x > t[i] ? 1u : 0u;
+      if (amax == 0.0f) c = 7;
+      // element 2j -> high nibble of byte j
+      word |= c << (8 * (e >> 1) + ((e & 1) ? 0 : 4));
     }
-    *(u32x4_t*)(codes + b * 32) = out[0];
-    *(u32x4_t*)(codes + b * 32 + 16) = out[1];
-    absmax[b] = amax;
+    if (in) {
+      *(uint32_t*)(codes + g * 4) = word;
+      if ((lane & 7) == 0) absmax[g >> 3] = amax;
+    }
   }
 }
 
@@ -173,8 +180,8 @@ hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t*
                                float* absmax, hipStream_t stream) {
   const int64_t nblocks = n * (k / 64);
   if (nblocks == 0) return hipSuccess;
-  int64_t grid = (nblocks + 255) / 256;
-  if (grid > 256 * 64) grid = 256 * 64;
+  int64_t grid = (nblocks * 8 + 255) / 256;   // a thread per 8 weights
+  if (grid > 256 * 32) grid = 256 * 32;
   nf4_quantize_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(w, nblocks, codes, absmax);
   return hipGetLastError();
 }

@@ -171,6 +171,7 @@ def test_quantize_validation_errors(L):
     assert L.qlora_nf4_quantize(FAKE, 4, 96, FAKE, FAKE, None) == -2      # k % 64 != 0
     assert L.qlora_nf4_quantize(FAKE, -1, 64, FAKE, FAKE, None) == -2     # negative rows
     assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == 0       # empty: no work
+    assert L.qlora_nf4_quantize(ctypes.c_void_p(0x1008), 4, 64, FAKE, FAKE, None) == -2   # misaligned
 
 
 def test_qkv_validation_errors(L):

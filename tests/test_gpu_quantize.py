@@ -83,3 +83,13 @@ def test_quantize_then_dequant_round_trip():
     torch.cuda.synchronize()
     assert torch.equal(q.codes, q2.codes)
     assert torch.equal(q.absmax, q2.absmax)
+
+
+def test_quantize_into_given_buffers():
+    W = I.normal_bf16("W", (128, 256), 0.02, seed=9).to(DEV)
+    ref = Q.nf4_quantize(W)
+    out = Q.NF4Weight(torch.full_like(ref.codes, 0xAA), torch.full_like(ref.absmax, -1.0))
+    got = Q.nf4_quantize(W, out=out)
+    torch.cuda.synchronize()
+    assert got.codes.data_ptr() == out.codes.data_ptr()
+    assert torch.equal(got.codes, ref.codes) and torch.equal(got.absmax, ref.absmax)

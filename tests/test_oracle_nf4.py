@@ -176,3 +176,45 @@ def test_packing_fixture():
 def test_rejects_ragged_k():
     with pytest.raises(ValueError):
         nf4.quantize(np.zeros((1, 96), dtype=np.uint16))
+
+
+def test_quantize_is_exact_nearest_level_for_every_significand_pair():
+    """For every pair of bf16 significands (absmax in [1, 2); weight magnitudes
+    in the 12 binades at and below it, both signs; zeros), the quantizer's fp64
+    nearest-level search gives the code of exact rational arithmetic: the number
+    of level midpoints strictly below w / absmax (a tie goes to the lower code).
+    Exact comparison in int64: with absmax = m_a / 128, w = +-m_w 2^e / 128 and a
+    midpoint mu = M / 2^28, w / absmax > mu  <=>  m_w 2^(e+39) > M m_a 2^11.
+    (No quotient of two bf16 values lands exactly on a midpoint of this table,
+    so the tie rule never acts on bf16 weights.)"""
+    L = nf4.nf4_levels().astype(np.float64)
+    mids = (L[:-1] + L[1:]) / 2
+    M = np.array([int(v * 2 ** 28) for v in mids], dtype=np.int64)
+    assert np.array_equal(M.astype(np.float64) / 2 ** 28, mids)       # midpoints exactly representable
+    mw = np.arange(128, 256, dtype=np.int64)
+    rows, want = [], []
+    for ma in range(128, 256):
+        a = ma / 128.0
+        vals, ints = [], []
+        for e in range(0, -12, -1):
+            for m in mw:
+                if e == 0 and m > ma:
+                    continue
+                for sgn in (1, -1):
+                    vals.append(sgn * m * 2.0 ** e / 128.0)
+                    ints.append(sgn * int(m) << (e + 39))
+        vals += [0.0, -0.0]
+        ints += [0, 0]
+        ints = np.array(ints, dtype=np.int64)
+        codes = (ints[:, None] > (M * ma * 2 ** 11)[None, :]).sum(axis=1)
+        for s in range(0, len(vals), 63):                       # block: absmax first, then 63 weights
+            chunk = vals[s:s + 63]
+            pad = 63 - len(chunk)
+            rows.append([a] + chunk + [0.0] * pad)
+            want.append([15] + codes[s:s + 63].tolist() + [7] * pad)
+    w = np.array(rows, dtype=np.float32)
+    bits = (w.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(nf4.bf16_bits_to_f64(bits), w.astype(np.float64))   # all exact in bf16
+    packed, absmax = nf4.quantize(bits)
+    assert np.array_equal(absmax[:, 0], w[:, 0])
+    assert np.array_equal(nf4.unpack_codes(packed), np.array(want, dtype=np.uint8))
