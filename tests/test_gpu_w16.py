@@ -60,6 +60,18 @@ def test_linear16_matches_oracle(m, k, n, r):
     _check(got, dict(Y=Y, U=U, dX=dX, dA=dA, dB=dB))
 
 
+@pytest.mark.parametrize("r", [16, 64])
+def test_linear16_rank_stabilized_scale(r):
+    # RSLoRA: s = alpha / sqrt(r) instead of alpha / r (alpha 16)
+    cfg = I.LinearCfg("rslora", 200, 256, 192, r, 16.0 / np.sqrt(r), 1.0)
+    d = I.linear_inputs(cfg, dense_w=True, seed=17)
+    got = _run_linear16(cfg, d)
+    X, W, A, B, dY = (f64(d[k_]) for k_ in ("X", "W", "A", "B", "dY"))
+    Y, U = OQ.linear_fwd(X, W, A, B, cfg.s)
+    dX, dA, dB, _ = OQ.linear_bwd(dY, X, U, W, A, B, cfg.s)
+    _check(got, dict(Y=Y, U=U, dX=dX, dA=dA, dB=dB))
+
+
 def test_linear16_equals_nf4_staged_bitwise():
     cfg = I.LinearCfg("w16", 300, 256, 320, 16, 1.0, 1.0)
     d = I.linear_inputs(cfg, dense_w=True, seed=5)
