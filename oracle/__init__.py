@@ -12,7 +12,10 @@ Modules
 nf4    : the 4-bit NormalFloat level table, quantizer, packing and the
          bit-exact dequantization contract.
 qlora  : QLoRA linear forward/backward, gated-MLP forward/backward
-         (SwiGLU and tanh-GeGLU), the matmul-chain FLOP counter.
+         (SwiGLU and tanh-GeGLU), q/k/v on one input, the matmul-chain FLOP
+         counter.
+fast_kernels : RMS layernorm, RoPE embeddings and the cross-entropy loss,
+         forward and backward (the pages' other hand-derived kernels).
 
 Sources (the pages this follows):
 - "Unsloth update: Mistral support and performance improvements"
