@@ -323,6 +323,59 @@ int qlora_qkv16_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64
                     int64_t m, const qlora_qkv16_weights* w, uint16_t* dX,
                     const qlora_qkv_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------ RMS layernorm, RoPE, cross entropy --
+ * The pages' other hand-derived training kernels (Mistral benchmark page,
+ * breakdown items 7 "Fast RoPE Embeddings", 8 "Fast RMS Layernorm", 9 "Fast
+ * Cross Entropy Loss"; Gemma page, "+1 to RMS LayerNorm" and "256K
+ * vocabulary"; Reddit talk summary, "chunked cross entropy"). None of them
+ * needs a workspace; every call is asynchronous on `stream`.
+ *
+ * RMS layernorm over rows of X [m][d] (d a multiple of 8):
+ *   r_i = 1 / sqrt(mean_j x_ij^2 + eps);  Y = X * r * w'  with w' = w
+ *   (gemma = 0: Llama, Mistral) or 1 + w (gemma = 1: Gemma); w [d] bf16.
+ *   rstd [m] fp32 receives r for the backward (caller-owned).
+ * Backward for a frozen w (LoRA trains the adapters only), g = dY * w':
+ *   dX = r * (g - X * r^2 * mean_j(g_j x_j)). No gradient of w. */
+int qlora_rmsnorm_fwd(const uint16_t* X, int64_t m, int64_t d, const uint16_t* w, float eps,
+                      int gemma, uint16_t* Y, float* rstd, void* stream);
+int qlora_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const float* rstd, int64_t m,
+                      int64_t d, const uint16_t* w, int gemma, uint16_t* dX, void* stream);
+
+/* RoPE on X [m][heads][head_dim] (row pitch ld in elements, a multiple of 8):
+ * each head vector is split into halves (a, b); with
+ * theta_j = pos[i] * base^(-2j/head_dim), j < head_dim/2,
+ *   Y = (a cos theta - b sin theta, b cos theta + a sin theta).
+ * The backward is the transposed rotation (the angle's sign reversed):
+ *   dX = (da cos + db sin, db cos - da sin).
+ * pos [m] int64 (the token's position in its sequence). Angles are formed in
+ * fp64 and reduced to [-pi, pi] before an fp32 sine and cosine (positions
+ * never pass through bf16). head_dim a multiple of 16, at most 256. Y may be
+ * X (in place, same pitch); Q and K of a fused q/k/v output can be passed
+ * as column slices with its pitch. */
+int qlora_rope_fwd(const uint16_t* X, int64_t ld_x, int64_t m, int64_t heads, int64_t head_dim,
+                   const int64_t* pos, float base, uint16_t* Y, int64_t ld_y, void* stream);
+int qlora_rope_bwd(const uint16_t* dY, int64_t ld_dy, int64_t m, int64_t heads, int64_t head_dim,
+                   const int64_t* pos, float base, uint16_t* dX, int64_t ld_dx, void* stream);
+
+/* Cross entropy of logits [m][V] bf16 (row pitch ld, a multiple of 8, >= V;
+ * any V) against labels [m] int64, where a label outside [0, V) (e.g. -100)
+ * marks a row without a target:
+ *   lse_i = logsumexp(x_i);  ce_i = lse_i - x_i[label_i] (0 without a target);
+ *   loss = sum_i ce_i / n,  n = number of rows with a target (loss 0 if n = 0).
+ * Outputs: lse, ce_rows [m] fp32; loss (fp32) and n_valid (int32) are device
+ * scalars, written with a fixed summation order.
+ * Backward: dlogits = (softmax(x_i) - onehot(label_i)) * dloss / n for rows
+ * with a target, 0 otherwise; dloss is a device fp32 scalar (NULL = 1.0);
+ * n_valid and lse as written by the forward. dlogits may be logits (in place,
+ * same pitch). Errors: QLORA_ESHAPE for sizes, pitches or alignment (bf16
+ * arrays 16-byte aligned), QLORA_EINVAL for NULL pointers. */
+int qlora_cross_entropy_fwd(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                            const int64_t* labels, float* lse, float* ce_rows, float* loss,
+                            int32_t* n_valid, void* stream);
+int qlora_cross_entropy_bwd(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                            const int64_t* labels, const float* lse, const float* dloss,
+                            const int32_t* n_valid, uint16_t* dlogits, int64_t ld_d, void* stream);
+
 /* ---------------------------------------------------------------- tracing --
  * Kernel timing aid for benchmarks and profiling. While enabled, every
  * dense-contraction (base GEMM) launch made by the entry points above is

@@ -138,6 +138,19 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64,
                           ctypes.POINTER(wt), c_vp, ctypes.POINTER(QkvGrads), c_vp,
                           ctypes.c_size_t, c_vp]
+        c_f = ctypes.c_float
+        for name, args in (
+                ("qlora_rmsnorm_fwd", [c_vp, c_i64, c_i64, c_vp, c_f, ctypes.c_int, c_vp, c_vp, c_vp]),
+                ("qlora_rmsnorm_bwd", [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, ctypes.c_int, c_vp, c_vp]),
+                ("qlora_rope_fwd", [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_f, c_vp, c_i64, c_vp]),
+                ("qlora_rope_bwd", [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_f, c_vp, c_i64, c_vp]),
+                ("qlora_cross_entropy_fwd", [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_vp]),
+                ("qlora_cross_entropy_bwd", [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_i64, c_vp])):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = args
         L.qlora_probe_mfma_peak.restype = ctypes.c_int
         L.qlora_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
@@ -166,5 +179,6 @@ EXPORTED = [
     "qlora_linear16_workspace_bytes", "qlora_linear16_fwd", "qlora_linear16_bwd",
     "qlora_mlp16_workspace_bytes", "qlora_mlp16_fwd", "qlora_mlp16_bwd",
     "qlora_qkv_workspace_bytes", "qlora_qkv_fwd", "qlora_qkv_bwd", "qlora_qkv16_fwd",
-    "qlora_qkv16_bwd",
+    "qlora_qkv16_bwd", "qlora_rmsnorm_fwd", "qlora_rmsnorm_bwd", "qlora_rope_fwd", "qlora_rope_bwd",
+    "qlora_cross_entropy_fwd", "qlora_cross_entropy_bwd",
 ]

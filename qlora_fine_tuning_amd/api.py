@@ -537,3 +537,105 @@ def qkv16_fwd(X, w: Qkv16Weights, out=None, ws=None):
 
 def qkv16_bwd(dQ, dK, dV, X, U, w: Qkv16Weights, need_dx=True, ws=None):
     return _qkv_bwd("qlora_qkv16_bwd", dQ, dK, dV, X, U, w, need_dx, ws)
+
+
+# -------------------------------------------- RMS layernorm, RoPE, cross entropy --
+def rmsnorm_fwd(X, w, eps: float, gemma: bool = False):
+    """Returns (Y [m][d] bf16, rstd [m] fp32); Gemma scales by 1 + w."""
+    m, d = X.shape
+    _need(X, "X", torch.bfloat16, (m, d))
+    _need(w, "w", torch.bfloat16, (d,))
+    Y = torch.empty_like(X)
+    rstd = torch.empty((m,), dtype=torch.float32, device=X.device)
+    _lib.check(_lib.lib().qlora_rmsnorm_fwd(_ptr(X), m, d, _ptr(w), float(eps), int(gemma), _ptr(Y),
+                                            _ptr(rstd), _stream()), "qlora_rmsnorm_fwd")
+    return Y, rstd
+
+
+def rmsnorm_bwd(dY, X, rstd, w, gemma: bool = False):
+    """dX [m][d] bf16 of the RMS layernorm (the norm weight is frozen)."""
+    m, d = X.shape
+    _need(dY, "dY", torch.bfloat16, (m, d))
+    _need(X, "X", torch.bfloat16, (m, d))
+    _need(rstd, "rstd", torch.float32, (m,))
+    _need(w, "w", torch.bfloat16, (d,))
+    dX = torch.empty_like(X)
+    _lib.check(_lib.lib().qlora_rmsnorm_bwd(_ptr(dY), _ptr(X), _ptr(rstd), m, d, _ptr(w), int(gemma),
+                                            _ptr(dX), _stream()), "qlora_rmsnorm_bwd")
+    return dX
+
+
+def _heads_view(t, name):
+    """A bf16 [m][heads][head_dim] tensor whose rows may be strided; returns its row pitch."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a bf16 GPU tensor [m][heads][head_dim]")
+    m, h, hd = t.shape
+    if t.stride(2) != 1 or t.stride(1) != hd:
+        raise ValueError(f"{name}: heads must be dense within a row")
+    return t.stride(0) if m > 1 else max(t.stride(0), h * hd)
+
+
+def _rope(fn, X, pos, base, out, inplace):
+    m, heads, hd = X.shape
+    ldx = _heads_view(X, "X")
+    _need(pos, "pos", torch.int64, (m,))
+    Y = X if inplace else (torch.empty_like(X) if out is None else out)
+    ldy = _heads_view(Y, "out")
+    _lib.check(getattr(_lib.lib(), fn)(_ptr(X), ldx, m, heads, hd, _ptr(pos), float(base), _ptr(Y), ldy,
+                                       _stream()), fn)
+    return Y
+
+
+def rope_fwd(X, pos, base: float = 10000.0, out=None, inplace=False):
+    """RoPE of X [m][heads][head_dim] at positions pos [m] (int64)."""
+    return _rope("qlora_rope_fwd", X, pos, base, out, inplace)
+
+
+def rope_bwd(dY, pos, base: float = 10000.0, out=None, inplace=False):
+    """Transposed rotation: dX from dY [m][heads][head_dim]."""
+    return _rope("qlora_rope_bwd", dY, pos, base, out, inplace)
+
+
+def _logit_rows(t, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a bf16 GPU tensor [m][V]")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def cross_entropy_fwd(logits, labels):
+    """Returns dict(loss [1] fp32, n_valid [1] int32, lse [m] fp32, ce [m] fp32); labels
+    int64 [m], a label outside [0, V) (e.g. -100) marks a row without a target."""
+    m, V = logits.shape
+    ld = _logit_rows(logits, "logits")
+    _need(labels, "labels", torch.int64, (m,))
+    dev = logits.device
+    out = dict(loss=torch.empty((1,), dtype=torch.float32, device=dev),
+               n_valid=torch.empty((1,), dtype=torch.int32, device=dev),
+               lse=torch.empty((m,), dtype=torch.float32, device=dev),
+               ce=torch.empty((m,), dtype=torch.float32, device=dev))
+    _lib.check(_lib.lib().qlora_cross_entropy_fwd(_ptr(logits), ld, m, V, _ptr(labels), _ptr(out["lse"]),
+                                                  _ptr(out["ce"]), _ptr(out["loss"]), _ptr(out["n_valid"]),
+                                                  _stream()), "qlora_cross_entropy_fwd")
+    return out
+
+
+def cross_entropy_bwd(logits, labels, fwd, dloss=None, inplace=False):
+    """dlogits [m][V] bf16 of the mean loss; dloss: optional fp32 device scalar."""
+    m, V = logits.shape
+    ld = _logit_rows(logits, "logits")
+    _need(labels, "labels", torch.int64, (m,))
+    _need(fwd["lse"], "lse", torch.float32, (m,))
+    _need(fwd["n_valid"], "n_valid", torch.int32, (1,))
+    if dloss is not None:
+        _need(dloss, "dloss", torch.float32, (1,))
+    if inplace:
+        dX = logits
+    else:   # rows padded to a multiple of 8 elements (16 bytes)
+        dX = torch.empty((m, (V + 7) // 8 * 8), dtype=torch.bfloat16, device=logits.device)[:, :V]
+    ldd = _logit_rows(dX, "dlogits")
+    _lib.check(_lib.lib().qlora_cross_entropy_bwd(_ptr(logits), ld, m, V, _ptr(labels), _ptr(fwd["lse"]),
+                                                  _ptr(dloss), _ptr(fwd["n_valid"]), _ptr(dX), ldd,
+                                                  _stream()), "qlora_cross_entropy_bwd")
+    return dX

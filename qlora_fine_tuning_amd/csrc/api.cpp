@@ -1231,4 +1231,92 @@ int qlora_qkv16_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64
   return qkv_bwd_impl(dy, ld, X, U, m, qkv_src16(w), dX, grads, MODE_BF16, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------- RMS layernorm, RoPE, cross entropy --
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int qlora_rmsnorm_fwd(const uint16_t* X, int64_t m, int64_t d, const uint16_t* w, float eps,
+                      int gemma, uint16_t* Y, float* rstd, void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 33) || d <= 0 || d % 8 || d >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (!w || !std::isfinite(eps) || eps < 0.0f || (gemma != 0 && gemma != 1)) return QLORA_EINVAL;
+  if (m == 0) return QLORA_OK;
+  if (!X || !Y || !rstd) return QLORA_EINVAL;
+  if (!al16(X) || !al16(Y) || !al16(w) || ((uintptr_t)rstd & 3)) return QLORA_ESHAPE;
+  QL_TRY(launch_rmsnorm_fwd(X, m, d, w, eps, gemma, Y, rstd, (hipStream_t)stream), "rmsnorm_fwd");
+  return QLORA_OK;
+}
+
+int qlora_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const float* rstd, int64_t m, int64_t d,
+                      const uint16_t* w, int gemma, uint16_t* dX, void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 33) || d <= 0 || d % 8 || d >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (!w || (gemma != 0 && gemma != 1)) return QLORA_EINVAL;
+  if (m == 0) return QLORA_OK;
+  if (!dY || !X || !rstd || !dX) return QLORA_EINVAL;
+  if (!al16(dY) || !al16(X) || !al16(w) || !al16(dX) || ((uintptr_t)rstd & 3)) return QLORA_ESHAPE;
+  QL_TRY(launch_rmsnorm_bwd(dY, X, rstd, m, d, w, gemma, dX, (hipStream_t)stream), "rmsnorm_bwd");
+  return QLORA_OK;
+}
+
+static int rope_impl(const uint16_t* X, int64_t ldx, int64_t m, int64_t heads, int64_t hd,
+                     const int64_t* pos, float base, uint16_t* Y, int64_t ldy, int backward,
+                     void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 31) || heads < 1 || heads > 4096 || hd < 16 || hd > 256 || hd % 16)
+    return QLORA_ESHAPE;
+  if (!std::isfinite(base) || base <= 0.0f) return QLORA_EINVAL;
+  if (m == 0) return QLORA_OK;
+  if (!X || !Y || !pos) return QLORA_EINVAL;
+  const int64_t width = heads * hd;
+  if (ldx < width || ldy < width || ldx % 8 || ldy % 8 || !al16(X) || !al16(Y)) return QLORA_ESHAPE;
+  if (X == Y && ldx != ldy) return QLORA_EINVAL;   // in place only with the same pitch
+  if (((uintptr_t)pos & 7)) return QLORA_ESHAPE;
+  RopeFreq fr;
+  for (int j = 0; j < 128; ++j) fr.inv_freq[j] = j < hd / 2 ? std::pow((double)base, -2.0 * j / (double)hd) : 0.0;
+  QL_TRY(launch_rope(X, ldx, Y, ldy, m, (int)heads, (int)hd, pos, fr, backward, (hipStream_t)stream),
+         backward ? "rope_bwd" : "rope_fwd");
+  return QLORA_OK;
+}
+
+int qlora_rope_fwd(const uint16_t* X, int64_t ld_x, int64_t m, int64_t heads, int64_t head_dim,
+                   const int64_t* pos, float base, uint16_t* Y, int64_t ld_y, void* stream) {
+  return rope_impl(X, ld_x, m, heads, head_dim, pos, base, Y, ld_y, 0, stream);
+}
+
+int qlora_rope_bwd(const uint16_t* dY, int64_t ld_dy, int64_t m, int64_t heads, int64_t head_dim,
+                   const int64_t* pos, float base, uint16_t* dX, int64_t ld_dx, void* stream) {
+  return rope_impl(dY, ld_dy, m, heads, head_dim, pos, base, dX, ld_dx, 1, stream);
+}
+
+int qlora_cross_entropy_fwd(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                            const int64_t* labels, float* lse, float* ce_rows, float* loss,
+                            int32_t* n_valid, void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 31) || V < 1 || V >= ((int64_t)1 << 40) || ld < V || ld % 8)
+    return QLORA_ESHAPE;
+  if (!loss || !n_valid) return QLORA_EINVAL;
+  if (m > 0 && (!logits || !labels || !lse || !ce_rows)) return QLORA_EINVAL;
+  if (m > 0 && (!al16(logits) || ((uintptr_t)labels & 7) || ((uintptr_t)lse & 3) ||
+                ((uintptr_t)ce_rows & 3)))
+    return QLORA_ESHAPE;
+  if (((uintptr_t)loss & 3) || ((uintptr_t)n_valid & 3)) return QLORA_ESHAPE;
+  QL_TRY(launch_xent_fwd(logits, ld, m, V, labels, lse, ce_rows, loss, n_valid, (hipStream_t)stream),
+         "cross_entropy_fwd");
+  return QLORA_OK;
+}
+
+int qlora_cross_entropy_bwd(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                            const int64_t* labels, const float* lse, const float* dloss,
+                            const int32_t* n_valid, uint16_t* dlogits, int64_t ld_d, void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 31) || V < 1 || V >= ((int64_t)1 << 40) || ld < V || ld % 8 ||
+      ld_d < V || ld_d % 8)
+    return QLORA_ESHAPE;
+  if (m == 0) return QLORA_OK;
+  if (!logits || !labels || !lse || !n_valid || !dlogits) return QLORA_EINVAL;
+  if (logits == dlogits && ld != ld_d) return QLORA_EINVAL;   // in place only with the same pitch
+  if (!al16(logits) || !al16(dlogits) || ((uintptr_t)labels & 7) || ((uintptr_t)lse & 3) ||
+      ((uintptr_t)n_valid & 3) || ((uintptr_t)dloss & 3))
+    return QLORA_ESHAPE;
+  QL_TRY(launch_xent_bwd(logits, ld, m, V, labels, lse, dloss, n_valid, dlogits, ld_d,
+                         (hipStream_t)stream),
+         "cross_entropy_bwd");
+  return QLORA_OK;
+}
+
 }  // extern "C"

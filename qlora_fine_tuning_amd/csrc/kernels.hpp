@@ -152,6 +152,32 @@ struct PrepJobs {
 hipError_t launch_prep(const PrepJobs& jobs, hipStream_t stream);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t stream);
 
+// ---- RMS layernorm, RoPE, cross entropy (fast.hip) ----
+// rmsnorm: X, Y, dY, dX [m][d] bf16 (d % 8 == 0), w [d] bf16; gemma: scale
+// by 1 + w instead of w; rstd [m] fp32 = 1/rms (forward output, backward input)
+hipError_t launch_rmsnorm_fwd(const uint16_t* X, int64_t m, int64_t d, const uint16_t* w, float eps,
+                              int gemma, uint16_t* Y, float* rstd, hipStream_t stream);
+hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const float* rstd, int64_t m,
+                              int64_t d, const uint16_t* w, int gemma, uint16_t* dX,
+                              hipStream_t stream);
+// RoPE on X [m][heads][hd] (row pitch ldx), half-split pairs (j, j + hd/2);
+// inv_freq[j] = base^(-2j/hd) in fp64 (hd % 16 == 0, hd <= 256); backward
+// rotates by the opposite angle. Y may be X (same pitch).
+struct RopeFreq {
+  double inv_freq[128];
+};
+hipError_t launch_rope(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t ldy, int64_t m, int heads,
+                       int hd, const int64_t* pos, const RopeFreq& fr, int backward,
+                       hipStream_t stream);
+// cross entropy over logits X [m][V] (row pitch ld, a multiple of 8); labels
+// int64 [m] (outside [0, V): no target). Forward: lse, ce [m] fp32, loss and
+// n_valid (device scalars). Backward: dX [m][V] (pitch ldd), may be X.
+hipError_t launch_xent_fwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
+                           float* lse, float* ce, float* loss, int32_t* n_valid, hipStream_t stream);
+hipError_t launch_xent_bwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
+                           const float* lse, const float* dloss, const int32_t* n_valid, uint16_t* dX,
+                           int64_t ldd, hipStream_t stream);
+
 // ---- diagnostics (probe.hip) ----
 // Sustained dense bf16 MFMA TFLOP/s and the shader clock (GHz) under that
 // load; synchronizes the host.

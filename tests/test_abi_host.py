@@ -205,3 +205,25 @@ def test_qkv_validation_errors(L):
     w16 = _lib.Qkv16Weights(FAKE, None, FAKE, 128, 128, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             8, 1.0)
     assert L.qlora_qkv16_fwd(*(lambda a: (a[0], a[1], ctypes.byref(w16)) + a[3:])(args())) == -1
+
+
+def test_norm_rope_xent_validation_errors(L):
+    F_ = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    f = ctypes.c_float
+    assert L.qlora_rmsnorm_fwd(F_, 4, 100, F_, f(1e-6), 0, F_, F_, None) == -2      # d % 8
+    assert L.qlora_rmsnorm_fwd(F_, 4, 64, None, f(1e-6), 0, F_, F_, None) == -1     # no weight
+    assert L.qlora_rmsnorm_fwd(F_, 4, 64, F_, f(-1.0), 0, F_, F_, None) == -1       # eps < 0
+    assert L.qlora_rmsnorm_fwd(F_, 4, 64, F_, f(1e-6), 2, F_, F_, None) == -1       # flag
+    assert L.qlora_rmsnorm_fwd(None, 0, 64, F_, f(1e-6), 0, None, None, None) == 0  # empty
+    assert L.qlora_rmsnorm_bwd(F_, F_, None, 4, 64, F_, 0, F_, None) == -1          # no rstd
+    assert L.qlora_rope_fwd(F_, 256, 4, 2, 24, F_, f(1e4), F_, 256, None) == -2     # hd % 16
+    assert L.qlora_rope_fwd(F_, 256, 4, 2, 512, F_, f(1e4), F_, 1024, None) == -2   # hd > 256
+    assert L.qlora_rope_fwd(F_, 200, 4, 2, 128, F_, f(1e4), F_, 256, None) == -2    # pitch < width
+    assert L.qlora_rope_fwd(F_, 256, 4, 2, 128, F_, f(0.0), F_, 256, None) == -1    # base
+    assert L.qlora_rope_fwd(F_, 256, 4, 2, 128, F_, f(1e4), F_, 264, None) == -1    # in place, pitches differ
+    assert L.qlora_rope_bwd(F_, 256, 4, 2, 128, None, f(1e4), F_, 256, None) == -1  # no positions
+    assert L.qlora_cross_entropy_fwd(F_, 100, 4, 100, F_, F_, F_, F_, F_, None) == -2   # pitch % 8
+    assert L.qlora_cross_entropy_fwd(F_, 96, 4, 100, F_, F_, F_, F_, F_, None) == -2    # pitch < V
+    assert L.qlora_cross_entropy_fwd(F_, 104, 4, 100, F_, F_, F_, None, F_, None) == -1  # no loss
+    assert L.qlora_cross_entropy_bwd(F_, 104, 4, 100, F_, F_, None, None, F_, 104, None) == -1
+    assert L.qlora_cross_entropy_bwd(F_, 104, 4, 100, F_, F_, None, F_, F_, 112, None) == -1  # in place
