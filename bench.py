@@ -34,6 +34,7 @@ METRIC_QKV = "QLoRA q/k/v fwd+bwd TFLOP/s + % bf16 MFMA peak, {model} shape, 819
 MLP_WORKLOADS = ["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"]
 QKV_WORKLOADS = ["mistral7b_qkv", "llama7b_qkv"]
 QUANT_WORKLOAD = "llama7b_mlp_quantize"
+FAST_WORKLOADS = ["llama7b_norm_rope_xent", "gemma7b_norm_rope_xent"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 QUANT_BYTES_PER_WEIGHT = 2 + 0.5 + 4 / 64   # bf16 in; codes + fp32 absmax out
 
@@ -44,7 +45,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama7b_mlp",
-                   choices=MLP_WORKLOADS + QKV_WORKLOADS + [QUANT_WORKLOAD])
+                   choices=MLP_WORKLOADS + QKV_WORKLOADS + [QUANT_WORKLOAD] + FAST_WORKLOADS)
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--base", default="nf4", choices=["nf4", "bf16"],
                    help="base weights: NF4 (QLoRA, default) or bf16 (16-bit LoRA variant)")
@@ -221,6 +222,123 @@ def bench_quantize(a):
     print(json.dumps(out), flush=True)
 
 
+def bench_fast(a):
+    """RMS layernorm, RoPE (q and k) and cross entropy, forward + backward, at one
+    model's sizes and 8192 tokens (4 x 2048). HBM-bound: value = algorithmic
+    bytes (every operand read once, every output written once) / step time."""
+    import numpy as np
+    import torch
+
+    import qlora_fine_tuning_amd as Q
+    from qlora_fine_tuning_amd import inputs as I
+
+    dev = "cuda:0"
+    llama = a.workload == "llama7b_norm_rope_xent"
+    m = 8192
+    d, hq, hk, hd, V, eps, gemma = ((4096, 32, 32, 128, 32000, 1e-6, False) if llama
+                                    else (3072, 16, 16, 256, 256000, 1e-6, True))
+    X = I.normal_bf16("X", (m, d), 1.0).to(dev)
+    w = (I.normal_bf16("W", (d,), 0.1) + (0 if gemma else 1)).to(torch.bfloat16).to(dev)
+    dY = I.normal_bf16("dY", (m, d), 1.0).to(dev)
+    q = I.normal_bf16("Wk", (m, hq, hd), 1.0).to(dev)
+    k = I.normal_bf16("Wv", (m, hk, hd), 1.0).to(dev)
+    pos = (torch.arange(m, dtype=torch.int64) % 2048).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(I.SEED)   # seeded device draw: the Gemma logits are 2.1e9 values
+    logits = (torch.randn((m, V), generator=gen, device=dev) * 2.0).to(torch.bfloat16)
+    g = np.random.default_rng(I.SEED)
+    lab_np = g.integers(0, V, size=m).astype(np.int64)
+    lab_np[::2048] = -100                                   # no target after each sequence's last token
+    labels = torch.from_numpy(lab_np).to(dev)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    e = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    parts = ["rmsnorm_fwd", "rmsnorm_bwd", "rope_fwd", "rope_bwd", "xent_fwd", "xent_bwd"]
+    nq, nk = m * hq * hd, m * hk * hd
+    alg = {"rmsnorm_fwd": 4 * m * d + 4 * m + 2 * d, "rmsnorm_bwd": 6 * m * d + 4 * m + 2 * d,
+           "rope_fwd": 4 * (nq + nk) + 8 * m, "rope_bwd": 4 * (nq + nk) + 8 * m,
+           "xent_fwd": 2 * m * V + 16 * m, "xent_bwd": 4 * m * V + 16 * m}
+
+    def step(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record()
+        mark(0)
+        Y, rstd = Q.rmsnorm_fwd(X, w, eps, gemma)
+        mark(1)
+        Q.rmsnorm_bwd(dY, X, rstd, w, gemma)
+        mark(2)
+        Q.rope_fwd(q, pos, out=qo)
+        Q.rope_fwd(k, pos, out=ko)
+        mark(3)
+        Q.rope_bwd(qo, pos, out=qo, inplace=True)
+        Q.rope_bwd(ko, pos, out=ko, inplace=True)
+        mark(4)
+        f = Q.cross_entropy_fwd(logits, labels)
+        mark(5)
+        Q.cross_entropy_bwd(logits, labels, f)
+        mark(6)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = e(), e()
+    ev0.record()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / a.steps
+    per = {p_: 0.0 for p_ in parts}
+    for _ in range(3):   # per-kernel breakdown, separate from the timed steps
+        evs = [e() for _ in range(7)]
+        step(evs)
+        torch.cuda.synchronize()
+        for i, p_ in enumerate(parts):
+            per[p_] += evs[i].elapsed_time(evs[i + 1]) / 3
+    total = sum(alg.values())
+    gbs = total / (ms / 1e3) / 1e9
+    dom = "xent_bwd"
+    dom_gbs = alg[dom] / (per[dom] / 1e3) / 1e9
+    out = {
+        "metric": f"RMS layernorm + RoPE + cross entropy fwd+bwd GB/s, {'Llama' if llama else 'Gemma'}-7B sizes, 8192 tok",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 arithmetic)", "data": "synthetic",
+        "config": {"workload": a.workload, "tokens": m, "d": d, "q_heads": hq, "k_heads": hk,
+                   "head_dim": hd, "vocab": V, "norm": "1+w" if gemma else "w", "global_batch": m,
+                   "parallelism": "none (1 GPU)"},
+        "wall_s_timed": round(wall, 3),
+        "kernels": {p_: {"us": round(per[p_] * 1e3, 1),
+                         "GB/s": round(alg[p_] / (per[p_] / 1e3) / 1e9, 1)} for p_ in parts},
+        "roofline": {"bound": "hbm", "kernel": "xent_bwd_kernel", "achieved": round(dom_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": alg[dom],
+                     "avg_launch_ms": round(per[dom], 4)},
+    }
+    if a.cpu_tokens > 0:   # the oracle on a bounded sample of rows
+        from oracle import fast_kernels as F
+        rows = 512
+        t0 = time.perf_counter()
+        x64 = X[:rows].float().cpu().double().numpy()
+        Yr, r = F.rms_layernorm_fwd(x64, w.float().cpu().double().numpy(), eps, gemma)
+        F.rms_layernorm_bwd(dY[:rows].float().cpu().double().numpy(), x64, r, w.float().cpu().double().numpy(), gemma)
+        p_np = pos[:rows].cpu().numpy()
+        for t in (q, k):
+            t64 = t[:rows].float().cpu().double().numpy()
+            F.rope_bwd(F.rope_fwd(t64, p_np, 10000.0), p_np, 10000.0)
+        l64 = logits[:rows].float().cpu().double().numpy()
+        loss, ce, lse, n = F.cross_entropy_fwd(l64, lab_np[:rows])
+        F.cross_entropy_bwd(l64, lab_np[:rows], lse, n)
+        t = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(total * rows / m / t / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {m} tokens, fp64 numpy (device-to-host copies included)",
+                               "seconds": round(t, 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -233,6 +351,9 @@ def main():
 
     if a.workload == QUANT_WORKLOAD:
         bench_quantize(a)
+        return
+    if a.workload in FAST_WORKLOADS:
+        bench_fast(a)
         return
 
     import torch

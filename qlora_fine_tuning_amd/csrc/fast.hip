@@ -4,9 +4,10 @@
 // "256K vocabulary"). All three are HBM-bound: each reads its operands once
 // with 16-byte loads and does its arithmetic in fp32.
 //
-//  rmsnorm : one wave per row. Pass 1 sums x^2 (bwd: (dy * w') * x), a wave
-//            reduction finishes it; pass 2 re-reads the row, which is still in
-//            cache, and writes y (bwd: dx). Forward saves r = 1/rms in fp32.
+//  rmsnorm : one wave per row. The row is loaded into registers at once (rows
+//            up to 8192; longer rows re-read it from cache in a second pass),
+//            x^2 (bwd: (dy * w') * x) is summed by a wave reduction, then y
+//            (bwd: dx) is written. Forward saves r = 1/rms in fp32.
 //  rope    : a thread takes 8 angle pairs (j, j + hd/2) of one token and up to
 //            8 heads, so each sine/cosine serves every head it covers. Angles
 //            are pos * base^(-2j/hd) in fp64, reduced to [-pi, pi] in fp64,
@@ -49,6 +50,14 @@ __device__ __forceinline__ u32x4_t pack8(const float* f) {
 }  // namespace
 
 // ------------------------------------------------------------ RMS layernorm --
+// Rows of up to RN_MAX * 512 elements stay in registers: every load of the
+// row is issued at once and the row is read once. Longer rows take a loop
+// that re-reads the row (from cache) in the second pass.
+constexpr int RN_MAX = 16;   // 16-byte chunks per lane, at most
+
+// NCH > 0: the row is register-resident as NCH chunks per lane (d <= NCH * 512);
+// NCH == 0: the looping form for any d.
+template <int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ X, int64_t m,
                                                           int64_t d, const uint16_t* __restrict__ w,
                                                           float eps, int gemma,
@@ -59,27 +68,60 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __rest
   if (row >= m) return;   // whole wave leaves together
   const uint16_t* x = X + row * d;
   const int64_t nc = d / 8;
-  float ss = 0.0f;
-  for (int64_t c = lane; c < nc; c += 64) {
-    float f[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
   const float wo = gemma ? 1.0f : 0.0f;
-  for (int64_t c = lane; c < nc; c += 64) {
-    float f[8], g[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
-    unpack8(*(const u32x4_t*)(w + c * 8), g);
+  float ss = 0.0f;
+  if constexpr (NCH > 0) {
+    u32x4_t v[NCH];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = f[e] * r * (g[e] + wo);
-    *(u32x4_t*)(Y + row * d + c * 8) = pack8(f);
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nc) v[i] = *(const u32x4_t*)(x + (lane + 64 * i) * 8);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nc) {
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+      }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = lane + 64 * i;
+      if (c < nc) {
+        float f[8], g[8];
+        unpack8(v[i], f);
+        unpack8(*(const u32x4_t*)(w + c * 8), g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * r * (g[e] + wo);
+        *(u32x4_t*)(Y + row * d + c * 8) = pack8(f);
+      }
+    }
+    if (lane == 0) rstd[row] = r;
+  } else {
+#pragma unroll 4
+    for (int64_t c = lane; c < nc; c += 64) {
+      float f[8];
+      unpack8(*(const u32x4_t*)(x + c * 8), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll 4
+    for (int64_t c = lane; c < nc; c += 64) {
+      float f[8], g[8];
+      unpack8(*(const u32x4_t*)(x + c * 8), f);
+      unpack8(*(const u32x4_t*)(w + c * 8), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] * r * (g[e] + wo);
+      *(u32x4_t*)(Y + row * d + c * 8) = pack8(f);
+    }
+    if (lane == 0) rstd[row] = r;
   }
-  if (lane == 0 && rstd) rstd[row] = r;
 }
 
+template <int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ dY,
                                                           const uint16_t* __restrict__ X,
                                                           const float* __restrict__ rstd, int64_t m,
@@ -92,34 +134,76 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
   const uint16_t* dy = dY + row * d;
   const int64_t nc = d / 8;
   const float wo = gemma ? 1.0f : 0.0f;
-  float dot = 0.0f;
-  for (int64_t c = lane; c < nc; c += 64) {
-    float f[8], g[8], ww[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
-    unpack8(*(const u32x4_t*)(dy + c * 8), g);
-    unpack8(*(const u32x4_t*)(w + c * 8), ww);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dot += g[e] * (ww[e] + wo) * f[e];
-  }
-  dot = wave_sum(dot);
   const float r = rstd[row];
-  const float k = r * r * dot / (float)d;
-  for (int64_t c = lane; c < nc; c += 64) {
-    float f[8], g[8], ww[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
-    unpack8(*(const u32x4_t*)(dy + c * 8), g);
-    unpack8(*(const u32x4_t*)(w + c * 8), ww);
+  float dot = 0.0f;
+  if constexpr (NCH > 0) {
+    u32x4_t vx[NCH], vg[NCH];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = r * (g[e] * (ww[e] + wo) - f[e] * k);
-    *(u32x4_t*)(dX + row * d + c * 8) = pack8(f);
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nc) {
+        vx[i] = *(const u32x4_t*)(x + (lane + 64 * i) * 8);
+        vg[i] = *(const u32x4_t*)(dy + (lane + 64 * i) * 8);
+      }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nc) {
+        float f[8], g[8], ww[8];
+        unpack8(vx[i], f);
+        unpack8(vg[i], g);
+        unpack8(*(const u32x4_t*)(w + (lane + 64 * i) * 8), ww);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += g[e] * (ww[e] + wo) * f[e];
+      }
+    dot = wave_sum(dot);
+    const float k = r * r * dot / (float)d;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = lane + 64 * i;
+      if (c < nc) {
+        float f[8], g[8], ww[8];
+        unpack8(vx[i], f);
+        unpack8(vg[i], g);
+        unpack8(*(const u32x4_t*)(w + c * 8), ww);   // w is small and cached
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = r * (g[e] * (ww[e] + wo) - f[e] * k);
+        *(u32x4_t*)(dX + row * d + c * 8) = pack8(f);
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int64_t c = lane; c < nc; c += 64) {
+      float f[8], g[8], ww[8];
+      unpack8(*(const u32x4_t*)(x + c * 8), f);
+      unpack8(*(const u32x4_t*)(dy + c * 8), g);
+      unpack8(*(const u32x4_t*)(w + c * 8), ww);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += g[e] * (ww[e] + wo) * f[e];
+    }
+    dot = wave_sum(dot);
+    const float k = r * r * dot / (float)d;
+#pragma unroll 4
+    for (int64_t c = lane; c < nc; c += 64) {
+      float f[8], g[8], ww[8];
+      unpack8(*(const u32x4_t*)(x + c * 8), f);
+      unpack8(*(const u32x4_t*)(dy + c * 8), g);
+      unpack8(*(const u32x4_t*)(w + c * 8), ww);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = r * (g[e] * (ww[e] + wo) - f[e] * k);
+      *(u32x4_t*)(dX + row * d + c * 8) = pack8(f);
+    }
   }
 }
 
 hipError_t launch_rmsnorm_fwd(const uint16_t* X, int64_t m, int64_t d, const uint16_t* w, float eps,
                               int gemma, uint16_t* Y, float* rstd, hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  rmsnorm_fwd_kernel<<<dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream>>>(X, m, d, w, eps, gemma,
-                                                                               Y, rstd);
+  const dim3 grid((unsigned)((m + 3) / 4));
+  if (d <= 8 * 512)
+    rmsnorm_fwd_kernel<8><<<grid, dim3(256), 0, stream>>>(X, m, d, w, eps, gemma, Y, rstd);
+  else if (d <= RN_MAX * 512)
+    rmsnorm_fwd_kernel<RN_MAX><<<grid, dim3(256), 0, stream>>>(X, m, d, w, eps, gemma, Y, rstd);
+  else
+    rmsnorm_fwd_kernel<0><<<grid, dim3(256), 0, stream>>>(X, m, d, w, eps, gemma, Y, rstd);
   return hipGetLastError();
 }
 
@@ -127,8 +211,13 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const float
                               int64_t d, const uint16_t* w, int gemma, uint16_t* dX,
                               hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  rmsnorm_bwd_kernel<<<dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream>>>(dY, X, rstd, m, d, w,
-                                                                               gemma, dX);
+  const dim3 grid((unsigned)((m + 3) / 4));
+  if (d <= 8 * 512)
+    rmsnorm_bwd_kernel<8><<<grid, dim3(256), 0, stream>>>(dY, X, rstd, m, d, w, gemma, dX);
+  else if (d <= RN_MAX * 512)
+    rmsnorm_bwd_kernel<RN_MAX><<<grid, dim3(256), 0, stream>>>(dY, X, rstd, m, d, w, gemma, dX);
+  else
+    rmsnorm_bwd_kernel<0><<<grid, dim3(256), 0, stream>>>(dY, X, rstd, m, d, w, gemma, dX);
   return hipGetLastError();
 }
 
@@ -161,20 +250,33 @@ __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* X, int64_t ld
     s[i] *= sign;
   }
   const int half = hd / 2;
-  const int hend = min(heads, hb + ROPE_HEADS_PER_THREAD);
-  for (int h = hb; h < hend; ++h) {
-    const uint16_t* xs = X + t * ldx + (int64_t)h * hd + q * 8;
-    float a[8], b[8], ya[8], yb[8];
-    unpack8(*(const u32x4_t*)xs, a);
-    unpack8(*(const u32x4_t*)(xs + half), b);
+  const int nh = min(heads - hb, ROPE_HEADS_PER_THREAD);
+  // all loads first: X and Y may be one buffer, so the compiler could not
+  // move a later head's loads above an earlier head's stores by itself
+  u32x4_t va[ROPE_HEADS_PER_THREAD], vb[ROPE_HEADS_PER_THREAD];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ya[i] = a[i] * c[i] - b[i] * s[i];
-      yb[i] = b[i] * c[i] + a[i] * s[i];
+  for (int i = 0; i < ROPE_HEADS_PER_THREAD; ++i) {
+    if (i < nh) {
+      const uint16_t* xs = X + t * ldx + (int64_t)(hb + i) * hd + q * 8;
+      va[i] = *(const u32x4_t*)xs;
+      vb[i] = *(const u32x4_t*)(xs + half);
     }
-    uint16_t* ys = Y + t * ldy + (int64_t)h * hd + q * 8;
-    *(u32x4_t*)ys = pack8(ya);
-    *(u32x4_t*)(ys + half) = pack8(yb);
+  }
+#pragma unroll
+  for (int i = 0; i < ROPE_HEADS_PER_THREAD; ++i) {
+    if (i < nh) {
+      float a[8], b[8], ya[8], yb[8];
+      unpack8(va[i], a);
+      unpack8(vb[i], b);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ya[k] = a[k] * c[k] - b[k] * s[k];
+        yb[k] = b[k] * c[k] + a[k] * s[k];
+      }
+      uint16_t* ys = Y + t * ldy + (int64_t)(hb + i) * hd + q * 8;
+      *(u32x4_t*)ys = pack8(ya);
+      *(u32x4_t*)(ys + half) = pack8(yb);
+    }
   }
 }
 
@@ -194,13 +296,23 @@ namespace {
 
 constexpr int XENT_THREADS = 256;
 
-// online (max, sum of exp(x - max)) of one value folded into (mx, sm)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// 2^x by the hardware instruction (v_exp_f32, about 1 ulp; results below the
+// normal range flush to 0, which a sum of exponentials cannot resolve anyway).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The running state is kept in base 2: mx is the maximum of x * log2(e) and
+// sm the sum of 2^(x log2(e) - mx), so each exponential is one fused
+// multiply-add and one v_exp_f32. (mx, sm) <- merge with (m2, s2); either
+// side may be empty (max -inf, sum 0).
 __device__ __forceinline__ void lse_merge(float& mx, float& sm, float m2, float s2) {
   if (m2 > mx) {
-    sm = sm * __expf(mx - m2) + s2;
+    sm = sm * exp2_hw(mx - m2) + s2;
     mx = m2;
   } else if (m2 > -INFINITY) {
-    sm += s2 * __expf(m2 - mx);
+    sm += s2 * exp2_hw(m2 - mx);
   }
 }
 
@@ -237,22 +349,35 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fwd_kernel(const uint16_t* 
   const uint16_t* x = X + row * ld;
   const int64_t nc = V / 8;
   float mx = -INFINITY, sm = 0.0f;
-  for (int64_t c = threadIdx.x; c < nc; c += XENT_THREADS) {
+  // fold 8 finite values: rescale the running sum to the new maximum (no
+  // branch; 2^(-inf) = 0 covers the empty start), then add their exponentials
+  auto fold = [&](const u32x4_t& v) {
     float f[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
+    unpack8(v, f);
     float cm = f[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
-    float cs = 0.0f;
+    const float mn = fmaxf(mx, cm * LOG2E);
+    float cs = sm * exp2_hw(mx - mn);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cs += __expf(f[e] - cm);
-    lse_merge(mx, sm, cm, cs);
+    for (int e = 0; e < 8; ++e) cs += exp2_hw(fmaf(f[e], LOG2E, -mn));
+    mx = mn;
+    sm = cs;
+  };
+  int64_t c = threadIdx.x;
+  for (; c + 3 * XENT_THREADS < nc; c += 4 * XENT_THREADS) {   // 4 loads in flight
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold(v[u]);
   }
+  for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)   // tail of V % 8
-    lse_merge(mx, sm, bf16_to_f32(x[j]), 1.0f);
+    lse_merge(mx, sm, bf16_to_f32(x[j]) * LOG2E, 1.0f);
   block_lse(mx, sm);
   if (threadIdx.x == 0) {
-    const float lse = mx + __logf(sm);
+    const float lse = (mx + __log2f(sm)) * LN2;
     const int64_t lab = labels[row];
     lse_out[row] = lse;
     ce_out[row] = (lab >= 0 && lab < V) ? lse - bf16_to_f32(x[lab]) : 0.0f;
@@ -260,28 +385,30 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fwd_kernel(const uint16_t* 
 }
 
 // loss = sum of CE over rows with a target / their number (0 when there are
-// none); fixed summation order: thread t takes rows t, t + 256, ...; then a
-// tree over the 256 partial sums.
-__global__ __launch_bounds__(256) void xent_mean_kernel(const float* __restrict__ ce,
-                                                        const int64_t* __restrict__ labels,
-                                                        int64_t m, int64_t V,
-                                                        float* __restrict__ loss,
-                                                        int32_t* __restrict__ n_valid) {
-  __shared__ double ps[256];
-  __shared__ int pn[256];
+// none). One workgroup of 1024 threads; fixed summation order: thread t adds
+// rows t, t + 1024, ... in order (fp64), then a tree over the 1024 partials.
+__global__ __launch_bounds__(1024) void xent_mean_kernel(const float* __restrict__ ce,
+                                                         const int64_t* __restrict__ labels,
+                                                         int64_t m, int64_t V,
+                                                         float* __restrict__ loss,
+                                                         int32_t* __restrict__ n_valid) {
+  __shared__ double ps[1024];
+  __shared__ int pn[1024];
   double s = 0.0;
   int n = 0;
-  for (int64_t i = threadIdx.x; i < m; i += 256) {
+#pragma unroll 8
+  for (int64_t i = threadIdx.x; i < m; i += 1024) {
     const int64_t lab = labels[i];
+    const float c = ce[i];
     if (lab >= 0 && lab < V) {
-      s += (double)ce[i];
+      s += (double)c;
       ++n;
     }
   }
   ps[threadIdx.x] = s;
   pn[threadIdx.x] = n;
   __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
+  for (int o = 512; o >= 1; o >>= 1) {
     if ((int)threadIdx.x < o) {
       ps[threadIdx.x] += ps[threadIdx.x + o];
       pn[threadIdx.x] += pn[threadIdx.x + o];
@@ -309,22 +436,23 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_bwd_kernel(const uint16_t* 
   const int n = *n_valid;
   const bool on = lab >= 0 && lab < V && n > 0;
   const float scale = on ? (dloss ? *dloss : 1.0f) / (float)n : 0.0f;
-  const float lse = lse_in[row];
+  const float l2 = lse_in[row] * LOG2E;
   const uint16_t* x = X + row * ld;
   uint16_t* dx = dX + row * ldd;
   const int64_t nc = V / 8;
+  #pragma unroll 4
   for (int64_t c = threadIdx.x; c < nc; c += XENT_THREADS) {
     float f[8];
     unpack8(*(const u32x4_t*)(x + c * 8), f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = on ? __expf(f[e] - lse) : 0.0f;
+      const float p = on ? exp2_hw(fmaf(f[e], LOG2E, -l2)) : 0.0f;
       f[e] = (p - (c * 8 + e == lab ? 1.0f : 0.0f)) * scale;
     }
     *(u32x4_t*)(dx + c * 8) = pack8(f);
   }
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS) {
-    const float p = on ? __expf(bf16_to_f32(x[j]) - lse) : 0.0f;
+    const float p = on ? exp2_hw(fmaf(bf16_to_f32(x[j]), LOG2E, -l2)) : 0.0f;
     dx[j] = (uint16_t)f32_to_bf16((p - (j == lab ? 1.0f : 0.0f)) * scale);
   }
 }
@@ -336,7 +464,7 @@ hipError_t launch_xent_fwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  xent_mean_kernel<<<dim3(1), dim3(256), 0, stream>>>(ce, labels, m, V, loss, n_valid);
+  xent_mean_kernel<<<dim3(1), dim3(1024), 0, stream>>>(ce, labels, m, V, loss, n_valid);
   return hipGetLastError();
 }
 

@@ -39,7 +39,8 @@ def _check(name, got, ref, tol=TOL):
 # ----------------------------------------------------------- RMS layernorm --
 @pytest.mark.parametrize("m,d,gemma,eps", [(37, 264, False, 1e-6), (37, 264, True, 1e-6),
                                            (1, 8, False, 1e-5), (300, 4096, False, 1e-5),
-                                           (64, 3072, True, 1e-6), (8192, 4096, False, 1e-6)])
+                                           (64, 3072, True, 1e-6), (8192, 4096, False, 1e-6),
+                                           (16, 6152, False, 1e-6), (8, 12296, True, 1e-5)])
 def test_rmsnorm(m, d, gemma, eps):
     X = I.normal_bf16("X", (m, d), 1.0, seed=m + d)
     w = I.normal_bf16("W", (d,), 0.1 if gemma else 0.3, seed=d) + (0 if gemma else 1)
