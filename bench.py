@@ -297,6 +297,17 @@ def bench_fast(a):
         torch.cuda.synchronize()
         for i, p_ in enumerate(parts):
             per[p_] += evs[i].elapsed_time(evs[i + 1]) / 3
+    # the fused cross-entropy forward + backward, timed on its own
+    xf = [e(), e()]
+    for _ in range(2):
+        Q.cross_entropy_fused(logits, labels)
+    xf[0].record()
+    for _ in range(5):
+        Q.cross_entropy_fused(logits, labels)
+    xf[1].record()
+    torch.cuda.synchronize()
+    fused_ms = xf[0].elapsed_time(xf[1]) / 5
+    fused_alg = 4 * m * V + 16 * m
     total = sum(alg.values())
     gbs = total / (ms / 1e3) / 1e9
     dom = "xent_bwd"
@@ -312,6 +323,9 @@ def bench_fast(a):
         "wall_s_timed": round(wall, 3),
         "kernels": {p_: {"us": round(per[p_] * 1e3, 1),
                          "GB/s": round(alg[p_] / (per[p_] / 1e3) / 1e9, 1)} for p_ in parts},
+        "xent_fused": {"us": round(fused_ms * 1e3, 1),
+                       "GB/s": round(fused_alg / (fused_ms / 1e3) / 1e9, 1),
+                       "vs_fwd_plus_bwd": round((per["xent_fwd"] + per["xent_bwd"]) / fused_ms, 3)},
         "roofline": {"bound": "hbm", "kernel": "xent_bwd_kernel", "achieved": round(dom_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
                      "traffic": None, "algorithmic_bytes": alg[dom],

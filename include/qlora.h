@@ -376,6 +376,18 @@ int qlora_cross_entropy_bwd(const uint16_t* logits, int64_t ld, int64_t m, int64
                             const int64_t* labels, const float* lse, const float* dloss,
                             const int32_t* n_valid, uint16_t* dlogits, int64_t ld_d, void* stream);
 
+/* Forward and backward in one call, for when the upstream gradient of the
+ * loss is known before the loss itself (training: 1, or a loss scale): the
+ * outputs of qlora_cross_entropy_fwd plus dlogits for dloss given as a host
+ * float, with the same bits as the two separate calls. Each row of logits is
+ * read from HBM once (the gradient pass re-reads it from cache), 2 B per
+ * logit instead of 4 over the pair. dlogits may be logits (in place, same
+ * pitch). Errors as for the separate calls; dloss must be finite. */
+int qlora_cross_entropy_fused(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                              const int64_t* labels, float dloss, float* lse, float* ce_rows,
+                              float* loss, int32_t* n_valid, uint16_t* dlogits, int64_t ld_d,
+                              void* stream);
+
 /* ---------------------------------------------------------------- tracing --
  * Kernel timing aid for benchmarks and profiling. While enabled, every
  * dense-contraction (base GEMM) launch made by the entry points above is

@@ -14,7 +14,7 @@ __all__ = [
     "Mlp16Weights", "mlp16_workspace_bytes", "mlp16_fwd", "mlp16_bwd",
     "QkvWeights", "Qkv16Weights", "qkv_workspace_bytes", "qkv_fwd", "qkv_bwd", "qkv16_fwd",
     "qkv16_bwd", "rmsnorm_fwd", "rmsnorm_bwd", "rope_fwd", "rope_bwd", "cross_entropy_fwd",
-    "cross_entropy_bwd",
+    "cross_entropy_bwd", "cross_entropy_fused",
 ]
 
 

@@ -147,7 +147,9 @@ def lib() -> ctypes.CDLL:
                 ("qlora_cross_entropy_fwd", [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                              c_vp]),
                 ("qlora_cross_entropy_bwd", [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                             c_i64, c_vp])):
+                                             c_i64, c_vp]),
+                ("qlora_cross_entropy_fused", [c_vp, c_i64, c_i64, c_i64, c_vp, c_f, c_vp, c_vp, c_vp,
+                                               c_vp, c_vp, c_i64, c_vp])):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = args
@@ -180,5 +182,5 @@ EXPORTED = [
     "qlora_mlp16_workspace_bytes", "qlora_mlp16_fwd", "qlora_mlp16_bwd",
     "qlora_qkv_workspace_bytes", "qlora_qkv_fwd", "qlora_qkv_bwd", "qlora_qkv16_fwd",
     "qlora_qkv16_bwd", "qlora_rmsnorm_fwd", "qlora_rmsnorm_bwd", "qlora_rope_fwd", "qlora_rope_bwd",
-    "qlora_cross_entropy_fwd", "qlora_cross_entropy_bwd",
+    "qlora_cross_entropy_fwd", "qlora_cross_entropy_bwd", "qlora_cross_entropy_fused",
 ]

@@ -639,3 +639,27 @@ def cross_entropy_bwd(logits, labels, fwd, dloss=None, inplace=False):
                                                   _ptr(dloss), _ptr(fwd["n_valid"]), _ptr(dX), ldd,
                                                   _stream()), "qlora_cross_entropy_bwd")
     return dX
+
+
+def cross_entropy_fused(logits, labels, dloss: float = 1.0, inplace=False):
+    """Forward and backward in one call (dloss known up front): the outputs of
+    cross_entropy_fwd plus "dlogits" for the mean loss scaled by dloss."""
+    m, V = logits.shape
+    ld = _logit_rows(logits, "logits")
+    _need(labels, "labels", torch.int64, (m,))
+    dev = logits.device
+    out = dict(loss=torch.empty((1,), dtype=torch.float32, device=dev),
+               n_valid=torch.empty((1,), dtype=torch.int32, device=dev),
+               lse=torch.empty((m,), dtype=torch.float32, device=dev),
+               ce=torch.empty((m,), dtype=torch.float32, device=dev))
+    if inplace:
+        dX = logits
+    else:
+        dX = torch.empty((m, (V + 7) // 8 * 8), dtype=torch.bfloat16, device=dev)[:, :V]
+    ldd = _logit_rows(dX, "dlogits")
+    _lib.check(_lib.lib().qlora_cross_entropy_fused(_ptr(logits), ld, m, V, _ptr(labels), float(dloss),
+                                                    _ptr(out["lse"]), _ptr(out["ce"]), _ptr(out["loss"]),
+                                                    _ptr(out["n_valid"]), _ptr(dX), ldd, _stream()),
+               "qlora_cross_entropy_fused")
+    out["dlogits"] = dX
+    return out

@@ -1319,4 +1319,24 @@ int qlora_cross_entropy_bwd(const uint16_t* logits, int64_t ld, int64_t m, int64
   return QLORA_OK;
 }
 
+int qlora_cross_entropy_fused(const uint16_t* logits, int64_t ld, int64_t m, int64_t V,
+                              const int64_t* labels, float dloss, float* lse, float* ce_rows,
+                              float* loss, int32_t* n_valid, uint16_t* dlogits, int64_t ld_d,
+                              void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 31) || V < 1 || V >= ((int64_t)1 << 40) || ld < V || ld % 8 ||
+      ld_d < V || ld_d % 8)
+    return QLORA_ESHAPE;
+  if (!loss || !n_valid || !std::isfinite(dloss)) return QLORA_EINVAL;
+  if (m > 0 && (!logits || !labels || !lse || !ce_rows || !dlogits)) return QLORA_EINVAL;
+  if (m > 0 && logits == dlogits && ld != ld_d) return QLORA_EINVAL;
+  if (m > 0 && (!al16(logits) || !al16(dlogits) || ((uintptr_t)labels & 7) ||
+                ((uintptr_t)lse & 3) || ((uintptr_t)ce_rows & 3)))
+    return QLORA_ESHAPE;
+  if (((uintptr_t)loss & 3) || ((uintptr_t)n_valid & 3)) return QLORA_ESHAPE;
+  QL_TRY(launch_xent_fused(logits, ld, m, V, labels, dloss, lse, ce_rows, loss, n_valid, dlogits, ld_d,
+                           (hipStream_t)stream),
+         "cross_entropy_fused");
+  return QLORA_OK;
+}
+
 }  // extern "C"

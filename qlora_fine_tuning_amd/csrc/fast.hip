@@ -429,13 +429,14 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_bwd_kernel(const uint16_t* 
                                                                 const int64_t* __restrict__ labels,
                                                                 const float* __restrict__ lse_in,
                                                                 const float* __restrict__ dloss,
+                                                                float dloss_val,
                                                                 const int32_t* __restrict__ n_valid,
                                                                 uint16_t* dX, int64_t ldd) {
   const int64_t row = blockIdx.x;
   const int64_t lab = labels[row];
   const int n = *n_valid;
   const bool on = lab >= 0 && lab < V && n > 0;
-  const float scale = on ? (dloss ? *dloss : 1.0f) / (float)n : 0.0f;
+  const float scale = on ? (dloss ? *dloss : dloss_val) / (float)n : 0.0f;
   const float l2 = lse_in[row] * LOG2E;
   const uint16_t* x = X + row * ld;
   uint16_t* dx = dX + row * ldd;
@@ -450,6 +451,96 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_bwd_kernel(const uint16_t* 
       f[e] = (p - (c * 8 + e == lab ? 1.0f : 0.0f)) * scale;
     }
     *(u32x4_t*)(dx + c * 8) = pack8(f);
+  }
+  for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS) {
+    const float p = on ? exp2_hw(fmaf(bf16_to_f32(x[j]), LOG2E, -l2)) : 0.0f;
+    dx[j] = (uint16_t)f32_to_bf16((p - (j == lab ? 1.0f : 0.0f)) * scale);
+  }
+}
+
+// number of rows with a target (one 1024-thread workgroup, fixed order)
+__global__ __launch_bounds__(1024) void xent_count_kernel(const int64_t* __restrict__ labels,
+                                                          int64_t m, int64_t V,
+                                                          int32_t* __restrict__ n_valid) {
+  __shared__ int pn[1024];
+  int n = 0;
+#pragma unroll 8
+  for (int64_t i = threadIdx.x; i < m; i += 1024) {
+    const int64_t lab = labels[i];
+    n += (lab >= 0 && lab < V) ? 1 : 0;
+  }
+  pn[threadIdx.x] = n;
+  __syncthreads();
+  for (int o = 512; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) pn[threadIdx.x] += pn[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_valid = pn[0];
+}
+
+// Forward and backward of one row in one visit: the online (max, sum) pass of
+// xent_fwd_kernel, then the gradient of xent_bwd_kernel with scale dloss / n
+// (n from xent_count_kernel); the second pass re-reads the row from cache.
+// Same arithmetic as the two separate kernels, so the same bits. dX may be X.
+__global__ __launch_bounds__(XENT_THREADS) void xent_fused_kernel(const uint16_t* X, int64_t ld,
+                                                                  int64_t V,
+                                                                  const int64_t* __restrict__ labels,
+                                                                  float dloss,
+                                                                  const int32_t* __restrict__ n_valid,
+                                                                  float* __restrict__ lse_out,
+                                                                  float* __restrict__ ce_out,
+                                                                  uint16_t* dX, int64_t ldd) {
+  const int64_t row = blockIdx.x;
+  const uint16_t* x = X + row * ld;
+  const int64_t nc = V / 8;
+  float mx = -INFINITY, sm = 0.0f;
+  auto fold = [&](const u32x4_t& v) {
+    float f[8];
+    unpack8(v, f);
+    float cm = f[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
+    const float mn = fmaxf(mx, cm * LOG2E);
+    float cs = sm * exp2_hw(mx - mn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs += exp2_hw(fmaf(f[e], LOG2E, -mn));
+    mx = mn;
+    sm = cs;
+  };
+  int64_t c = threadIdx.x;
+  for (; c + 3 * XENT_THREADS < nc; c += 4 * XENT_THREADS) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold(v[u]);
+  }
+  for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
+  for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)
+    lse_merge(mx, sm, bf16_to_f32(x[j]) * LOG2E, 1.0f);
+  block_lse(mx, sm);   // ends with every thread past the block's barrier
+  const float lse = (mx + __log2f(sm)) * LN2;
+  const int64_t lab = labels[row];
+  if (threadIdx.x == 0) {
+    lse_out[row] = lse;
+    ce_out[row] = (lab >= 0 && lab < V) ? lse - bf16_to_f32(x[lab]) : 0.0f;
+  }
+  __syncthreads();   // x[lab] is read before any thread overwrites the row
+  const int n = *n_valid;
+  const bool on = lab >= 0 && lab < V && n > 0;
+  const float scale = on ? dloss / (float)n : 0.0f;
+  const float l2 = lse * LOG2E;
+  uint16_t* dx = dX + row * ldd;
+#pragma unroll 4
+  for (int64_t cc = threadIdx.x; cc < nc; cc += XENT_THREADS) {
+    float f[8];
+    unpack8(*(const u32x4_t*)(x + cc * 8), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = on ? exp2_hw(fmaf(f[e], LOG2E, -l2)) : 0.0f;
+      f[e] = (p - (cc * 8 + e == lab ? 1.0f : 0.0f)) * scale;
+    }
+    *(u32x4_t*)(dx + cc * 8) = pack8(f);
   }
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS) {
     const float p = on ? exp2_hw(fmaf(bf16_to_f32(x[j]), LOG2E, -l2)) : 0.0f;
@@ -473,7 +564,38 @@ hipError_t launch_xent_bwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, 
                            int64_t ldd, hipStream_t stream) {
   if (m == 0) return hipSuccess;
   xent_bwd_kernel<<<dim3((unsigned)m), dim3(XENT_THREADS), 0, stream>>>(X, ld, V, labels, lse, dloss,
-                                                                       n_valid, dX, ldd);
+                                                                       1.0f, n_valid, dX, ldd);
+  return hipGetLastError();
+}
+
+}  // namespace qlora
+
+namespace qlora {
+
+// Rows of up to 64 KB take the one-visit kernel: with about 2048 rows in
+// flight the re-read hits cache. Longer rows (Gemma's 256K vocabulary) would
+// be read twice from HBM, so they take the forward and backward kernels in
+// turn, which give the same bits.
+constexpr int64_t XENT_FUSED_MAX_ROW_BYTES = 65536;
+
+hipError_t launch_xent_fused(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
+                             float dloss, float* lse, float* ce, float* loss, int32_t* n_valid,
+                             uint16_t* dX, int64_t ldd, hipStream_t stream) {
+  if (V * 2 > XENT_FUSED_MAX_ROW_BYTES) {
+    hipError_t e = launch_xent_fwd(X, ld, m, V, labels, lse, ce, loss, n_valid, stream);
+    if (e != hipSuccess || m == 0) return e;
+    xent_bwd_kernel<<<dim3((unsigned)m), dim3(XENT_THREADS), 0, stream>>>(X, ld, V, labels, lse, nullptr,
+                                                                         dloss, n_valid, dX, ldd);
+    return hipGetLastError();
+  }
+  xent_count_kernel<<<dim3(1), dim3(1024), 0, stream>>>(labels, m, V, n_valid);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m == 0) return e;
+  xent_fused_kernel<<<dim3((unsigned)m), dim3(XENT_THREADS), 0, stream>>>(X, ld, V, labels, dloss,
+                                                                         n_valid, lse, ce, dX, ldd);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  xent_mean_kernel<<<dim3(1), dim3(1024), 0, stream>>>(ce, labels, m, V, loss, n_valid);
   return hipGetLastError();
 }
 

@@ -174,6 +174,10 @@ hipError_t launch_rope(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t ldy,
 // n_valid (device scalars). Backward: dX [m][V] (pitch ldd), may be X.
 hipError_t launch_xent_fwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
                            float* lse, float* ce, float* loss, int32_t* n_valid, hipStream_t stream);
+// forward and backward in one visit of each row; dloss is the upstream scale
+hipError_t launch_xent_fused(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
+                             float dloss, float* lse, float* ce, float* loss, int32_t* n_valid,
+                             uint16_t* dX, int64_t ldd, hipStream_t stream);
 hipError_t launch_xent_bwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, const int64_t* labels,
                            const float* lse, const float* dloss, const int32_t* n_valid, uint16_t* dX,
                            int64_t ldd, hipStream_t stream);

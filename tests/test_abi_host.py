@@ -227,3 +227,7 @@ def test_norm_rope_xent_validation_errors(L):
     assert L.qlora_cross_entropy_fwd(F_, 104, 4, 100, F_, F_, F_, None, F_, None) == -1  # no loss
     assert L.qlora_cross_entropy_bwd(F_, 104, 4, 100, F_, F_, None, None, F_, 104, None) == -1
     assert L.qlora_cross_entropy_bwd(F_, 104, 4, 100, F_, F_, None, F_, F_, 112, None) == -1  # in place
+    assert L.qlora_cross_entropy_fused(F_, 104, 4, 100, F_, f(1.0), F_, F_, None, F_, F_, 104, None) == -1
+    assert L.qlora_cross_entropy_fused(F_, 104, 4, 100, F_, f(float("nan")), F_, F_, F_, F_, F_, 104,
+                                       None) == -1
+    assert L.qlora_cross_entropy_fused(F_, 104, 4, 100, F_, f(1.0), F_, F_, F_, F_, F_, 100, None) == -2

@@ -201,3 +201,24 @@ def test_cross_entropy_full_size_llama():
     X64 = f64(X[rows])
     dXr = F.cross_entropy_bwd(X64, lab[rows], lse[rows], n)
     _check("dX rows", dX[torch.as_tensor(rows, device=DEV)], dXr)
+
+
+@pytest.mark.parametrize("m,V,pad", [(13, 1001, 8), (64, 32000, 0), (3, 256000, 0)])
+def test_cross_entropy_fused_equals_separate_calls(m, V, pad):
+    ld = (V + pad + 7) // 8 * 8
+    full = I.normal_bf16("X", (m, ld), 3.0, seed=V + 2 * m)
+    lab = torch.from_numpy(_labels(m, V, seed=V + 1)).to(DEV)
+    Xd = full.to(DEV)[:, :V]
+    say(f"cross entropy fused m={m} V={V}")
+    sep = Q.cross_entropy_fwd(Xd, lab)
+    g_sep = Q.cross_entropy_bwd(Xd, lab, sep, dloss=torch.tensor([0.375], device=DEV))
+    fus = Q.cross_entropy_fused(Xd, lab, dloss=0.375)
+    X2 = full.to(DEV)[:, :V]   # a second padded copy, overwritten in place
+    fin = Q.cross_entropy_fused(X2, lab, dloss=0.375, inplace=True)
+    torch.cuda.synchronize()
+    for k in ("loss", "n_valid", "lse", "ce"):
+        assert torch.equal(sep[k], fus[k]) and torch.equal(sep[k], fin[k]), k
+    assert torch.equal(g_sep, fus["dlogits"]) and torch.equal(g_sep, fin["dlogits"])
+    assert fin["dlogits"].data_ptr() == X2.data_ptr()
+    loss, ce, lse, n = F.cross_entropy_fwd(f64(full[:, :V]), lab.cpu().numpy())
+    _check("dX vs oracle", fus["dlogits"], F.cross_entropy_bwd(f64(full[:, :V]), lab.cpu().numpy(), lse, n, 0.375))
