@@ -33,6 +33,7 @@ METRIC = "QLoRA MLP fwd+bwd TFLOP/s + % bf16 MFMA peak, Llama-7B shape, 8192 tok
 METRIC_QKV = "QLoRA q/k/v fwd+bwd TFLOP/s + % bf16 MFMA peak, {model} shape, 8192 tok"
 MLP_WORKLOADS = ["llama7b_mlp", "mistral7b_mlp", "gemma7b_mlp"]
 QKV_WORKLOADS = ["mistral7b_qkv", "llama7b_qkv"]
+LINEAR_WORKLOADS = ["llama7b_q_proj", "mistral7b_kv_proj"]
 QUANT_WORKLOAD = "llama7b_mlp_quantize"
 FAST_WORKLOADS = ["llama7b_norm_rope_xent", "gemma7b_norm_rope_xent"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -45,7 +46,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama7b_mlp",
-                   choices=MLP_WORKLOADS + QKV_WORKLOADS + [QUANT_WORKLOAD] + FAST_WORKLOADS)
+                   choices=MLP_WORKLOADS + QKV_WORKLOADS + LINEAR_WORKLOADS + [QUANT_WORKLOAD]
+                   + FAST_WORKLOADS)
+    p.add_argument("--tokens", type=int, default=0,
+                   help="token count instead of the workload's 8192 (e.g. one GPU's data-parallel share)")
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--base", default="nf4", choices=["nf4", "bf16"],
                    help="base weights: NF4 (QLoRA, default) or bf16 (16-bit LoRA variant)")
@@ -77,6 +81,12 @@ def mlp_flops(m, d, h, r):
     weight gradient) plus 2*m*r*(in+out) per LoRA projection forward and twice
     that backward."""
     return 6 * 2 * m * d * h + 3 * 3 * 2 * m * r * (d + h)
+
+
+def linear_flops(m, k, n, r):
+    """Algorithmic FLOPs of one linear layer forward + backward: two base products
+    2*m*k*n, 2*m*r*(k+n) of LoRA forward and twice that backward."""
+    return 4 * m * k * n + 6 * m * r * (k + n)
 
 
 def qkv_flops(m, d, ns, r):
@@ -376,13 +386,29 @@ def main():
     from qlora_fine_tuning_amd import _lib
     from qlora_fine_tuning_amd import inputs as I
 
+    import dataclasses
+
     qkv = a.workload in QKV_WORKLOADS
+    lin = a.workload in LINEAR_WORKLOADS
     cfg = {"llama7b_mlp": I.LLAMA_MLP, "mistral7b_mlp": I.MISTRAL_MLP,
            "gemma7b_mlp": I.GEMMA_MLP, "mistral7b_qkv": I.MISTRAL_QKV,
-           "llama7b_qkv": I.LLAMA_QKV}[a.workload]
+           "llama7b_qkv": I.LLAMA_QKV, "llama7b_q_proj": I.QPROJ,
+           "mistral7b_kv_proj": I.MISTRAL_KV}[a.workload]
+    full_m = cfg.m
+    if a.tokens:
+        cfg = dataclasses.replace(cfg, m=a.tokens)
     dev = "cuda:0"
     w16 = a.base == "bf16"
-    if qkv:
+    if lin:
+        if w16:
+            sys.exit("the linear workloads run the NF4 layer (--base nf4)")
+        d = I.linear_inputs(cfg, dense_w=False, role="k" if a.workload == "mistral7b_kv_proj" else "")
+        wl = Q.NF4Weight(d["codes"].to(dev), d["absmax"].to(dev))
+        A_, B_ = d["A"].to(dev), d["B"].to(dev)
+        X, dY = d["X"].to(dev), d["dY"].to(dev)
+        nbytes = Q.linear_workspace_bytes(cfg.m, cfg.k, cfg.n, cfg.r, a.mode)
+        w = wl
+    elif qkv:
         if a.mode == "fused":
             sys.exit("the q/k/v path always stages its bf16 weights (no fused mode)")
         d = I.qkv_inputs(cfg, dense_w=w16)
@@ -412,7 +438,10 @@ def main():
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step():
-        if qkv:
+        if lin:
+            _, U = Q.linear_fwd(X, wl, A_, B_, cfg.s, mode=a.mode, ws=ws)
+            Q.linear_bwd(dY, X, U, wl, A_, B_, cfg.s, mode=a.mode, ws=ws)
+        elif qkv:
             fwd, bwd = (Q.qkv16_fwd, Q.qkv16_bwd) if w16 else (Q.qkv_fwd, Q.qkv_bwd)
             _, _, _, U = fwd(X, w, ws=ws)
             bwd(*dYs, X, U, w, ws=ws)
@@ -442,17 +471,27 @@ def main():
 
     peak_meas, shader_ghz = Q.probe_mfma_peak(20000)
 
-    flops = qkv_flops(cfg.m, cfg.d, ns, cfg.r) if qkv else mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
+    if lin:
+        flops = linear_flops(cfg.m, cfg.k, cfg.n, cfg.r)
+    elif qkv:
+        flops = qkv_flops(cfg.m, cfg.d, ns, cfg.r)
+    else:
+        flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
-    traffic = None if w16 else gemm_traffic(os.path.join(os.path.dirname(_lib.__file__), "csrc"),
-                                            cfg.name, "staged" if (qkv or a.mode == "auto") else a.mode)
-    if qkv:
-        metric = METRIC_QKV.format(model="Mistral-7B" if cfg is I.MISTRAL_QKV else "Llama-7B")
+    traffic = None if (w16 or cfg.m != full_m) else gemm_traffic(
+        os.path.join(os.path.dirname(_lib.__file__), "csrc"), cfg.name,
+        "staged" if (qkv or a.mode == "auto") else a.mode)
+    if lin:
+        metric = f"QLoRA linear fwd+bwd TFLOP/s + % bf16 MFMA peak, {cfg.name}, {cfg.m} tok"
+        shape = {"k": cfg.k, "n": cfg.n}
+    elif qkv:
+        metric = METRIC_QKV.format(model="Mistral-7B" if a.workload == "mistral7b_qkv" else "Llama-7B")
         shape = {"d": cfg.d, "n_q": cfg.n_q, "n_k": cfg.n_k, "n_v": cfg.n_v}
     else:
         metric = METRIC
         shape = {"d": cfg.d, "h": cfg.h, "act": cfg.act}
+    metric = metric.replace("8192 tok", f"{cfg.m} tok")
     out = {
         "metric": metric, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
@@ -475,7 +514,7 @@ def main():
                      "frac_of_measured_peak": round(achieved / peak_meas, 4),
                      "shader_ghz_under_mfma_load": round(shader_ghz, 3)},
     }
-    if a.cpu_tokens > 0 and not w16:
+    if a.cpu_tokens > 0 and not w16 and not lin:
         del X, dY, ws, w
         torch.cuda.empty_cache()
         base = cpu_baseline_qkv if qkv else cpu_baseline

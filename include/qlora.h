@@ -124,6 +124,15 @@ const char* qlora_version(void);
 /* The 16 NF4 levels compiled into the library, ascending (host buffer). */
 void qlora_nf4_levels(float out_host[16]);
 
+/* K splits the library uses for a base GEMM with a plain-store epilogue
+ * (output [m][n], depth k) when the base weight is bf16 in memory (the staged
+ * and 16-bit paths): outputs with fewer than 256 tiles of 256 x 256 run as up
+ * to 8 K ranges of at least 512, each writing fp32 partials to the workspace,
+ * then one pass sums them in a fixed order and stores bf16. 1 means no split;
+ * -1 for negative sizes. A pure function of the shape (workspace queries
+ * include the partials), so results are deterministic. Host only. */
+int qlora_gemm_split_count(int64_t m, int64_t n, int64_t k);
+
 /* Standalone dequantization: out [n][k] bf16 = dequant(W). Bit-exact
  * contract: bf16_rne(fp32_rne(level[code] * absmax)). */
 int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);

@@ -7,7 +7,7 @@ the library; the first call does, and fails loudly if it was not built.
 """
 
 __all__ = [
-    "NF4Weight", "MlpWeights", "version", "nf4_levels", "nf4_dequant", "nf4_quantize",
+    "NF4Weight", "MlpWeights", "version", "nf4_levels", "gemm_split_count", "nf4_dequant", "nf4_quantize",
     "linear_workspace_bytes", "linear_fwd", "linear_bwd",
     "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read", "probe_mfma_peak",
     "linear16_workspace_bytes", "linear16_fwd", "linear16_bwd",

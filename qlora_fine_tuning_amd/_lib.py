@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_last_error.argtypes = []
         L.qlora_version.restype = ctypes.c_char_p
         L.qlora_version.argtypes = []
+        L.qlora_gemm_split_count.restype = ctypes.c_int
+        L.qlora_gemm_split_count.argtypes = [ctypes.c_int64] * 3
         L.qlora_nf4_levels.restype = None
         L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.qlora_nf4_dequant.restype = ctypes.c_int
@@ -175,6 +177,7 @@ def check(status: int, what: str) -> None:
 
 EXPORTED = [
     "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
+    "qlora_gemm_split_count",
     "qlora_nf4_dequant", "qlora_nf4_quantize", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",

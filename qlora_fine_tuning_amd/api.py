@@ -108,6 +108,11 @@ def nf4_levels() -> torch.Tensor:
     return torch.tensor(list(buf), dtype=torch.float32)
 
 
+def gemm_split_count(m: int, n: int, k: int) -> int:
+    """K splits of a store-epilogue base GEMM [m][n] of depth k on a bf16 B operand."""
+    return int(_lib.lib().qlora_gemm_split_count(m, n, k))
+
+
 def nf4_dequant(w: NF4Weight) -> torch.Tensor:
     out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
     _lib.check(_lib.lib().qlora_nf4_dequant(w.c_struct(), _ptr(out), _stream()), "qlora_nf4_dequant")

@@ -90,12 +90,27 @@ int resolve_mode(int mode) {
 
 bool valid_mode(int mode) { return mode >= QLORA_DEQUANT_AUTO && mode <= QLORA_DEQUANT_STAGED; }
 
+// Split-K partials of a store GEMM (M x N, depth K) on a bf16 B operand: the
+// launch gives a small output several K ranges when it has too few tiles to
+// fill the chip. Fused-dequant launches never split.
+int64_t splitk_elems(int64_t M, int64_t N, int64_t K, bool bf16_b) {
+  if (!bf16_b || M <= 0) return 0;
+  const int sp = gemm_splits((int)M, (int)N, (int)K);
+  return sp > 1 ? sp * M * N : 0;
+}
+void use_splitk(GemmArgs& g, float* part) {
+  if (g.bsrc != BSRC_BF16) return;
+  const int sp = gemm_splits(g.M, g.N, g.K);
+  if (sp > 1) { g.splits = sp; g.part = part; }
+}
+
 // ------------------------------------------------------------ linear plan --
 struct LinearFwdWs {
   uint16_t* bext;  // [n][KE]
   uint16_t* uext;  // [m][KE]
   uint16_t* wbf;   // [n][k] (staged)
   float* rpart;    // row-product split partials
+  float* kpart;    // split-K partials of the GEMM
 };
 
 size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearFwdWs* w) {
@@ -105,6 +120,7 @@ size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.uext = c.take<uint16_t>(m * KE);
   t.wbf = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(n * k) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
+  t.kpart = c.take<float>(splitk_elems(m, n, k, staged_like(mode)));
   if (w) *w = t;
   return c.off;
 }
@@ -117,6 +133,7 @@ struct LinearBwdWs {
   float* part;     // [chunks][max(n,k)][r]
   uint16_t* wt;    // [k][n]   dequantized W^T
   float* rpart;    // row-product split partials
+  float* kpart;    // split-K partials of the dX GEMM
 };
 
 size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearBwdWs* w) {
@@ -130,6 +147,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.part = c.take<float>(chunks * std::max(n, k) * r);
   t.wt = staged_like(mode) ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
+  t.kpart = c.take<float>(splitk_elems(m, k, n, staged_like(mode)));
   if (w) *w = t;
   return c.off;
 }
@@ -145,6 +163,7 @@ struct MlpFwdWs {
   uint16_t* wgu;     // [2h][d] staged, 32-row interleave of gate/up
   uint16_t* wd;      // [d][h]  staged
   float* rpart;      // row-product split partials
+  float* kpart;      // split-K partials of the down GEMM
 };
 
 size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpFwdWs* w) {
@@ -159,6 +178,7 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.wgu = staged_like(mode) ? c.take<uint16_t>(2 * h * d) : nullptr;
   t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
   t.rpart = c.take<float>(16 * m * 2 * r);
+  t.kpart = c.take<float>(splitk_elems(m, d, h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
 }
@@ -177,6 +197,7 @@ struct MlpBwdWs {
   uint16_t* wdt;     // [h][d]
   uint16_t* wgut;    // [d][2h]
   float* rpart;      // row-product split partials
+  float* kpart;      // split-K partials of the dX GEMM
 };
 
 size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpBwdWs* w) {
@@ -196,6 +217,7 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.wdt = staged_like(mode) ? c.take<uint16_t>(h * d) : nullptr;
   t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
   t.rpart = c.take<float>(16 * m * 2 * r);
+  t.kpart = c.take<float>(splitk_elems(m, d, 2 * h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
 }
@@ -334,6 +356,12 @@ const char* qlora_last_error(void) { return g_last_error.c_str(); }
 
 const char* qlora_version(void) { return "qlora-mi355x 0.1 gfx950"; }
 
+int qlora_gemm_split_count(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return -1;
+  if (m >= ((int64_t)1 << 30) || n >= ((int64_t)1 << 30) || k >= ((int64_t)1 << 30)) return 1;
+  return gemm_splits((int)m, (int)n, (int)k);
+}
+
 int qlora_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
                        void* stream) {
   if (n < 0 || k < 0 || k % 64 || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 31))
@@ -437,6 +465,7 @@ static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const ui
   g.Ae = t.uext; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
   g.M = (int)m; g.N = (int)n; g.K = (int)k; g.KE = KE;
   g.epi = EPI_STORE; g.C = Y; g.ldc = n;
+  use_splitk(g, t.kpart);
   QL_TRY(run_gemm(g, r, st), "linear_fwd: GEMM");
   return QLORA_OK;
 }
@@ -500,6 +529,7 @@ static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U
     g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
     g.M = (int)m; g.N = (int)k; g.K = (int)n; g.KE = KE;
     g.epi = EPI_STORE; g.C = dX; g.ldc = k;
+    use_splitk(g, t.kpart);
     QL_TRY(run_gemm(g, r, st), "linear_bwd: dX GEMM");
   }
   // dA = s T^T X
@@ -686,6 +716,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   g2.Ae = t.uextd; g2.ldae = KEd; g2.Be = t.bextd; g2.ldbe = KEd;
   g2.M = (int)m; g2.N = (int)d; g2.K = (int)h; g2.KE = KEd;
   g2.epi = EPI_STORE; g2.C = Y; g2.ldc = d;
+  use_splitk(g2, t.kpart);
   if (staged) QL_TRY(side.wait(2), "mlp_fwd: join");
   QL_TRY(run_gemm(g2, r, st), "mlp_fwd: down GEMM");
   return QLORA_OK;
@@ -832,6 +863,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     g2.Ae = t.textgu; g2.ldae = KEgu; g2.Be = t.bextdx; g2.ldbe = KEgu;
     g2.M = (int)m; g2.N = (int)d; g2.K = (int)(2 * h); g2.KE = KEgu;
     g2.epi = EPI_STORE; g2.C = dX; g2.ldc = d;
+    use_splitk(g2, t.kpart);
     QL_TRY(side.wait(1), "mlp_bwd: wait");   // transposed gate/up weights
     QL_TRY(run_gemm(g2, 2 * r, st), "mlp_bwd: dX GEMM");
   }
@@ -949,6 +981,7 @@ struct QkvFwdWs {
   uint16_t* uext;   // [m][KE]
   uint16_t* wcat;   // [nt][d]   [W_q; W_k; W_v] in bf16
   float* rpart;     // row-product split partials
+  float* kpart;     // split-K partials of the GEMM
 };
 
 static size_t plan_qkv_fwd(Carver& c, int64_t m, int64_t d, int64_t nt, int64_t r, QkvFwdWs* w) {
@@ -959,6 +992,7 @@ static size_t plan_qkv_fwd(Carver& c, int64_t m, int64_t d, int64_t nt, int64_t 
   t.uext = c.take<uint16_t>(m * KE);
   t.wcat = c.take<uint16_t>(nt * d);
   t.rpart = c.take<float>(16 * m * 3 * r);
+  t.kpart = c.take<float>(splitk_elems(m, nt, d, true));
   if (w) *w = t;
   return c.off;
 }
@@ -971,6 +1005,7 @@ struct QkvBwdWs {
   float* part;      // column-reduction partials
   uint16_t* wt;     // [d][nt]   [W_q^T | W_k^T | W_v^T] in bf16
   float* rpart;     // row-product split partials
+  float* kpart;     // split-K partials of the dX GEMM
 };
 
 static size_t plan_qkv_bwd(Carver& c, int64_t m, int64_t d, const int64_t n[3], int64_t r,
@@ -987,6 +1022,7 @@ static size_t plan_qkv_bwd(Carver& c, int64_t m, int64_t d, const int64_t n[3], 
   t.part = c.take<float>(chunks * std::max(nmax * r, d * ra));
   t.wt = c.take<uint16_t>(d * nt);
   t.rpart = c.take<float>(16 * m * r);
+  t.kpart = c.take<float>(splitk_elems(m, d, nt, true));
   if (w) *w = t;
   return c.off;
 }
@@ -1074,6 +1110,7 @@ static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t*
   g.epi = EPI_STORE3;
   g.C = out[0]; g.ldc = ld[0]; g.C1 = out[1]; g.ldc1 = ld[1]; g.C2 = out[2]; g.ldc2 = ld[2];
   g.nc1 = (int)off[1]; g.nc2 = (int)off[2];
+  use_splitk(g, t.kpart);
   QL_TRY(side.wait(1), "qkv_fwd: wait");
   QL_TRY(run_gemm(g, r, st), "qkv_fwd: GEMM");
   return QLORA_OK;
@@ -1185,6 +1222,7 @@ static int qkv_bwd_impl(const uint16_t* const dy[3], const int64_t lddy[3], cons
     g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
     g.M = (int)m; g.N = (int)d; g.K = (int)nt; g.KE = (int)KE;
     g.epi = EPI_STORE; g.C = dX; g.ldc = d;
+    use_splitk(g, t.kpart);
     QL_TRY(side.wait(1), "qkv_bwd: wait");
     QL_TRY(run_gemm(g, 3 * r, st), "qkv_bwd: dX GEMM");
   }

@@ -565,7 +565,11 @@ void gemm_bf16_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
-  const int pid = xcd_remap(blockIdx.x, ntm * ntn);
+  // job -> (tile, K split); the splits of a tile are consecutive job ids
+  const int nsplit = p.splits > 1 ? p.splits : 1;
+  const int job = xcd_remap(blockIdx.x, ntm * ntn * nsplit);
+  const int ksp = job % nsplit;
+  const int pid = job / nsplit;
   const int GM = 8;
   const int per_group = GM * ntn;
   const int group = pid / per_group;
@@ -575,6 +579,9 @@ void gemm_bf16_kernel(GemmArgs p) {
   const int tn = (pid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = p.K / BK;
+  // this job's k-steps [kt0, kt1) (the host keeps every split non-empty)
+  const int kper = (nk + nsplit - 1) / nsplit;
+  const int kt0 = ksp * kper, kt1 = min(nk, kt0 + kper);
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -691,13 +698,13 @@ void gemm_bf16_kernel(GemmArgs p) {
 
   // ---- main loop ----
 #pragma unroll
-  for (int q = 0; q < 16; ++q) issue1(0, q);
+  for (int q = 0; q < 16; ++q) issue1(kt0, q);
   for (int s = 1; s < G_PF; ++s)
-    if (s < nk) prefetch(s);
+    if (kt0 + s < kt1) prefetch(kt0 + s);
   wait_vm<0>();
   ring_barrier();
   Frag f0, f1;
-  load_frag(f0, stage_ptr(0), 0);
+  load_frag(f0, stage_ptr(kt0), 0);
   // step kt; PRE: step kt+1 exists (issue its loads and the L2 touch of kt+2)
   auto step = [&](int kt, auto pre_c) {
     constexpr bool pre = decltype(pre_c)::value;
@@ -715,23 +722,23 @@ void gemm_bf16_kernel(GemmArgs p) {
       interleave(8, (pre && ks < 2) ? 8 : 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (pre) prefetch(min(kt + G_PF, nk - 1));   // issued last: vmcnt retires in order
-    if (pre) wait_vm<2>(); else wait_vm<0>();     // step kt+1 landed (the touches may fly)
+    if (pre) prefetch(min(kt + G_PF, kt1 - 1));   // issued last: vmcnt retires in order
+    if (pre) wait_vm<2>(); else wait_vm<0>();      // step kt+1 landed (the touches may fly)
     ring_barrier();
-    if (kt + 1 < nk) load_frag(f0, stage_ptr(kt + 1), 0);
+    if (kt + 1 < kt1) load_frag(f0, stage_ptr(kt + 1), 0);
     mma(f1);
     interleave(8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  int kt = 0;
-  for (; kt + 1 < nk; ++kt) step(kt, std::integral_constant<bool, true>());
+  int kt = kt0;
+  for (; kt + 1 < kt1; ++kt) step(kt, std::integral_constant<bool, true>());
   step(kt, std::integral_constant<bool, false>());
   wait_vm<0>();
   __syncthreads();
 
   // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be;
-  // columns at or past KE read as zeros ----
-  if (p.KE > 0) {
+  // columns at or past KE read as zeros; split 0 only ----
+  if (p.KE > 0 && ksp == 0) {
     const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
     const int neA = rec_bytes(rowsA, p.ldae);
     const int neB = rec_bytes(rowsB, p.ldbe);
@@ -801,7 +808,11 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int row = grow(s), col = col0 + cc;
         if (row < p.M && col < p.N) {
           const float* x = &stage[s * SP + cc];
-          if (EPI == EPI_STORE || EPI == EPI_STORE3) {
+          if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1) {   // fp32 partial
+            float* o = p.part + ((int64_t)ksp * p.M + row) * p.N + col;
+            *(f32x4_t*)o = *(const f32x4_t*)x;
+            *(f32x4_t*)(o + 4) = *(const f32x4_t*)(x + 4);
+          } else if (EPI == EPI_STORE || EPI == EPI_STORE3) {
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             u32x4_t o;
             o[0] = pack_bf16x2(x0[0], x0[1]);
@@ -888,11 +899,64 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Split-K reduction: C = bf16(sum_s part[s]) in fixed order; a thread takes 8
+// columns of one row. EPI_STORE3 routes the columns as the GEMM epilogue does.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
+  const int64_t groups = (int64_t)p.M * (p.N / 8);
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= groups) return;
+  const int row = (int)(e / (p.N / 8));
+  const int col = (int)(e - (int64_t)row * (p.N / 8)) * 8;
+  f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+  for (int k = 0; k < p.splits; ++k) {
+    const float* src = p.part + ((int64_t)k * p.M + row) * p.N + col;
+    s0 += *(const f32x4_t*)src;
+    s1 += *(const f32x4_t*)(src + 4);
+  }
+  u32x4_t o;
+  o[0] = pack_bf16x2(s0[0], s0[1]);
+  o[1] = pack_bf16x2(s0[2], s0[3]);
+  o[2] = pack_bf16x2(s1[0], s1[1]);
+  o[3] = pack_bf16x2(s1[2], s1[3]);
+  uint16_t* dst;
+  if (EPI == EPI_STORE3)
+    dst = col < p.nc1   ? p.C + (int64_t)row * p.ldc + col
+          : col < p.nc2 ? p.C1 + (int64_t)row * p.ldc1 + (col - p.nc1)
+                        : p.C2 + (int64_t)row * p.ldc2 + (col - p.nc2);
+  else
+    dst = p.C + (int64_t)row * p.ldc + col;
+  *(u32x4_t*)dst = o;
+}
+
 template <int EPI, bool SEGA>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
-  gemm_bf16_kernel<EPI, SEGA><<<dim3(ntm * ntn), dim3(256), 0, stream>>>(a);
+  const int nsplit = a.splits > 1 ? a.splits : 1;
+  if (nsplit > 1) {
+    const int nk = a.K / BK, kper = (nk + nsplit - 1) / nsplit;
+    if ((EPI != EPI_STORE && EPI != EPI_STORE3) || !a.part || a.N % 8 || (nsplit - 1) * kper >= nk)
+      return hipErrorInvalidValue;
+  }
+  gemm_bf16_kernel<EPI, SEGA><<<dim3(ntm * ntn * nsplit), dim3(256), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  if (EPI == EPI_STORE || EPI == EPI_STORE3) {
+    const int64_t groups = (int64_t)a.M * (a.N / 8);
+    splitk_reduce_kernel<EPI><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream>>>(a);
+  }
   return hipGetLastError();
+}
+
+int gemm_splits(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int nk = K / BK;
+  if (tiles <= 0 || tiles >= 256 || nk < 16) return 1;
+  int sp = (int)(256 / tiles);
+  if (sp > nk / 8) sp = nk / 8;
+  if (sp > 8) sp = 8;
+  while (sp > 1 && (sp - 1) * ((nk + sp - 1) / sp) >= nk) --sp;
+  return sp < 1 ? 1 : sp;
 }
 
 template <int BSRC>
@@ -913,7 +977,7 @@ static hipError_t launch_b(const GemmArgs& a, hipStream_t stream) {
     }
     return hipErrorInvalidValue;
   }
-  if (a.A1) return hipErrorInvalidValue;
+  if (a.A1 || a.splits > 1) return hipErrorInvalidValue;
   switch (a.epi) {
     case EPI_STORE: return launch_t<BSRC, EPI_STORE>(a, stream);
     case EPI_GATEUP: return launch_t<BSRC, EPI_GATEUP>(a, stream);

@@ -76,6 +76,11 @@ struct GemmArgs {
   const uint16_t* Be;
   int64_t ldbe;
   int M, N, K, KE;
+  // split-K (EPI_STORE / EPI_STORE3, bf16 B source): splits > 1 runs each
+  // tile as `splits` K ranges writing fp32 partials part [splits][M][N], then a
+  // reduction sums them in order and stores; the K-extension rides on split 0
+  int splits;
+  float* part;
   // epilogue
   int epi;
   uint16_t* C;
@@ -96,6 +101,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// K splits for an M x N x K product with a store epilogue: enough to give
+// about 256 concurrent tiles when the output has fewer, each split at least 8
+// k-steps of 64, at most 8 splits, every split non-empty. A fixed function of
+// the shape, so workspace queries and launches agree.
+int gemm_splits(int M, int N, int K);
 
 // ---- LoRA skinny kernels (lora.hip) ----
 // U = G L^T for G [M][K] bf16 (ldg), L [R][K] bf16 (ldl), 1 <= R <= 64.

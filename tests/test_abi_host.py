@@ -70,6 +70,27 @@ def test_workspace_queries(L):
         8192, 4096, 11008, 16, 1)
 
 
+def test_gemm_split_count(L):
+    """K splits: none at 256 or more output tiles or below 16 k-steps of 64; otherwise
+    enough ranges to reach about 256 tiles, each at least 8 k-steps, at most 8."""
+    f = L.qlora_gemm_split_count
+    assert f(8192, 4096, 11008) == 1        # 512 tiles
+    assert f(4096, 4096, 4096) == 1         # exactly 256 tiles
+    assert f(8192, 1024, 4096) == 2         # 128 tiles
+    assert f(1024, 4096, 11008) == 4        # 64 tiles
+    assert f(1024, 4096, 22016) == 4
+    assert f(129, 1024, 4160) == 8          # 4 tiles, capped at 8
+    assert f(300, 320, 2368) == 4           # 37 k-steps: 8 per split at most 4 ranges
+    assert f(300, 2368, 960) == 1           # 15 k-steps
+    assert f(1, 64, 1536) == 3
+    assert f(0, 64, 4096) == 1
+    assert f(-1, 64, 64) == -1
+    # the fp32 partials are part of the workspace: the staged linear (which
+    # splits) needs at least 2 x m x n x 4 bytes more than the fused one
+    assert L.qlora_linear_workspace_bytes(129, 4160, 1024, 8, 2) - L.qlora_linear_workspace_bytes(
+        129, 4160, 1024, 8, 1) >= 2 * 129 * 1024 * 4
+
+
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
