@@ -665,31 +665,35 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
     J.zero(d, KEd - 2 * r, t.bextd + 2 * r, KEd, 1);
     QL_TRY(launch_prep(J, st), "mlp_fwd: LoRA layouts");
   }
-  // staged: the three dequants run on the helper stream while the caller's
-  // stream does the row products; each GEMM waits for its own weight
+  // staged: the caller's stream writes the gate/up weight that the first GEMM
+  // needs, while the helper stream does the row product [Ug | Uu] and then the
+  // down weight; each GEMM waits for exactly what it reads
   const bool staged = staged_like(mode);
   const bool w16 = mode == MODE_BF16;
   Side side(st);
+  // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
+  auto row_u = [&](hipStream_t q) {
+    return launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
+                         t.uextgu, KEgu, KEgu, t.rpart, q);
+  };
   if (staged) {
     QL_TRY(side.open(), "mlp_fwd: helper stream");
     QL_TRY(side.fork(0), "mlp_fwd: fork");
     hipStream_t ss = side.stream();
+    QL_TRY(row_u(ss), "mlp_fwd: Ug, Uu");
+    QL_TRY(side.mark(1), "mlp_fwd: mark");
     if (w16) {   // 16-bit base: interleave copy of gate/up; down is used as it is
-      QL_TRY(launch_w16_rows(w->gate.w16, h, d, t.wgu, d, 1, ss), "mlp_fwd: gate/up copy");
-      QL_TRY(launch_w16_rows(w->up.w16, h, d, t.wgu, d, 2, ss), "mlp_fwd: gate/up copy");
-      QL_TRY(side.mark(1), "mlp_fwd: mark");
+      QL_TRY(launch_w16_rows(w->gate.w16, h, d, t.wgu, d, 1, st), "mlp_fwd: gate/up copy");
+      QL_TRY(launch_w16_rows(w->up.w16, h, d, t.wgu, d, 2, st), "mlp_fwd: gate/up copy");
     } else {
-      QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, ss), "mlp_fwd: dequant");
-      QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, ss), "mlp_fwd: dequant");
-      QL_TRY(side.mark(1), "mlp_fwd: mark");
+      QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
+      QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
       QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
     }
     QL_TRY(side.mark(2), "mlp_fwd: mark");
+  } else {
+    QL_TRY(row_u(st), "mlp_fwd: Ug, Uu");
   }
-  // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
-  QL_TRY(launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
-                       t.uextgu, KEgu, KEgu, t.rpart, st),
-         "mlp_fwd: Ug, Uu");
   // gate || up GEMM with the activation epilogue
   GemmArgs g = gemm_args();
   g.A = X; g.lda = d;
@@ -783,6 +787,15 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   QL_TRY(side.open(), "mlp_bwd: helper stream");
   hipStream_t ss = side.stream();
   QL_TRY(side.fork(0), "mlp_bwd: fork");
+  // Td = dY Bd: on the helper stream beside the caller's W_d^T when staged
+  auto row_td = [&](hipStream_t q) {
+    return launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
+                         t.textd, KEd, KEd, t.rpart, q);
+  };
+  if (staged) {
+    QL_TRY(row_td(ss), "mlp_bwd: Td");
+    QL_TRY(side.mark(2), "mlp_bwd: mark");
+  }
   if (w16) {
     QL_TRY(launch_w16_transpose(w->gate.w16, h, d, t.wgut, 2 * h, 0, ss), "mlp_bwd: Wg^T");
     QL_TRY(launch_w16_transpose(w->up.w16, h, d, t.wgut, 2 * h, h, ss), "mlp_bwd: Wu^T");
@@ -805,10 +818,12 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   else if (staged)
     QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
            "mlp_bwd: dequant Wd^T");
-  QL_TRY(launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
-                       t.textd, KEd, KEd, t.rpart, st),
-         "mlp_bwd: Td");
-  QL_TRY(side.fork(2), "mlp_bwd: fork");
+  if (staged) {
+    QL_TRY(side.wait(2), "mlp_bwd: wait");
+  } else {
+    QL_TRY(row_td(st), "mlp_bwd: Td");
+    QL_TRY(side.fork(2), "mlp_bwd: fork");
+  }
   // dAd = s Td^T H, H recomputed from g, u (helper stream, beside the dH GEMM)
   QL_TRY(launch_colreduce(nullptr, g_save, u_save, w->act, h, (int)m, (int)h, t.td, r, (int)r,
                           t.part, ss),
