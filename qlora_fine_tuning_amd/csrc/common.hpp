@@ -38,8 +38,11 @@ __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rc
 //   act 1: gelu_tanh(g) = g/2 * (1 + tanh z), z = sqrt(2/pi) (g + 0.044715 g^3)
 //          gelu'(g) = (1 + tanh z)/2 + g/2 (1 - tanh^2 z) sqrt(2/pi) (1 + 3*0.044715 g^2)
 // tanh z is formed as 2 * sigmoid(2z) - 1.
-__device__ __forceinline__ void act_fwd_bwd(int act, float g, float* a, float* da) {
-  if (act == 0) {
+// ACT is a compile-time constant here so that code applying it to many values
+// has no branch per value; the int overloads pick one of the two.
+template <int ACT>
+__device__ __forceinline__ void act_fwd_bwd_t(float g, float* a, float* da) {
+  if (ACT == 0) {
     float sg = sigmoidf_(g);
     *a = g * sg;
     *da = sg * (1.0f + g * (1.0f - sg));
@@ -54,13 +57,23 @@ __device__ __forceinline__ void act_fwd_bwd(int act, float g, float* a, float* d
   }
 }
 
-__device__ __forceinline__ float act_fwd(int act, float g) {
-  if (act == 0) return g * sigmoidf_(g);
+template <int ACT>
+__device__ __forceinline__ float act_fwd_t(float g) {
+  if (ACT == 0) return g * sigmoidf_(g);
   const float k0 = 0.7978845608028654f;
   const float k1 = 0.044715f;
   float z = k0 * (g + k1 * g * g * g);
   float th = 2.0f * sigmoidf_(2.0f * z) - 1.0f;
   return 0.5f * g * (1.0f + th);
+}
+
+__device__ __forceinline__ void act_fwd_bwd(int act, float g, float* a, float* da) {
+  if (act == 0) act_fwd_bwd_t<0>(g, a, da);
+  else act_fwd_bwd_t<1>(g, a, da);
+}
+
+__device__ __forceinline__ float act_fwd(int act, float g) {
+  return act == 0 ? act_fwd_t<0>(g) : act_fwd_t<1>(g);
 }
 
 }  // namespace qlora

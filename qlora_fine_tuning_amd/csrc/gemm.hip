@@ -116,6 +116,16 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Orders one wave's LDS accesses across its lanes (a lane reads what another
+// lane of the same wave wrote). LDS serves a wave's instructions in issue
+// order, so only the compiler has to be held back. Unlike __syncthreads() it
+// waits for nothing: the global stores in flight keep going.
+__device__ __forceinline__ void wave_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
 __constant__ uint32_t c_nf4_levels_gemm[16] = {QLORA_NF4_LEVEL_BITS};
@@ -409,99 +419,131 @@ void gemm_nt_kernel(GemmArgs p) {
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);  // fits in the ring
   const int row0 = m0 + wm * 128;
   const int col0 = n0 + wn * 64;
+  // the activation is fixed per launch: one branch here, none per value
+  auto slabs = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
+      // ACT_BWD: this slab's g and u are fetched before the staging so that
+      // their latency overlaps it (rows past M read nothing)
+      u32x4_t gw[4], uw[4];
+      if (EPI == EPI_ACT_BWD) {
+        const int cc = (lane & 7) * 8;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * SP + nt * 32 + (lane & 31)] = acc[mt][nt][v];
-    __syncthreads();
-    if (EPI == EPI_STORE) {
-      // lane: 8 consecutive columns of one row per step, 8 rows per step
-      const int cc = (lane & 7) * 8;
-      for (int q = 0; q < 4; ++q) {
-        const int rr = q * 8 + (lane >> 3);
-        const int row = row0 + mt * 32 + rr;
-        const int col = col0 + cc;
-        const f32x4_t x0 = *(const f32x4_t*)&stage[rr * SP + cc];
-        const f32x4_t x1 = *(const f32x4_t*)&stage[rr * SP + cc + 4];
-        if (row < p.M && col < p.N) {
-          u32x4_t o;
-          o[0] = pack_bf16x2(x0[0], x0[1]);
-          o[1] = pack_bf16x2(x0[2], x0[3]);
-          o[2] = pack_bf16x2(x1[0], x1[1]);
-          o[3] = pack_bf16x2(x1[2], x1[3]);
-          *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
-        }
-      }
-    } else if (EPI == EPI_GATEUP) {
-      // staged columns: [gate j0..j0+31 | up j0..j0+31], j0 = col0 / 2
-      const int jj = (lane & 3) * 8;
-      const int64_t j = (int64_t)(col0 >> 1) + jj;
-      for (int q = 0; q < 2; ++q) {
-        const int rr = q * 16 + (lane >> 2);
-        const int row = row0 + mt * 32 + rr;
-        const float* gs = &stage[rr * SP + jj];
-        const float* us = gs + 32;
-        if (row < p.M && col0 < p.N) {
-          u32x4_t og, ou, oh;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float hv[2];
-            uint32_t gb[2], ub[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              gb[t] = f32_to_bf16(gs[2 * e + t]);
-              ub[t] = f32_to_bf16(us[2 * e + t]);
-              hv[t] = act_fwd(p.act, bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
-            }
-            og[e] = gb[0] | (gb[1] << 16);
-            ou[e] = ub[0] | (ub[1] << 16);
-            oh[e] = pack_bf16x2(hv[0], hv[1]);
+        for (int q = 0; q < 4; ++q) {
+          const int row = row0 + mt * 32 + q * 8 + (lane >> 3), col = col0 + cc;
+          gw[q] = u32x4_t{0u, 0u, 0u, 0u};
+          uw[q] = u32x4_t{0u, 0u, 0u, 0u};
+          if (row < p.M && col < p.N) {
+            const int64_t o = (int64_t)row * p.hdim + col;
+            gw[q] = *(const u32x4_t*)(p.g_in + o);
+            uw[q] = *(const u32x4_t*)(p.u_in + o);
           }
-          const int64_t o = (int64_t)row * p.hdim + j;
-          *(u32x4_t*)(p.g_out + o) = og;
-          *(u32x4_t*)(p.u_out + o) = ou;
-          *(u32x4_t*)(p.h_out + o) = oh;
         }
       }
-    } else {  // EPI_ACT_BWD: staged values are dH
-      const int cc = (lane & 7) * 8;
-      for (int q = 0; q < 4; ++q) {
-        const int rr = q * 8 + (lane >> 3);
-        const int row = row0 + mt * 32 + rr;
-        const int col = col0 + cc;
-        if (row < p.M && col < p.N) {
-          const int64_t o = (int64_t)row * p.hdim + col;
-          const u32x4_t gw = *(const u32x4_t*)(p.g_in + o);
-          const u32x4_t uw = *(const u32x4_t*)(p.u_in + o);
-          const float* dh = &stage[rr * SP + cc];
-          u32x4_t odg, odu;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float dg[2], du[2];
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const float g = bf16_to_f32(t ? (gw[e] >> 16) : (gw[e] & 0xFFFFu));
-              const float u = bf16_to_f32(t ? (uw[e] >> 16) : (uw[e] & 0xFFFFu));
-              float a, da;
-              act_fwd_bwd(p.act, g, &a, &da);
-              const float d = dh[2 * e + t];
-              dg[t] = d * u * da;
-              du[t] = d * a;
-            }
-            odg[e] = pack_bf16x2(dg[0], dg[1]);
-            odu[e] = pack_bf16x2(du[0], du[1]);
+        for (int v = 0; v < 16; ++v)
+          stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * SP + nt * 32 + (lane & 31)] = acc[mt][nt][v];
+      wave_sync();   // the staging region is this wave's own
+      if (EPI == EPI_STORE) {
+        // lane: 8 consecutive columns of one row per step, 8 rows per step
+        const int cc = (lane & 7) * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = q * 8 + (lane >> 3);
+          const int row = row0 + mt * 32 + rr;
+          const int col = col0 + cc;
+          const f32x4_t x0 = *(const f32x4_t*)&stage[rr * SP + cc];
+          const f32x4_t x1 = *(const f32x4_t*)&stage[rr * SP + cc + 4];
+          if (row < p.M && col < p.N) {
+            u32x4_t o;
+            o[0] = pack_bf16x2(x0[0], x0[1]);
+            o[1] = pack_bf16x2(x0[2], x0[3]);
+            o[2] = pack_bf16x2(x1[0], x1[1]);
+            o[3] = pack_bf16x2(x1[2], x1[3]);
+            *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
           }
-          const int64_t od = (int64_t)row * (2 * p.hdim) + col;
-          *(u32x4_t*)(p.dgu + od) = odg;
-          *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
+        }
+      } else if (EPI == EPI_GATEUP) {
+        // staged columns: [gate j0..j0+31 | up j0..j0+31], j0 = col0 / 2
+        const int jj = (lane & 3) * 8;
+        const int64_t j = (int64_t)(col0 >> 1) + jj;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int rr = q * 16 + (lane >> 2);
+          const int row = row0 + mt * 32 + rr;
+          const float* gs = &stage[rr * SP + jj];
+          const float* us = gs + 32;
+          if (row < p.M && col0 < p.N) {
+            float gv[8], uv[8];
+            *(f32x4_t*)gv = *(const f32x4_t*)gs;
+            *(f32x4_t*)(gv + 4) = *(const f32x4_t*)(gs + 4);
+            *(f32x4_t*)uv = *(const f32x4_t*)us;
+            *(f32x4_t*)(uv + 4) = *(const f32x4_t*)(us + 4);
+            u32x4_t og, ou, oh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float hv[2];
+              uint32_t gb[2], ub[2];
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                gb[t] = f32_to_bf16(gv[2 * e + t]);
+                ub[t] = f32_to_bf16(uv[2 * e + t]);
+                hv[t] = act_fwd_t<ACT>(bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
+              }
+              og[e] = gb[0] | (gb[1] << 16);
+              ou[e] = ub[0] | (ub[1] << 16);
+              oh[e] = pack_bf16x2(hv[0], hv[1]);
+            }
+            const int64_t o = (int64_t)row * p.hdim + j;
+            *(u32x4_t*)(p.g_out + o) = og;
+            *(u32x4_t*)(p.u_out + o) = ou;
+            *(u32x4_t*)(p.h_out + o) = oh;
+          }
+        }
+      } else {  // EPI_ACT_BWD: staged values are dH
+        const int cc = (lane & 7) * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = q * 8 + (lane >> 3);
+          const int row = row0 + mt * 32 + rr;
+          const int col = col0 + cc;
+          if (row < p.M && col < p.N) {
+            float dh[8];
+            *(f32x4_t*)dh = *(const f32x4_t*)&stage[rr * SP + cc];
+            *(f32x4_t*)(dh + 4) = *(const f32x4_t*)&stage[rr * SP + cc + 4];
+            u32x4_t odg, odu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float dg[2], du[2];
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                const float g = bf16_to_f32(t ? (gw[q][e] >> 16) : (gw[q][e] & 0xFFFFu));
+                const float u = bf16_to_f32(t ? (uw[q][e] >> 16) : (uw[q][e] & 0xFFFFu));
+                float a, da;
+                act_fwd_bwd_t<ACT>(g, &a, &da);
+                const float d = dh[2 * e + t];
+                dg[t] = d * u * da;
+                du[t] = d * a;
+              }
+              odg[e] = pack_bf16x2(dg[0], dg[1]);
+              odu[e] = pack_bf16x2(du[0], du[1]);
+            }
+            const int64_t od = (int64_t)row * (2 * p.hdim) + col;
+            *(u32x4_t*)(p.dgu + od) = odg;
+            *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
+          }
         }
       }
+      wave_sync();
     }
-    __syncthreads();
-  }
+  };
+  if ((EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.act != 0)
+    slabs(std::integral_constant<int, 1>());
+  else
+    slabs(std::integral_constant<int, 0>());
 }
 
 
@@ -772,8 +814,9 @@ void gemm_bf16_kernel(GemmArgs p) {
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
   const int col0 = n0 + wn * 128;
   // one slab per call; mt is a compile-time constant so that acc stays in registers
-  auto slab = [&](auto mt_c) {
+  auto slab = [&](auto mt_c, auto act_c) {
     constexpr int mt = decltype(mt_c)::value;
+    constexpr int ACT = decltype(act_c)::value;
     auto grow = [&](int s) { return m0 + wm * 128 + 8 * (s >> 1) + 2 * mt + (s & 1); };
     // ACT_BWD: fetch this slab's g and u first so that their latency overlaps
     // the staging (rows past M read nothing)
@@ -798,7 +841,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
         stage[(2 * (r & 15) + (r >> 4)) * SP + 8 * (j & 15) + 2 * nt + (j >> 4)] = acc[mt][nt][v];
       }
-    __syncthreads();
+    wave_sync();   // the staging region is this wave's own
     if (EPI == EPI_STORE || EPI == EPI_STORE3 || EPI == EPI_ACT_BWD) {
       // lane: 8 consecutive columns of one staged row; 4 rows per pass
       const int cc = (lane & 15) * 8;
@@ -828,6 +871,7 @@ void gemm_bf16_kernel(GemmArgs p) {
               dst = p.C + (int64_t)row * p.ldc + col;
             *(u32x4_t*)dst = o;
           } else {  // staged values are dH
+            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             u32x4_t odg, odu;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -837,8 +881,8 @@ void gemm_bf16_kernel(GemmArgs p) {
                 const float g = bf16_to_f32(t ? (gw[q][e] >> 16) : (gw[q][e] & 0xFFFFu));
                 const float u = bf16_to_f32(t ? (uw[q][e] >> 16) : (uw[q][e] & 0xFFFFu));
                 float a, da;
-                act_fwd_bwd(p.act, g, &a, &da);
-                const float d = x[2 * e + t];
+                act_fwd_bwd_t<ACT>(g, &a, &da);
+                const float d = e < 2 ? x0[2 * e + t] : x1[2 * e - 4 + t];
                 dg[t] = d * u * da;
                 du[t] = d * a;
               }
@@ -862,6 +906,11 @@ void gemm_bf16_kernel(GemmArgs p) {
         if (row < p.M && col0 < p.N) {
           const float* gs = &stage[s * SP + gcol];
           const float* us = gs + 32;
+          float gv[8], uv[8];
+          *(f32x4_t*)gv = *(const f32x4_t*)gs;
+          *(f32x4_t*)(gv + 4) = *(const f32x4_t*)(gs + 4);
+          *(f32x4_t*)uv = *(const f32x4_t*)us;
+          *(f32x4_t*)(uv + 4) = *(const f32x4_t*)(us + 4);
           u32x4_t og, ou, oh;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -869,9 +918,9 @@ void gemm_bf16_kernel(GemmArgs p) {
             uint32_t gb[2], ub[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              gb[t] = f32_to_bf16(gs[2 * e + t]);
-              ub[t] = f32_to_bf16(us[2 * e + t]);
-              hv[t] = act_fwd(p.act, bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
+              gb[t] = f32_to_bf16(gv[2 * e + t]);
+              ub[t] = f32_to_bf16(uv[2 * e + t]);
+              hv[t] = act_fwd_t<ACT>(bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
             }
             og[e] = gb[0] | (gb[1] << 16);
             ou[e] = ub[0] | (ub[1] << 16);
@@ -884,12 +933,19 @@ void gemm_bf16_kernel(GemmArgs p) {
         }
       }
     }
-    __syncthreads();
+    wave_sync();
   };
-  slab(std::integral_constant<int, 0>());
-  slab(std::integral_constant<int, 1>());
-  slab(std::integral_constant<int, 2>());
-  slab(std::integral_constant<int, 3>());
+  // the activation is fixed per launch: one branch here, none per value
+  auto slabs = [&](auto act_c) {
+    slab(std::integral_constant<int, 0>(), act_c);
+    slab(std::integral_constant<int, 1>(), act_c);
+    slab(std::integral_constant<int, 2>(), act_c);
+    slab(std::integral_constant<int, 3>(), act_c);
+  };
+  if ((EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.act != 0)
+    slabs(std::integral_constant<int, 1>());
+  else
+    slabs(std::integral_constant<int, 0>());
 }
 
 template <int BSRC, int EPI>
