@@ -20,6 +20,7 @@ oracle on a bounded token sample of the same workload).
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -95,16 +96,25 @@ def qkv_flops(m, d, ns, r):
     return sum(4 * m * d * n + 6 * m * r * (d + n) for n in ns)
 
 
+def code_digest(path):
+    """SHA-256 of a C++ source with comments and whitespace removed, so that a
+    comment edit does not count as a kernel change."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def gemm_traffic(lib_src_dir, workload, mode):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
     or None when it was taken on another workload or dequant mode, or the
-    kernel source changed since."""
+    kernel code changed since."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256(open(os.path.join(lib_src_dir, "gemm.hip"), "rb").read()).hexdigest()
+    h = code_digest(os.path.join(lib_src_dir, "gemm.hip"))
     for rec in json.load(open(path)):
-        if (rec.get("gemm_hip_sha256") == h and rec.get("workload_name") == workload
+        if (rec.get("gemm_hip_code_sha256") == h and rec.get("workload_name") == workload
                 and rec.get("dequant_mode") == mode):
             return rec.get("hbm_bytes_per_launch")
     return None

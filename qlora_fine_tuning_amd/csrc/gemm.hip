@@ -40,6 +40,17 @@
 // features, its K runs over output features, and the dequant writes the
 // transposed bf16 tile.
 //
+// Epilogues (both kernels): each wave stages a 32-row slab of its
+// accumulators through its own LDS region, so only wave-local ordering is
+// needed, and stores 16 bytes per lane. The gated epilogues take the
+// activation as a compile-time constant (one branch per launch, none per
+// value): with one wave per SIMD the epilogue runs with the matrix cores
+// idle, so its instruction count matters.
+//
+// Split-K (gemm_bf16_kernel, store epilogues only): an output with fewer than
+// 256 tiles is computed as several K ranges that write fp32 partials;
+// splitk_reduce_kernel sums them in a fixed order and stores bf16.
+//
 // Tile order: workgroup ids are dealt to the 8 XCDs round-robin; ids are
 // remapped so that each XCD walks a contiguous range of tiles, grouped 8
 // M-tiles at a time, which keeps shared A rows / B columns in that XCD's L2.
