@@ -580,10 +580,7 @@ void gemm_nt_kernel(GemmArgs p) {
 // step-(k+1) loads mostly hit; one barrier per step.
 // ===========================================================================
 namespace {
-constexpr int G_PITCH = 1040;           // bytes per 8-row DMA block
-constexpr int G_OPB = 32 * G_PITCH;     // one operand (256 rows x 64) per stage
-constexpr int G_STAGE = 2 * G_OPB;
-constexpr int G_PF = 2;                 // L2 prefetch distance (k-steps)
+constexpr int G_SLOT = 32768;           // one operand (256 rows x 64 bf16) of one k-step
 
 // buffer load of `size` bytes per lane into LDS at lds + size*lane; the
 // resource is rebuilt from uniform integers at each use (it stays in SGPRs)
@@ -612,7 +609,7 @@ constexpr uint32_t OOB = 0x80000000u;
 template <int EPI, bool SEGA>
 __global__ __launch_bounds__(256)
 void gemm_bf16_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G_STAGE + 256];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * G_SLOT];   // all 160 KB of LDS
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -644,16 +641,27 @@ void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // ---- operand sources: wave w, load j (0..7) fills DMA block 8w + j ----
+  // ---- operand ring ----
+  // Five 32 KB slots. Half-stage H_i, counted from this job's first k-step
+  // (H_2s = the A operand of step kt0 + s, H_2s+1 = its B operand), lives in
+  // slot i % 5: while a step reads two slots, the other three hold the next
+  // one and a half steps. A slot is 32 DMA blocks of 1 KB; block q holds tile
+  // rows 8q..8q+7 (64 bf16 each) at byte 1024 q. In each 256-byte unit u of a
+  // block (rows 2u, 2u+1), 16-byte position p holds logical position
+  // p ^ (q & 15), logical = (row & 1) * 8 + chunk. The 16 lanes of a fragment
+  // read take one logical position from 16 consecutive blocks, so they hit 16
+  // different bank groups without padding; the ring then fits LDS.
   const int64_t rowsA = min(BM, p.M - m0), rowsB = min(BN, p.N - n0);
   const uint64_t bA = (uint64_t)(p.A + (int64_t)m0 * p.lda), bB = (uint64_t)(p.B + (int64_t)n0 * p.ldb);
   const int nA = rec_bytes(rowsA, p.lda);
   const int nB = rec_bytes(rowsB, p.ldb);
-  const int lrow = 64 * wave + (lane >> 3);                      // + 8 j
-  const uint32_t voA = (uint32_t)(lrow * p.lda + (lane & 7) * 8) * 2u;
-  const uint32_t voB = (uint32_t)(lrow * p.ldb + (lane & 7) * 8) * 2u;
-  const uint32_t stA = (uint32_t)(8 * p.lda * 2), stB = (uint32_t)(8 * p.ldb * 2);
-  const uint32_t pfA = (uint32_t)(tid * p.lda * 2), pfB = (uint32_t)(tid * p.ldb * 2);
+  // DMA: wave w, load j (0..7) fills block q = 8w + j; lane l writes position
+  // l of it. Tile row and first column of that position:
+  auto drow = [&](int j) {
+    const int pl = (lane & 15) ^ ((8 * wave + j) & 15);
+    return 8 * (8 * wave + j) + 2 * (lane >> 4) + (pl >> 3);
+  };
+  auto dcol = [&](int j) { return (((lane & 15) ^ ((8 * wave + j) & 15)) & 7) * 8; };
   // A operand of k-step kt. SEGA: K is split into up to three segments, each
   // its own matrix with its own row pitch (segment starts are multiples of
   // BK, so a step never straddles two). The per-lane offsets are formed from
@@ -686,46 +694,38 @@ void gemm_bf16_kernel(GemmArgs p) {
     l = sl0 + (uint32_t)f1 * (sl1 - sl0) + (uint32_t)f2 * (sl2 - sl1);
     k = f1 * sk1 + f2 * (sk2 - sk1);
   };
-  const uint32_t lcol = (uint32_t)(lane & 7) * 16u;
-  auto stage_ptr = [&](int kt) { return smem + (kt & 1) * G_STAGE; };
-  auto issue1 = [&](int kt, int q) {   // even q: A load q/2, odd q: B load q/2
-    uint8_t* st = stage_ptr(kt);
-    const int j = q >> 1, kb = kt * BK * 2;
-    if ((q & 1) == 0) {
+  auto slot = [&](int i) { return smem + (i % 5) * G_SLOT; };
+  auto issue_half = [&](int i, int j) {   // this wave's load j of half-stage H_i
+    const int kt = kt0 + (i >> 1), kb = kt * BK * 2;
+    uint8_t* dst = slot(i) + (8 * wave + j) * 1024;
+    if ((i & 1) == 0) {
       if constexpr (SEGA) {
         uint64_t b; int n; uint32_t l; int k;
         aseg(kt, b, n, l, k);
-        bload_lds<16>(b, n, st + (8 * wave + j) * G_PITCH, (uint32_t)(lrow + 8 * j) * l + lcol, kb - k);
+        bload_lds<16>(b, n, dst, (uint32_t)drow(j) * l + (uint32_t)dcol(j) * 2u, kb - k);
       } else {
-        bload_lds<16>(bA, nA, st + (8 * wave + j) * G_PITCH, voA + j * stA, kb);
+        bload_lds<16>(bA, nA, dst, (uint32_t)(drow(j) * p.lda + dcol(j)) * 2u, kb);
       }
     } else {
-      bload_lds<16>(bB, nB, st + G_OPB + (8 * wave + j) * G_PITCH, voB + j * stB, kb);
+      bload_lds<16>(bB, nB, dst, (uint32_t)(drow(j) * p.ldb + dcol(j)) * 2u, kb);
     }
-  };
-  auto prefetch = [&](int kt) {   // tile row tid: touch its 128-B line of step kt (A and B)
-    if constexpr (SEGA) {
-      uint64_t b; int n; uint32_t l; int k;
-      aseg(kt, b, n, l, k);
-      bload_lds<4>(b, n, smem + 2 * G_STAGE, (uint32_t)tid * l, kt * BK * 2 - k);
-    } else {
-      bload_lds<4>(bA, nA, smem + 2 * G_STAGE, pfA, kt * BK * 2);
-    }
-    bload_lds<4>(bB, nB, smem + 2 * G_STAGE, pfB, kt * BK * 2);
   };
 
   // ---- fragments ----
-  const int fr = (16 * wm + (lane & 15)) * G_PITCH + ((lane >> 4) & 1) * 128 + (lane >> 5) * 16;
-  const int fc = (16 * wn + (lane & 15)) * G_PITCH + ((lane >> 4) & 1) * 128 + (lane >> 5) * 16;
+  // tile mt of substep ks: block 16*wm + (lane & 15), unit mt, logical position
+  // ((lane >> 4) & 1) * 8 + 2 ks + (lane >> 5)
+  const int fq = (16 * wm + (lane & 15)) * 1024, gq = (16 * wn + (lane & 15)) * 1024;
+  auto fpos = [&](int ks) { return ((((lane >> 4) & 1) * 8 + 2 * ks + (lane >> 5)) ^ (lane & 15)) * 16; };
   struct Frag {
     bf16x8_t a[4], b[4];
   };
-  auto load_frag = [&](Frag& f, const uint8_t* st, int ks) {
+  auto load_frag_at = [&](Frag& f, const uint8_t* sa, const uint8_t* sb, int ks) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) f.a[mt] = *(const bf16x8_t*)(st + fr + mt * 256 + ks * 32);
+    for (int mt = 0; mt < 4; ++mt) f.a[mt] = *(const bf16x8_t*)(sa + fq + mt * 256 + fpos(ks));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) f.b[nt] = *(const bf16x8_t*)(st + G_OPB + fc + nt * 256 + ks * 32);
+    for (int nt = 0; nt < 4; ++nt) f.b[nt] = *(const bf16x8_t*)(sb + gq + nt * 256 + fpos(ks));
   };
+  auto load_frag = [&](Frag& f, int st, int ks) { load_frag_at(f, slot(2 * st), slot(2 * st + 1), ks); };
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -750,66 +750,81 @@ void gemm_bf16_kernel(GemmArgs p) {
   };
 
   // ---- main loop ----
+  // Step s frees the slots of step s-1, so it issues H_2s+3 (B of step s+1,
+  // for s >= 1: the prologue has B of step 1) in its first substep and H_2s+4
+  // (A of step s+2) in its second, then waits for step s+1's A and B; A of
+  // step s+2 may stay in flight (vmcnt retires in order).
+  const int ns = kt1 - kt0, nh = 2 * ns;
+  for (int i = 0; i < 4 && i < nh; ++i) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) issue1(kt0, q);
-  for (int s = 1; s < G_PF; ++s)
-    if (kt0 + s < kt1) prefetch(kt0 + s);
-  wait_vm<0>();
+    for (int j = 0; j < 8; ++j) issue_half(i, j);
+  }
+  if (nh > 2) wait_vm<16>(); else wait_vm<0>();
   ring_barrier();
   Frag f0, f1;
-  load_frag(f0, stage_ptr(kt0), 0);
-  // step kt; PRE: step kt+1 exists (issue its loads and the L2 touch of kt+2)
-  auto step = [&](int kt, auto pre_c) {
-    constexpr bool pre = decltype(pre_c)::value;
-    const uint8_t* st = stage_ptr(kt);
+  load_frag(f0, 0, 0);
+  auto step = [&](int st, auto ib_c, auto ia_c) {
+    constexpr bool iB = decltype(ib_c)::value, iA = decltype(ia_c)::value;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       Frag& cur = (ks & 1) ? f1 : f0;
       Frag& nxt = (ks & 1) ? f0 : f1;
       load_frag(nxt, st, ks + 1);
-      if (pre && ks < 2) {
+      if (ks == 0 && iB) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) issue1(kt + 1, ks * 8 + q);
+        for (int j = 0; j < 8; ++j) issue_half(2 * st + 3, j);
+      }
+      if (ks == 1 && iA) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_half(2 * st + 4, j);
       }
       mma(cur);
-      interleave(8, (pre && ks < 2) ? 8 : 0);
+      interleave(8, ((ks == 0 && iB) || (ks == 1 && iA)) ? 8 : 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (pre) prefetch(min(kt + G_PF, kt1 - 1));   // issued last: vmcnt retires in order
-    if (pre) wait_vm<2>(); else wait_vm<0>();      // step kt+1 landed (the touches may fly)
+    if (st + 1 < ns) {
+      if (iA) wait_vm<8>(); else wait_vm<0>();
+    }
     ring_barrier();
-    if (kt + 1 < kt1) load_frag(f0, stage_ptr(kt + 1), 0);
+    if (st + 1 < ns) load_frag(f0, st + 1, 0);
     mma(f1);
     interleave(8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  int kt = kt0;
-  for (; kt + 1 < kt1; ++kt) step(kt, std::integral_constant<bool, true>());
-  step(kt, std::integral_constant<bool, false>());
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  if (ns >= 3) {
+    step(0, F_(), T_());
+    for (int st = 1; st < ns - 2; ++st) step(st, T_(), T_());
+    step(ns - 2, T_(), F_());
+    step(ns - 1, F_(), F_());
+  } else {
+    for (int st = 0; st < ns; ++st) step(st, F_(), F_());
+  }
   wait_vm<0>();
   __syncthreads();
 
-  // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be;
-  // columns at or past KE read as zeros; split 0 only ----
+  // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be in
+  // slots 0 and 1, same layout; columns at or past KE read as zeros; split 0
+  // only ----
   if (p.KE > 0 && ksp == 0) {
     const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
     const int neA = rec_bytes(rowsA, p.ldae);
     const int neB = rec_bytes(rowsB, p.ldbe);
     for (int e = 0; e * BK < p.KE; ++e) {
-      const int c = e * BK + (lane & 7) * 8;   // this lane's first column
-      const bool in = c < p.KE;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int row = lrow + 8 * j;
-        bload_lds<16>(eA, neA, smem + (8 * wave + j) * G_PITCH, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
-        bload_lds<16>(eB, neB, smem + G_OPB + (8 * wave + j) * G_PITCH, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
+        const int row = drow(j), c = e * BK + dcol(j);   // c < KE covers all 8 columns (KE % 16 == 0)
+        const bool in = c < p.KE;
+        bload_lds<16>(eA, neA, slot(0) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
+        bload_lds<16>(eB, neB, slot(1) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
       }
       wait_vm<0>();
       ring_barrier();
       const int nsub = (min(BK, p.KE - e * BK) + 15) >> 4;
       for (int ks = 0; ks < nsub; ++ks) {
         Frag f;
-        load_frag(f, smem, ks);
+        load_frag_at(f, slot(0), slot(1), ks);
         mma(f);
       }
       __syncthreads();
