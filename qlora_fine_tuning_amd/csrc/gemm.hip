@@ -751,9 +751,10 @@ void gemm_bf16_kernel(GemmArgs p) {
 
   // ---- main loop ----
   // Step s frees the slots of step s-1, so it issues H_2s+3 (B of step s+1,
-  // for s >= 1: the prologue has B of step 1) in its first substep and H_2s+4
-  // (A of step s+2) in its second, then waits for step s+1's A and B; A of
-  // step s+2 may stay in flight (vmcnt retires in order).
+  // for s >= 1: the prologue has B of step 1) over its first two substeps and
+  // H_2s+4 (A of step s+2) over its second and third, then waits for step
+  // s+1's A and B; A of step s+2, issued last, may stay in flight (vmcnt
+  // retires in order).
   const int ns = kt1 - kt0, nh = 2 * ns;
   for (int i = 0; i < 4 && i < nh; ++i) {
 #pragma unroll
@@ -770,16 +771,22 @@ void gemm_bf16_kernel(GemmArgs p) {
       Frag& cur = (ks & 1) ? f1 : f0;
       Frag& nxt = (ks & 1) ? f0 : f1;
       load_frag(nxt, st, ks + 1);
-      if (ks == 0 && iB) {
+      // B of step st+1: loads 0-5 in substep 0, 6-7 in substep 1; A of step
+      // st+2: loads 0-1 in substep 1, 2-7 in substep 2 (spread, B first)
+      const int b0 = ks == 0 ? 0 : (ks == 1 ? 6 : 8), b1 = ks == 0 ? 6 : 8;
+      const int a0 = ks == 1 ? 0 : (ks == 2 ? 2 : 8), a1 = ks == 1 ? 2 : (ks == 2 ? 8 : 0);
+      if (iB) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) issue_half(2 * st + 3, j);
+        for (int j = 0; j < 8; ++j)
+          if (j >= b0 && j < b1) issue_half(2 * st + 3, j);
       }
-      if (ks == 1 && iA) {
+      if (iA) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) issue_half(2 * st + 4, j);
+        for (int j = 0; j < 8; ++j)
+          if (j >= a0 && j < a1) issue_half(2 * st + 4, j);
       }
       mma(cur);
-      interleave(8, ((ks == 0 && iB) || (ks == 1 && iA)) ? 8 : 0);
+      interleave(8, (iB ? b1 - b0 : 0) + (iA && a1 > a0 ? a1 - a0 : 0));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (st + 1 < ns) {
