@@ -14,15 +14,16 @@
 // gemm_bf16_kernel (B in bf16: a staged dequant, or 16-bit base weights):
 // 256 x 256 output tile per workgroup of 4 waves (one per SIMD) laid out
 // 2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32
-// accumulators per lane). K is walked in 64-wide steps through a 2-deep LDS
-// ring filled by buffer loads straight into LDS (one buffer resource per
-// operand tile, so rows past M or N read as zeros). Each 8-row, 1 KB load
-// block sits at a 1040-byte pitch, which makes the ds_read_b128 fragment
-// reads conflict-free; the MFMA row order is permuted to match and undone in
-// the epilogue. Fragments of the next substep are read while the matrix
-// cores work on the current one, and sched_group_barrier hints interleave
-// the LDS reads and load issues with the MFMAs. Each step also touches the
-// tile's lines two steps ahead with 4-byte loads, so the next DMA hits L2.
+// accumulators per lane). K is walked in 64-wide steps. Operands reach LDS
+// through buffer loads straight into LDS (one buffer resource per operand
+// tile, so rows past M or N read as zeros), into a ring of five 32 KB
+// half-stage slots (one operand of one step each): while a step reads two
+// slots, the next step and a half are in flight. The 1 KB load blocks are
+// unpadded and XOR-swizzled so that the ds_read_b128 fragment reads stay
+// conflict-free; the MFMA row order is permuted to match and undone in the
+// epilogue. Fragments of the next substep are read while the matrix cores
+// work on the current one, and sched_group_barrier hints interleave the LDS
+// reads and load issues with the MFMAs.
 // Optional extras: A split along K into up to three matrices (dX = sum of
 // dY_p W_p over separately stored dY_p), and an epilogue that writes column
 // ranges to three outputs (q, k, v from one GEMM).
@@ -566,18 +567,19 @@ void gemm_nt_kernel(GemmArgs p) {
 // Operand feed: buffer loads straight into LDS (buffer_load_dwordx4 ... lds),
 // through a buffer resource per tile whose size ends at the matrix end, so
 // rows past M (N) read as zeros without per-row clamps. One load instruction
-// moves 8 rows x 128 B in global order (full 128-byte lines); consecutive
-// 1 KB blocks sit at a 1040-byte pitch, and the MFMA lanes read rows in the
-// order below, which makes every 16-lane phase of a ds_read_b128 hit 16
-// different bank groups:
+// fills a 1 KB block with 8 rows x 128 B (full 128-byte lines). Blocks are
+// unpadded; inside each 256-byte unit of block q, 16-byte position p holds
+// logical position p ^ (q & 15). The MFMA lanes read rows in the order below,
+// so the 16 lanes of a ds_read_b128 phase read 16 consecutive blocks and hit
+// 16 different bank groups:
 //   MFMA row i (0..31) of tile t of wave w reads tile row
 //   8 * (16 * w + (i & 15)) + 2 * t + (i >> 4)          (A; B likewise).
 // The epilogue undoes this permutation.
 //
-// Pipeline per 64-wide k-step (2 LDS stages): the loads of step k+1 are
-// issued during the first half of step k, interleaved with its MFMAs; one
-// 4-byte touch per tile row pulls the lines of step k+2 into L2 so that the
-// step-(k+1) loads mostly hit; one barrier per step.
+// Pipeline per 64-wide k-step: a ring of five half-stage slots (A or B of one
+// step each). Step s reads two slots; over its first three substeps it issues
+// B of step s+1 and A of step s+2 into the two slots freed by step s-1, then
+// waits for step s+1's halves only; one barrier per step.
 // ===========================================================================
 namespace {
 constexpr int G_SLOT = 32768;           // one operand (256 rows x 64 bf16) of one k-step
