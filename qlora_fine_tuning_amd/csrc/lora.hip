@@ -154,6 +154,23 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
 
 // U = sum of the split partials (fixed order); writes fp32 U (split across
 // two outputs at column `split`) and the bf16 K-extension operand.
+// sum_{q < n} p[q * stride], added in order q = 0, 1, ... (the same bits as
+// a plain loop); the loads are issued 8 at a time so that their latencies
+// overlap instead of following one another.
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_t stride, int n) {
+  float sum = 0.0f;
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; q < n; ++q) sum += p[(int64_t)q * stride];
+  return sum;
+}
+
 __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restrict__ part,
                                                             int nsplit, int M, int R, float s,
                                                             float* __restrict__ Uf,
@@ -165,8 +182,7 @@ __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restr
   if (e >= (int64_t)M * W) return;
   const int i = (int)(e / W), j = (int)(e - (int64_t)i * W);
   if (j < R) {
-    float sum = 0.0f;
-    for (int q = 0; q < nsplit; ++q) sum += part[((int64_t)q * M + i) * R + j];
+    const float sum = ordered_sum(part + (int64_t)i * R + j, (int64_t)M * R, nsplit);
     if (j < split) {
       if (Uf) Uf[(int64_t)i * ldu + j] = sum;
     } else if (Uf2) {
@@ -385,8 +401,7 @@ __global__ __launch_bounds__(256) void colreduce_finish_kernel(const float* __re
   if (e >= (int64_t)C * nj) return;
   const int col = (int)(e / nj);
   const int jj = (int)(e - (int64_t)col * nj);
-  float sum = 0.0f;
-  for (int ch = 0; ch < chunks; ++ch) sum += part[((int64_t)ch * C + col) * R + j0 + jj];
+  const float sum = ordered_sum(part + (int64_t)col * R + j0 + jj, (int64_t)C * R, chunks);
   out[(int64_t)col * ocs + (int64_t)jj * ojs] = (uint16_t)f32_to_bf16(s * sum);
 }
 
