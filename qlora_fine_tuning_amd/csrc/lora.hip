@@ -152,8 +152,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
     }
 }
 
-// U = sum of the split partials (fixed order); writes fp32 U (split across
-// two outputs at column `split`) and the bf16 K-extension operand.
 // sum_{q < n} p[q * stride], added in order q = 0, 1, ... (the same bits as
 // a plain loop); the loads are issued 8 at a time so that their latencies
 // overlap instead of following one another.
@@ -171,6 +169,8 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_
   return sum;
 }
 
+// U = sum of the split partials (fixed order); writes fp32 U (split across
+// two outputs at column `split`) and the bf16 K-extension operand.
 __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restrict__ part,
                                                             int nsplit, int M, int R, float s,
                                                             float* __restrict__ Uf,
