@@ -75,7 +75,11 @@ constexpr int B_BYTES = BN * BK * 2;
 constexpr int C_BYTES = 8192;
 constexpr int S_BYTES = 2048;
 constexpr int STAGE_BF16 = A_BYTES + B_BYTES;
-constexpr int STAGE_NF4 = A_BYTES + B_BYTES + C_BYTES + S_BYTES;
+// NF4 modes: the raw codes and absmax of a k-step (C_BYTES + S_BYTES) have a
+// ring of their own, 3 deep, so that they are fetched two steps ahead: they
+// are needed in the middle of the step before theirs (for the dequant).
+constexpr int RAW_BYTES = C_BYTES + S_BYTES;
+constexpr int NRAW = 3;
 
 // element offset of (row, 16-byte chunk) in a [rows][64] bf16 LDS tile
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -146,9 +150,10 @@ template <int BSRC, int EPI>
 __global__ __launch_bounds__(NTHR)
 void gemm_nt_kernel(GemmArgs p) {
   constexpr bool NF4 = BSRC != BSRC_BF16;
-  constexpr int STAGE = NF4 ? STAGE_NF4 : STAGE_BF16;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE + (NF4 ? 64 : 0)];
-  float* lut = reinterpret_cast<float*>(smem + NSTAGE * STAGE);  // NF4 only
+  constexpr int STAGE = STAGE_BF16;
+  constexpr int RAW = NF4 ? NRAW * RAW_BYTES : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE + RAW + (NF4 ? 64 : 0)];
+  float* lut = reinterpret_cast<float*>(smem + NSTAGE * STAGE + RAW);  // NF4 only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -247,22 +252,24 @@ void gemm_nt_kernel(GemmArgs p) {
   }
 
   auto stage_ptr = [&](int kt) { return smem + (kt % NSTAGE) * STAGE; };
-  // NF4 issue order: codes, absmax, then A, so that waiting for a step's
-  // codes leaves its A loads in flight (vmcnt counts in order).
+  auto raw_ptr = [&](int kt) { return smem + NSTAGE * STAGE + (kt % NRAW) * RAW_BYTES; };
+  // NF4: codes and absmax of step kt into its raw slot (2 loads per wave)
+  auto issue_raw = [&](int kt) {
+    uint8_t* rw = raw_ptr(kt);
+    const uint8_t* c = srcC;
+    const float* sc = srcS;
+    int kl = kt;
+    if (BSRC == BSRC_NF4_T && p.ksplit > 0 && kt * BK >= p.ksplit) {
+      c = srcC1;
+      sc = srcS1;
+      kl = kt - p.ksplit / BK;
+    }
+    dma16(c + kl * cstep, rw + wave * 1024);
+    dma4(sc + kl * sstep, rw + C_BYTES + wave * 256);
+  };
+  // the bf16 operands of step kt (A; B too when it is not NF4): 4 or 8 loads per wave
   auto issue = [&](int kt) {
     uint8_t* st = stage_ptr(kt);
-    if (NF4) {
-      const uint8_t* c = srcC;
-      const float* sc = srcS;
-      int kl = kt;
-      if (BSRC == BSRC_NF4_T && p.ksplit > 0 && kt * BK >= p.ksplit) {
-        c = srcC1;
-        sc = srcS1;
-        kl = kt - p.ksplit / BK;
-      }
-      dma16(c + kl * cstep, st + A_BYTES + B_BYTES + wave * 1024);
-      dma4(sc + kl * sstep, st + A_BYTES + B_BYTES + C_BYTES + wave * 256);
-    }
     const int k0 = kt * BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma16(srcA[j] + k0, st + (wave * 4 + j) * 1024);
@@ -271,14 +278,12 @@ void gemm_nt_kernel(GemmArgs p) {
       for (int j = 0; j < 4; ++j) dma16(srcB[j] + k0, st + A_BYTES + (wave * 4 + j) * 1024);
     }
   };
-  constexpr int L = NF4 ? 6 : 8;   // loads per wave per k-step
-  constexpr int LA = 4;            // the A loads among them (issued last)
 
   // NF4: dequantize the raw codes of a landed k-step into its bf16 B tile.
   auto dequant_stage = [&](int kt) {
     uint8_t* st = stage_ptr(kt);
-    const uint8_t* cb = st + A_BYTES + B_BYTES;
-    const float* sb = (const float*)(st + A_BYTES + B_BYTES + C_BYTES);
+    const uint8_t* cb = raw_ptr(kt);
+    const float* sb = (const float*)(raw_ptr(kt) + C_BYTES);
     uint16_t* bt = (uint16_t*)(st + A_BYTES);
     if (BSRC != BSRC_NF4_T) {
       // thread t: tile row t/2, 32 weights (k half t&1) = chunks 4*(t&1) .. +3
@@ -356,20 +361,32 @@ void gemm_nt_kernel(GemmArgs p) {
   // them; the MFMAs of step kt run meanwhile, with the fragments of the next
   // substep (and, across the barrier, of step kt+1's first substep) loaded
   // ahead. The closing barrier publishes step kt+1 and retires step kt.
-  issue(0);
-  wait_vm<0>();
+  // NF4 issue order inside step kt: A of kt+1 (4 loads), then codes and
+  // absmax of kt+2 (2 loads). Mid-step the codes of kt+1 (issued a step
+  // earlier, older than both) must have landed: wait_vm<4 + 2>; at the end
+  // A of kt+1 must have: wait_vm<2> (the codes of kt+2 may still fly).
+  if (NF4) {
+    issue_raw(0);
+    issue(0);
+    if (nk > 1) issue_raw(1);
+    if (nk > 1) wait_vm<2>(); else wait_vm<0>();
+  } else {
+    issue(0);
+    wait_vm<0>();
+  }
   ring_barrier();   // step 0 raw data (and lut) visible
   if (NF4) {
     dequant_stage(0);
-    wait_vm<0>();
+    if (nk > 1) wait_vm<2>(); else wait_vm<0>();   // its LDS stores done (codes of step 1 may fly)
     ring_barrier();
   }
   Frag f0, f1;
   load_frag(f0, stage_ptr(0), 0);
-  wait_vm<0>();
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
+    const bool more2 = kt + 2 < nk;
     if (more) issue(kt + 1);
+    if (NF4 && more2) issue_raw(kt + 2);
     const uint8_t* st = stage_ptr(kt);
     load_frag(f1, st, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -380,7 +397,7 @@ void gemm_nt_kernel(GemmArgs p) {
     mma(f1);
     __builtin_amdgcn_sched_barrier(0);
     if (NF4 && more) {
-      wait_vm<LA>();   // codes + absmax of step kt+1 landed (A may still fly)
+      if (more2) wait_vm<6>(); else wait_vm<4>();   // codes + absmax of step kt+1 landed
       ring_barrier();  // ... for every wave
       dequant_stage(kt + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -389,7 +406,8 @@ void gemm_nt_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<0>();      // step kt+1 landed; all LDS traffic of this wave done
+    if (NF4 && more2) wait_vm<2>();   // step kt+1 landed (codes of kt+2 may fly); LDS done
+    else wait_vm<0>();
     ring_barrier();
     load_frag(f0, stage_ptr(more ? kt + 1 : kt), 0);
     __builtin_amdgcn_sched_barrier(0);
