@@ -104,7 +104,8 @@ SMALL = [I.QkvCfg("one_ext", 300, 192, 256, 128, 64, 8, 2.0, 1.0),      # 3r <= 
          I.QkvCfg("padded_r22", 77, 64, 64, 64, 64, 22, 1.0, 1.0),    # KE 144 > 6r
          I.QkvCfg("padded_r4", 65, 128, 128, 64, 64, 4, 4.0, 1.0),     # KE 32 > 6r
          I.QkvCfg("r64", 40, 64, 64, 64, 128, 64, 0.25, 1.0),
-         I.QkvCfg("one_token", 1, 64, 64, 64, 64, 1, 1.0, 1.0)]
+         I.QkvCfg("one_token", 1, 64, 64, 64, 64, 1, 1.0, 1.0),
+         I.QkvCfg("ragged_r16", 77, 128, 128, 256, 128, 16, 1.0, 1.0)]
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
