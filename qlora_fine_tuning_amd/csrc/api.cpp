@@ -645,7 +645,10 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
   const float s = w->s;
 
-  // LoRA operand layouts
+  // LoRA operand layouts (launched below: on the helper stream when staged,
+  // ahead of the row product there, so the caller's stream starts with the
+  // dequant; every reader of these layouts waits for the helper stream)
+  PrepJobs fwd_jobs;
   {  // Lgu = [Ag; Au]; Bext_gu rows interleaved by 32 (gate: [Bg 0 Bg 0 0..],
      // up: [0 Bu 0 Bu 0..]); Bext_d = [Bd | Bd | 0]
     PrepJobs J;
@@ -663,7 +666,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
     J.copy(w->b_down, r, 1, d, r, t.bextd, KEd, 1);
     J.copy(w->b_down, r, 1, d, r, t.bextd + r, KEd, 1);
     J.zero(d, KEd - 2 * r, t.bextd + 2 * r, KEd, 1);
-    QL_TRY(launch_prep(J, st), "mlp_fwd: LoRA layouts");
+    fwd_jobs = J;
   }
   // staged: the caller's stream writes the gate/up weight that the first GEMM
   // needs, while the helper stream does the row product [Ug | Uu] and then the
@@ -680,6 +683,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
     QL_TRY(side.open(), "mlp_fwd: helper stream");
     QL_TRY(side.fork(0), "mlp_fwd: fork");
     hipStream_t ss = side.stream();
+    QL_TRY(launch_prep(fwd_jobs, ss), "mlp_fwd: LoRA layouts");
     QL_TRY(row_u(ss), "mlp_fwd: Ug, Uu");
     QL_TRY(side.mark(1), "mlp_fwd: mark");
     if (w16) {   // 16-bit base: interleave copy of gate/up; down is used as it is
@@ -692,6 +696,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
     }
     QL_TRY(side.mark(2), "mlp_fwd: mark");
   } else {
+    QL_TRY(launch_prep(fwd_jobs, st), "mlp_fwd: LoRA layouts");
     QL_TRY(row_u(st), "mlp_fwd: Ug, Uu");
   }
   // gate || up GEMM with the activation epilogue
@@ -758,7 +763,9 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   const int chunks = colreduce_chunks((int)m);
   const float s = w->s;
 
-  // LoRA operand layouts
+  // LoRA operand layouts (launched below: on the helper stream when staged,
+  // ahead of Td there; every reader waits for the helper stream)
+  PrepJobs bwd_jobs;
   {  // ltd = Bd^T; bextdh = [Ad^T | Ad^T | 0]; ltgu = blockdiag(Bg^T, Bu^T);
      // bextdx = [Ag^T | Au^T | Ag^T | Au^T | 0]
     PrepJobs J;
@@ -775,7 +782,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     J.copy(w->a_gate, 1, d, d, r, t.bextdx + 2 * r, KEgu, 1);
     J.copy(w->a_up, 1, d, d, r, t.bextdx + 3 * r, KEgu, 1);
     J.zero(d, KEgu - 4 * r, t.bextdx + 4 * r, KEgu, 1);
-    QL_TRY(launch_prep(J, st), "mlp_bwd: LoRA layouts");
+    bwd_jobs = J;
   }
   // The column reductions (dB, dA) and the transposed dequant of the gate/up
   // weights run on the helper stream, overlapping the row products and the two
@@ -786,7 +793,9 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   Side side(st);
   QL_TRY(side.open(), "mlp_bwd: helper stream");
   hipStream_t ss = side.stream();
+  if (!staged) QL_TRY(launch_prep(bwd_jobs, st), "mlp_bwd: LoRA layouts");
   QL_TRY(side.fork(0), "mlp_bwd: fork");
+  if (staged) QL_TRY(launch_prep(bwd_jobs, ss), "mlp_bwd: LoRA layouts");
   // Td = dY Bd: on the helper stream beside the caller's W_d^T when staged
   auto row_td = [&](hipStream_t q) {
     return launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
