@@ -12,6 +12,8 @@
 //                -> Ud = H Ad^T -> down GEMM
 //   MLP bwd    : Td = dY Bd, dBd -> dH GEMM with act' epilogue (dg, du) -> dAd (H recomputed)
 //                -> [Tg|Tu] = [dg|du] blockdiag(Bg,Bu), dBg, dBu -> dX GEMM (K = 2h) -> dAg, dAu
+//   (with a bf16 weight and r <= 16, Ud and [Tg|Tu] are formed in the epilogues
+//   that write H and dg, du, as per-wave partials, and only summed afterwards)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -82,6 +84,12 @@ WSrc src_w16(const uint16_t* w, int64_t n, int64_t k) {
 bool bad_src(const WSrc& w, int mode) { return mode == MODE_BF16 ? !w.w16 : (!w.codes || !w.absmax); }
 // a bf16 copy of the weight (or of its transpose) lives in the workspace
 bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE_BF16; }
+
+// The MLP's two row products over h-wide activations (Ud = H Ad^T and
+// [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)) come from the epilogues of the
+// GEMMs that write those activations when the GEMM reads a bf16 weight and
+// r <= 16; otherwise a separate pass reads the activations back.
+bool rp_epilogue(int mode, int64_t r) { return staged_like(mode) && r <= 16; }
 
 int resolve_mode(int mode) {
   if (mode == QLORA_DEQUANT_AUTO) return QLORA_DEQUANT_STAGED;
@@ -177,7 +185,7 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.H = c.take<uint16_t>(m * h);
   t.wgu = staged_like(mode) ? c.take<uint16_t>(2 * h * d) : nullptr;
   t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
-  t.rpart = c.take<float>(16 * m * 2 * r);
+  t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(mode, r) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
   t.kpart = c.take<float>(splitk_elems(m, d, h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
@@ -216,7 +224,7 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
   t.wdt = staged_like(mode) ? c.take<uint16_t>(h * d) : nullptr;
   t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
-  t.rpart = c.take<float>(16 * m * 2 * r);
+  t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(mode, r) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
   t.kpart = c.take<float>(splitk_elems(m, d, 2 * h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
@@ -711,12 +719,19 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   g.Ae = t.uextgu; g.ldae = KEgu; g.Be = t.bextgu; g.ldbe = KEgu;
   g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
   g.epi = EPI_GATEUP; g.g_out = g_save; g.u_out = u_save; g.h_out = t.H; g.hdim = h; g.act = w->act;
+  // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
+  const bool rp = rp_epilogue(mode, r);
+  if (rp) { g.rp_l = w->a_down; g.rp_ldl = h; g.rp_r = (int)r; g.rp_part = t.rpart; }
   if (staged) QL_TRY(side.wait(1), "mlp_fwd: wait");
   QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
-  // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
-  QL_TRY(launch_rowdot(t.H, h, w->a_down, h, (int)m, (int)h, (int)r, s, Ud, nullptr, (int)r, r,
-                       t.uextd, KEd, KEd, t.rpart, st),
-         "mlp_fwd: Ud");
+  if (rp)
+    QL_TRY(launch_rowdot_finish(t.rpart, gemm_rowprod_splits((int)(2 * h)), (int)m, (int)r, s, Ud,
+                                nullptr, (int)r, r, t.uextd, KEd, KEd, st),
+           "mlp_fwd: Ud");
+  else
+    QL_TRY(launch_rowdot(t.H, h, w->a_down, h, (int)m, (int)h, (int)r, s, Ud, nullptr, (int)r, r,
+                         t.uextd, KEd, KEd, t.rpart, st),
+           "mlp_fwd: Ud");
   GemmArgs g2 = gemm_args();
   g2.A = t.H; g2.lda = h;
   if (w16) { g2.bsrc = BSRC_BF16; g2.B = w->down.w16; g2.ldb = h; }
@@ -847,6 +862,12 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   g.Ae = t.textd; g.ldae = KEd; g.Be = t.bextdh; g.ldbe = KEd;
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
+  // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu): in the epilogue, or below
+  const bool rp = rp_epilogue(mode, r);
+  if (rp) {
+    g.rp_l = t.ltgu; g.rp_l2 = t.ltgu + r * 2 * h + h; g.rp_ldl = 2 * h;
+    g.rp_r = (int)r; g.rp_part = t.rpart;
+  }
   QL_TRY(run_gemm(g, r, st), "mlp_bwd: dH GEMM");
   QL_TRY(side.fork(3), "mlp_bwd: fork");
   // dBg = s dg^T Ug ; dBu = s du^T Uu (helper stream)
@@ -859,10 +880,14 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
          "mlp_bwd: dBu partials");
   QL_TRY(launch_colreduce_finish(t.part, chunks, (int)h, (int)r, 0, (int)r, s, gr->b_up, r, 1, ss),
          "mlp_bwd: dBu");
-  // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)
-  QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s, t.tgu,
-                       nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
-         "mlp_bwd: Tg, Tu");
+  if (rp)
+    QL_TRY(launch_rowdot_finish(t.rpart, gemm_rowprod_splits((int)h), (int)m, (int)(2 * r), s,
+                                t.tgu, nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, st),
+           "mlp_bwd: Tg, Tu");
+  else
+    QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s,
+                         t.tgu, nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
+           "mlp_bwd: Tg, Tu");
   QL_TRY(side.fork(4), "mlp_bwd: fork");
   // dAg = s Tg^T X ; dAu = s Tu^T X (helper stream, beside the dX GEMM)
   QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),

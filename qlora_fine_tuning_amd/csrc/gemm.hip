@@ -828,8 +828,48 @@ void gemm_bf16_kernel(GemmArgs p) {
   } else {
     for (int st = 0; st < ns; ++st) step(st, F_(), F_());
   }
+  // GATEUP row product: the rank-r fragments of the wave's 64 H columns,
+  // loaded here so that the wait below covers them. Waited for later, behind
+  // the epilogue's conditional stores, they would cost a wait for all of those.
+  const bool rp_on = (EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.rp_r > 0;
+  bf16x8_t rpb[2];
+  if (EPI == EPI_GATEUP && rp_on) {
+    const int jr = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int64_t c = (int64_t)((n0 + wn * 128) >> 1) + 32 * kc + 8 * kq;
+      rpb[kc] = bf16x8_t{};
+      if (jr < p.rp_r && c < p.hdim) rpb[kc] = *(const bf16x8_t*)(p.rp_l + (int64_t)jr * p.rp_ldl + c);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   __syncthreads();
+
+  // ACT_BWD row product: the rank-r operand over the tile's 256 columns
+  // (gate rows 0-15, then up rows 16-31: 32 x 256 bf16) is brought by DMA
+  // into the end of the last ring slot, which nothing else uses from here on;
+  // the wait of the K-extension (or the one before the epilogue) covers it,
+  // so the epilogue reads it from LDS. Row i keeps logical 16-byte chunk c at
+  // physical chunk c ^ (i & 15) of its 512 bytes: the 16 rows of a fragment
+  // read hit 16 different bank groups. Rows j >= rp_r and columns at or past
+  // hdim load as zeros.
+  constexpr int RPL_OFF = 5 * G_SLOT - 16384;
+  if (EPI == EPI_ACT_BWD && rp_on) {
+    const int up = wave >= 2;   // waves 0, 1: gate rows; 2, 3: up rows
+    const uint64_t base = (uint64_t)(up ? p.rp_l2 : p.rp_l);
+    const int nrec = rec_bytes(p.rp_r, p.rp_ldl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int inst = 4 * wave + q;
+      const int i = 2 * inst + (lane >> 5), j = i & 15;
+      const int c = (lane & 31) ^ j;
+      const int64_t col = n0 + 8 * c;
+      const bool in = j < p.rp_r && col < p.hdim;
+      bload_lds<16>(base, nrec, smem + RPL_OFF + inst * 1024,
+                    in ? (uint32_t)((int64_t)j * p.rp_ldl + col) * 2u : OOB, 0);
+    }
+  }
 
   // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be in
   // slots 0 and 1, same layout; columns at or past KE read as zeros; split 0
@@ -858,6 +898,11 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
   }
 
+  if (EPI == EPI_ACT_BWD && rp_on) {
+    wait_vm<0>();
+    __syncthreads();
+  }
+
   // ---- epilogue ----
   // acc[mt][nt][v]: MFMA row r = 8*(v/4) + 4*(lane/32) + v%4, col j = lane%32, i.e.
   // tile row wm*128 + 8*(r&15) + 2*mt + (r>>4), tile col wn*128 + 8*(j&15) + 2*nt + (j>>4).
@@ -866,6 +911,61 @@ void gemm_bf16_kernel(GemmArgs p) {
   constexpr int SP = 132;  // floats per staged row
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
   const int col0 = n0 + wn * 128;
+  // Row product (rp_r > 0): the slab's bf16 results (GATEUP: H, 32 x 64; ACT_BWD:
+  // dg and du, 32 x 128 each) are also written to a panel of this wave's own
+  // after the staging regions, with a 16-byte-odd row pitch so that the 16
+  // rows of a fragment read hit 16 different bank groups, then multiplied by
+  // the rank-r operand on MFMA 16x16x32.
+  constexpr int RPP = EPI == EPI_GATEUP ? 72 : 136;           // bf16 per panel row
+  constexpr int RPW = EPI == EPI_GATEUP ? 32 * RPP : 2 * 32 * RPP;
+  uint16_t* rpan = reinterpret_cast<uint16_t*>(smem + 4 * 32 * SP * 4) + wave * RPW;
+  // ACT_BWD: the rank-r fragments of this wave's 128 columns from the LDS
+  // copy (half 0: gate rows, 1: up rows); lane (i = lane % 16, q = lane / 16)
+  // gets row i, columns 32 kc + 8 q of the wave's range
+  auto lds_frags = [&](bf16x8_t* b, int half) {
+    const int jr = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int c = wn * 16 + 4 * kc + kq;
+      b[kc] = *(const bf16x8_t*)(smem + RPL_OFF + (16 * half + jr) * 512 + ((c ^ jr) << 4));
+    }
+  };
+  // sum_c L[j][c] panel[s][c] over the wave's panel columns for the 32 panel
+  // rows, as D[j][s] (L as the row operand), stored to this wave's split at
+  // columns jofs + j (j < rp_r): a lane holds 4 consecutive j of one row.
+  auto rowprod = [&](const uint16_t* pan, auto nkc_c, const bf16x8_t* b, int jofs, auto&& growf) {
+    constexpr int NKC = decltype(nkc_c)::value;
+    const int sr = lane & 15, kq = lane >> 4;
+    f32x4_t d[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      d[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const bf16x8_t a = *(const bf16x8_t*)(pan + (16 * rg + sr) * RPP + 32 * kc + 8 * kq);
+        d[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kc], a, d[rg], 0, 0, 0);
+      }
+    }
+    // d[rg][v] = D[j = 4 kq + v][panel row 16 rg + sr]
+    const int rw = EPI == EPI_GATEUP ? p.rp_r : 2 * p.rp_r;
+    const int j0 = 4 * kq;
+    float* out = p.rp_part + (int64_t)(2 * tn + wn) * p.M * rw + jofs + j0;
+    const bool vec = ((jofs | rw) & 3) == 0 && j0 + 4 <= p.rp_r;
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int row = growf(16 * rg + sr);
+      if (row >= p.M || j0 >= p.rp_r) continue;
+      float* o = out + (int64_t)row * rw;
+      if (vec) {
+        *(f32x4_t*)o = d[rg];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (j0 + v < p.rp_r) o[v] = d[rg][v];
+      }
+    }
+  };
+
   // one slab per call; mt is a compile-time constant so that acc stays in registers
   auto slab = [&](auto mt_c, auto act_c) {
     constexpr int mt = decltype(mt_c)::value;
@@ -902,6 +1002,7 @@ void gemm_bf16_kernel(GemmArgs p) {
       for (int q = 0; q < 8; ++q) {
         const int s = q * 4 + (lane >> 4);
         const int row = grow(s), col = col0 + cc;
+        u32x4_t odg = u32x4_t{0u, 0u, 0u, 0u}, odu = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col < p.N) {
           const float* x = &stage[s * SP + cc];
           if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1) {   // fp32 partial
@@ -925,7 +1026,6 @@ void gemm_bf16_kernel(GemmArgs p) {
             *(u32x4_t*)dst = o;
           } else {  // staged values are dH
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
-            u32x4_t odg, odu;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float dg[2], du[2];
@@ -947,6 +1047,18 @@ void gemm_bf16_kernel(GemmArgs p) {
             *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
           }
         }
+        if (EPI == EPI_ACT_BWD && rp_on) {   // zeros outside the output
+          *(u32x4_t*)(rpan + s * RPP + cc) = odg;
+          *(u32x4_t*)(rpan + (32 + s) * RPP + cc) = odu;
+        }
+      }
+      if (EPI == EPI_ACT_BWD && rp_on) {
+        wave_sync();
+        bf16x8_t lb[4];
+        lds_frags(lb, 0);
+        rowprod(rpan, std::integral_constant<int, 4>(), lb, 0, grow);
+        lds_frags(lb, 1);
+        rowprod(rpan + 32 * RPP, std::integral_constant<int, 4>(), lb, p.rp_r, grow);
       }
     } else {  // EPI_GATEUP: staged columns [gate j0..+31 | up j0..+31 | gate j0+32.. | up j0+32..]
       const int jj = (lane & 7) * 8;                       // 0..56: output index within 64
@@ -956,6 +1068,7 @@ void gemm_bf16_kernel(GemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int s = q * 8 + (lane >> 3);
         const int row = grow(s);
+        u32x4_t oh = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col0 < p.N) {
           const float* gs = &stage[s * SP + gcol];
           const float* us = gs + 32;
@@ -964,7 +1077,7 @@ void gemm_bf16_kernel(GemmArgs p) {
           *(f32x4_t*)(gv + 4) = *(const f32x4_t*)(gs + 4);
           *(f32x4_t*)uv = *(const f32x4_t*)us;
           *(f32x4_t*)(uv + 4) = *(const f32x4_t*)(us + 4);
-          u32x4_t og, ou, oh;
+          u32x4_t og, ou;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float hv[2];
@@ -984,6 +1097,11 @@ void gemm_bf16_kernel(GemmArgs p) {
           *(u32x4_t*)(p.u_out + o) = ou;
           *(u32x4_t*)(p.h_out + o) = oh;
         }
+        if (rp_on) *(u32x4_t*)(rpan + s * RPP + jj) = oh;   // zeros outside the output
+      }
+      if (rp_on) {
+        wave_sync();
+        rowprod(rpan, std::integral_constant<int, 2>(), rpb, 0, grow);
       }
     }
     wave_sync();
@@ -1056,6 +1174,8 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
   }
   return hipGetLastError();
 }
+
+int gemm_rowprod_splits(int N) { return 2 * ((N + BN - 1) / BN); }
 
 int gemm_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);

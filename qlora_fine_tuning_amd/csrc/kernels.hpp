@@ -98,6 +98,20 @@ struct GemmArgs {
   uint16_t* dgu;
   int64_t hdim;
   int act;
+  // row product in the GATEUP / ACT_BWD epilogues (gemm_bf16_kernel only):
+  // with rp_r in 1..16, each wave multiplies the bf16 values it writes (H;
+  // dg and du) by a rank-r operand over its own columns and stores an fp32
+  // partial part[2 * tile_col + wave_col][row][j]; gemm_rowprod_splits(N)
+  // partials per row, summed by launch_rowdot_finish.
+  //   GATEUP:  j < r: sum_c H[row][c] rp_l[j][c]                  (width r)
+  //   ACT_BWD: j < r: sum_c dg[row][c] rp_l[j][c]; r + j: sum_c du[row][c]
+  //            rp_l2[j][c]                                        (width 2r)
+  // rp_l, rp_l2: bf16 with row pitch rp_ldl; c runs over [0, hdim).
+  const uint16_t* rp_l;
+  const uint16_t* rp_l2;
+  int64_t rp_ldl;
+  int rp_r;   // 0: off
+  float* rp_part;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
@@ -106,6 +120,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // k-steps of 64, at most 8 splits, every split non-empty. A fixed function of
 // the shape, so workspace queries and launches agree.
 int gemm_splits(int M, int N, int K);
+// partials per row written by the epilogue row product of an N-column GEMM
+int gemm_rowprod_splits(int N);
 
 // ---- LoRA skinny kernels (lora.hip) ----
 // U = G L^T for G [M][K] bf16 (ldg), L [R][K] bf16 (ldl), 1 <= R <= 64.
@@ -118,6 +134,11 @@ int rowdot_splits(int M, int K);
 hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
                          int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
                          uint16_t* Ue, int64_t ldue, int KE, float* part, hipStream_t stream);
+// The fixed-order sum of nsplit partials part [nsplit][M][R] and the outputs
+// of launch_rowdot (Uf, Uf2, Ue) from it.
+hipError_t launch_rowdot_finish(const float* part, int nsplit, int M, int R, float s, float* Uf,
+                                float* Uf2, int split, int64_t ldu, uint16_t* Ue, int64_t ldue,
+                                int KE, hipStream_t stream);
 
 // Column reduction over tokens, first stage: for each chunk c of rows,
 // part[c][col][j] = sum_{i in chunk} G[i][col] * V[i][vofs + j], j < R.

@@ -169,8 +169,26 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_
   return sum;
 }
 
+// The same sum for 4 consecutive columns (p 16-byte aligned, stride a
+// multiple of 4): component-wise the same additions in the same order.
+__device__ __forceinline__ f32x4_t ordered_sum4(const float* __restrict__ p, int64_t stride, int n) {
+  f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const f32x4_t*)(p + (int64_t)(q + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; q < n; ++q) sum += *(const f32x4_t*)(p + (int64_t)q * stride);
+  return sum;
+}
+
 // U = sum of the split partials (fixed order); writes fp32 U (split across
-// two outputs at column `split`) and the bf16 K-extension operand.
+// two outputs at column `split`) and the bf16 K-extension operand
+// Ue = [hi(sU) | lo(sU) | 0]. A thread takes 4 consecutive columns of one row
+// of [0, max(R, KE)): with R % 4 == 0 it reads them as one 16-byte partial.
 __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restrict__ part,
                                                             int nsplit, int M, int R, float s,
                                                             float* __restrict__ Uf,
@@ -178,24 +196,37 @@ __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restr
                                                             int64_t ldu, uint16_t* __restrict__ Ue,
                                                             int64_t ldue, int KE) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int W = KE > R ? KE : R;
-  if (e >= (int64_t)M * W) return;
-  const int i = (int)(e / W), j = (int)(e - (int64_t)i * W);
-  if (j < R) {
-    const float sum = ordered_sum(part + (int64_t)i * R + j, (int64_t)M * R, nsplit);
-    if (j < split) {
-      if (Uf) Uf[(int64_t)i * ldu + j] = sum;
-    } else if (Uf2) {
-      Uf2[(int64_t)i * ldu + (j - split)] = sum;
+  const int W4 = ((KE > R ? KE : R) + 3) >> 2;
+  if (e >= (int64_t)M * W4) return;
+  const int i = (int)(e / W4), j0 = 4 * (int)(e - (int64_t)i * W4);
+  float sum[4];
+  if ((R & 3) == 0 && j0 < R) {
+    const f32x4_t v = ordered_sum4(part + (int64_t)i * R + j0, (int64_t)M * R, nsplit);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sum[t] = v[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      sum[t] = j0 + t < R ? ordered_sum(part + (int64_t)i * R + j0 + t, (int64_t)M * R, nsplit) : 0.0f;
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = j0 + t;
+    if (j < R) {
+      if (j < split) {
+        if (Uf) Uf[(int64_t)i * ldu + j] = sum[t];
+      } else if (Uf2) {
+        Uf2[(int64_t)i * ldu + (j - split)] = sum[t];
+      }
+      if (Ue) {
+        const float su = s * sum[t];
+        const uint32_t hi = f32_to_bf16(su);
+        Ue[(int64_t)i * ldue + j] = (uint16_t)hi;
+        Ue[(int64_t)i * ldue + R + j] = (uint16_t)f32_to_bf16(su - bf16_to_f32(hi));
+      }
+    } else if (Ue && j >= 2 * R && j < KE) {
+      Ue[(int64_t)i * ldue + j] = 0;
     }
-    if (Ue) {
-      const float su = s * sum;
-      const uint32_t hi = f32_to_bf16(su);
-      Ue[(int64_t)i * ldue + j] = (uint16_t)hi;
-      Ue[(int64_t)i * ldue + R + j] = (uint16_t)f32_to_bf16(su - bf16_to_f32(hi));
-    }
-  } else if (Ue && j >= 2 * R && j < KE) {
-    Ue[(int64_t)i * ldue + j] = 0;
   }
 }
 
@@ -217,8 +248,16 @@ hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int6
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int W = KE > R ? KE : R;
-  const int64_t total = (int64_t)M * W;
+  return launch_rowdot_finish(part, nsplit, M, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE, stream);
+}
+
+hipError_t launch_rowdot_finish(const float* part, int nsplit, int M, int R, float s, float* Uf,
+                                float* Uf2, int split, int64_t ldu, uint16_t* Ue, int64_t ldue,
+                                int KE, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  if (R < 1 || R > 64 || nsplit < 1) return hipErrorInvalidValue;
+  const int W4 = ((KE > R ? KE : R) + 3) / 4;
+  const int64_t total = (int64_t)M * W4;
   rowdot_finish_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
       part, nsplit, M, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE);
   return hipGetLastError();

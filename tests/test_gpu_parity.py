@@ -205,13 +205,39 @@ def test_mlp_small(cfg, mode):
     _check(_run_mlp(cfg, d, mode), _oracle_mlp(cfg, d))
 
 
-def test_mlp_fused_equals_staged_bitwise():
-    cfg = TINY_MLP[0]
+@pytest.mark.parametrize("cfg", [TINY_MLP[0], I.MlpCfg("h256_geglu", 130, 128, 256, 16, 1.0,
+                                                      "geglu_tanh", 1.0)], ids=lambda c: c.name)
+def test_mlp_fused_equals_staged_bitwise(cfg):
+    """Dequantizing inside the GEMM gives the bits of the staged weight.
+
+    The row products over the h-wide activations (Ud = H Ad^T, [Tg | Tu] =
+    [dg | du] blockdiag(Bg, Bu)) are summed in a different grouping in the
+    two modes (staged, r <= 16: per-wave partials written by the GEMM
+    epilogues; fused: a separate pass), so what depends on them (Ud, Y; dX,
+    dAg, dAu) may differ in the last bits; every other output must be equal.
+    The backward runs from one saved set in both modes."""
     d = _mlp_case(cfg, dense=True)
-    a = _run_mlp(cfg, d, "staged")
-    b = _run_mlp(cfg, d, "fused")
-    for k in a:
-        assert torch.equal(a[k], b[k]), k
+    w = _weights(cfg, d)
+    X, dY = d["X"].to(DEV), d["dY"].to(DEV)
+    say(f"mlp staged/fused {cfg.name} m={X.shape[0]} d={cfg.d} h={cfg.h}")
+    Ya, sva = Q.mlp_fwd(X, w, mode="staged")
+    Yb, svb = Q.mlp_fwd(X, w, mode="fused")
+    gra = Q.mlp_bwd(dY, X, sva, w, mode="staged")
+    grb = Q.mlp_bwd(dY, X, sva, w, mode="fused")
+    torch.cuda.synchronize()
+
+    def close(a, b, k):   # one bf16 step at the largest magnitude
+        a, b = a.float(), b.float()
+        assert (a - b).abs().max().item() <= 2.0 ** -7 * b.abs().max().item(), k
+
+    for k in ("g", "u", "Ug", "Uu"):
+        assert torch.equal(sva[k], svb[k]), k
+    close(sva["Ud"], svb["Ud"], "Ud")
+    close(Ya, Yb, "Y")
+    for k in ("dBd", "dAd", "dBg", "dBu"):
+        assert torch.equal(gra[k], grb[k]), k
+    for k in ("dX", "dAg", "dAu"):
+        close(gra[k], grb[k], k)
 
 
 @pytest.mark.parametrize("cfg", [I.LLAMA_MLP, I.MISTRAL_MLP, I.GEMMA_MLP], ids=lambda c: c.name)
