@@ -142,6 +142,17 @@ __device__ __forceinline__ void wave_sync() {
   asm volatile("" ::: "memory");
 }
 
+// This lane's index in the wave, computed where it is used. Being volatile,
+// it is neither merged with an earlier copy nor kept live across the code
+// before it: a value the register allocator spilled would be reloaded from
+// scratch, and that load's wait would also wait for every store issued
+// before it.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 }  // namespace
 
 __constant__ uint32_t c_nf4_levels_gemm[16] = {QLORA_NF4_LEVEL_BITS};
@@ -911,57 +922,73 @@ void gemm_bf16_kernel(GemmArgs p) {
   constexpr int SP = 132;  // floats per staged row
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
   const int col0 = n0 + wn * 128;
-  // Row product (rp_r > 0): the slab's bf16 results (GATEUP: H, 32 x 64; ACT_BWD:
-  // dg and du, 32 x 128 each) are also written to a panel of this wave's own
-  // after the staging regions, with a 16-byte-odd row pitch so that the 16
-  // rows of a fragment read hit 16 different bank groups, then multiplied by
-  // the rank-r operand on MFMA 16x16x32.
-  constexpr int RPP = EPI == EPI_GATEUP ? 72 : 136;           // bf16 per panel row
-  constexpr int RPW = EPI == EPI_GATEUP ? 32 * RPP : 2 * 32 * RPP;
-  uint16_t* rpan = reinterpret_cast<uint16_t*>(smem + 4 * 32 * SP * 4) + wave * RPW;
+  // Row product (rp_r > 0). A slab's bf16 results (GATEUP: H, 32 x 64; ACT_BWD:
+  // dg | du, 32 x 256) replace the first bytes of their own staged row once
+  // the row has been read (one wave reads and writes it, and LDS serves a
+  // wave in order). The 528-byte row pitch is 33 16-byte units, so the 16
+  // rows of a fragment read hit 16 different bank groups. The panel is
+  // multiplied by the rank-r operand on MFMA 16x16x32, and the four 16x16
+  // results per lane and slab are parked in LDS after the staging regions:
+  // xpark[slab][wave][t] (t = 2 half + rg, 64 lanes x 16 bytes each). At the
+  // end of the tile the two waves of a tile row add their halves of the
+  // columns and store one fp32 partial per tile column.
+  constexpr int PP = 2 * SP;   // bf16 per panel row
+  constexpr int ND = EPI == EPI_GATEUP ? 2 : 4;
+  f32x4_t* xpark = reinterpret_cast<f32x4_t*>(smem + 4 * 32 * SP * 4);
   // ACT_BWD: the rank-r fragments of this wave's 128 columns from the LDS
   // copy (half 0: gate rows, 1: up rows); lane (i = lane % 16, q = lane / 16)
   // gets row i, columns 32 kc + 8 q of the wave's range
   auto lds_frags = [&](bf16x8_t* b, int half) {
-    const int jr = lane & 15, kq = lane >> 4;
+    const int ln = lane_here(), jr = ln & 15, kq = ln >> 4;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int c = wn * 16 + 4 * kc + kq;
       b[kc] = *(const bf16x8_t*)(smem + RPL_OFF + (16 * half + jr) * 512 + ((c ^ jr) << 4));
     }
   };
-  // sum_c L[j][c] panel[s][c] over the wave's panel columns for the 32 panel
-  // rows, as D[j][s] (L as the row operand), stored to this wave's split at
-  // columns jofs + j (j < rp_r): a lane holds 4 consecutive j of one row.
-  auto rowprod = [&](const uint16_t* pan, auto nkc_c, const bf16x8_t* b, int jofs, auto&& growf) {
+  // D[j][s] = sum_c L[j][c] panel[s][c] over the wave's panel columns for the
+  // 32 panel rows (L as the row operand); lane (sr, kq) gets j = 4 kq + v of
+  // panel row 16 rg + sr in d[rg][v]; parked as xpark[mt][wave][2 half + rg]
+  auto rowprod = [&](const uint16_t* pan, auto nkc_c, const bf16x8_t* b, int mt, int half) {
     constexpr int NKC = decltype(nkc_c)::value;
-    const int sr = lane & 15, kq = lane >> 4;
-    f32x4_t d[2];
+    const int ln = lane_here(), sr = ln & 15, kq = ln >> 4;
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      d[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4_t d = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8_t a = *(const bf16x8_t*)(pan + (16 * rg + sr) * RPP + 32 * kc + 8 * kq);
-        d[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kc], a, d[rg], 0, 0, 0);
+        const bf16x8_t a = *(const bf16x8_t*)(pan + (16 * rg + sr) * PP + 32 * kc + 8 * kq);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kc], a, d, 0, 0, 0);
       }
+      xpark[((mt * 4 + wave) * ND + 2 * half + rg) * 64 + ln] = d;
     }
-    // d[rg][v] = D[j = 4 kq + v][panel row 16 rg + sr]
+  };
+  // after the four slabs: wave (wm, wn) sums and stores slabs 2 wn and 2 wn + 1
+  // of its tile row, adding the wn = 0 half of the columns first
+  auto rowprod_store = [&]() {
     const int rw = EPI == EPI_GATEUP ? p.rp_r : 2 * p.rp_r;
-    const int j0 = 4 * kq;
-    float* out = p.rp_part + (int64_t)(2 * tn + wn) * p.M * rw + jofs + j0;
-    const bool vec = ((jofs | rw) & 3) == 0 && j0 + 4 <= p.rp_r;
+    const int ln = lane_here(), sr = ln & 15, j0 = 4 * (ln >> 4);
+    float* out = p.rp_part + (int64_t)tn * p.M * rw;
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      const int row = growf(16 * rg + sr);
-      if (row >= p.M || j0 >= p.rp_r) continue;
-      float* o = out + (int64_t)row * rw;
-      if (vec) {
-        *(f32x4_t*)o = d[rg];
-      } else {
+    for (int k = 0; k < 2; ++k) {
+      const int mt = 2 * wn + k;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (j0 + v < p.rp_r) o[v] = d[rg][v];
+      for (int t = 0; t < ND; ++t) {
+        const int half = t >> 1, rg = t & 1;
+        const f32x4_t d = xpark[((mt * 4 + 2 * wm) * ND + t) * 64 + ln] +
+                          xpark[((mt * 4 + 2 * wm + 1) * ND + t) * 64 + ln];
+        const int s = 16 * rg + sr;
+        const int row = m0 + wm * 128 + 8 * (s >> 1) + 2 * mt + (s & 1);
+        const int jofs = half * p.rp_r;
+        if (row >= p.M || j0 >= p.rp_r) continue;
+        float* o = out + (int64_t)row * rw + jofs + j0;
+        if (((jofs | rw) & 3) == 0 && j0 + 4 <= p.rp_r) {
+          *(f32x4_t*)o = d;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (j0 + v < p.rp_r) o[v] = d[v];
+        }
       }
     }
   };
@@ -1047,18 +1074,20 @@ void gemm_bf16_kernel(GemmArgs p) {
             *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
           }
         }
-        if (EPI == EPI_ACT_BWD && rp_on) {   // zeros outside the output
-          *(u32x4_t*)(rpan + s * RPP + cc) = odg;
-          *(u32x4_t*)(rpan + (32 + s) * RPP + cc) = odu;
+        if (EPI == EPI_ACT_BWD && rp_on) {   // over the row just read; zeros outside the output
+          uint16_t* pr = reinterpret_cast<uint16_t*>(stage) + s * PP + cc;
+          *(u32x4_t*)pr = odg;
+          *(u32x4_t*)(pr + 128) = odu;
         }
       }
       if (EPI == EPI_ACT_BWD && rp_on) {
         wave_sync();
+        const uint16_t* pan = reinterpret_cast<const uint16_t*>(stage);
         bf16x8_t lb[4];
         lds_frags(lb, 0);
-        rowprod(rpan, std::integral_constant<int, 4>(), lb, 0, grow);
+        rowprod(pan, std::integral_constant<int, 4>(), lb, mt, 0);
         lds_frags(lb, 1);
-        rowprod(rpan + 32 * RPP, std::integral_constant<int, 4>(), lb, p.rp_r, grow);
+        rowprod(pan + 128, std::integral_constant<int, 4>(), lb, mt, 1);
       }
     } else {  // EPI_GATEUP: staged columns [gate j0..+31 | up j0..+31 | gate j0+32.. | up j0+32..]
       const int jj = (lane & 7) * 8;                       // 0..56: output index within 64
@@ -1097,11 +1126,12 @@ void gemm_bf16_kernel(GemmArgs p) {
           *(u32x4_t*)(p.u_out + o) = ou;
           *(u32x4_t*)(p.h_out + o) = oh;
         }
-        if (rp_on) *(u32x4_t*)(rpan + s * RPP + jj) = oh;   // zeros outside the output
+        if (rp_on)   // over the row just read; zeros outside the output
+          *(u32x4_t*)(reinterpret_cast<uint16_t*>(stage) + s * PP + jj) = oh;
       }
       if (rp_on) {
         wave_sync();
-        rowprod(rpan, std::integral_constant<int, 2>(), rpb, 0, grow);
+        rowprod(reinterpret_cast<const uint16_t*>(stage), std::integral_constant<int, 2>(), rpb, mt, 0);
       }
     }
     wave_sync();
@@ -1117,6 +1147,13 @@ void gemm_bf16_kernel(GemmArgs p) {
     slabs(std::integral_constant<int, 1>());
   else
     slabs(std::integral_constant<int, 0>());
+  if (rp_on) {
+    // every wave's parked results are in LDS (lgkmcnt(0)); the global stores
+    // in flight are not waited for
+    wait_vm<63>();
+    ring_barrier();
+    rowprod_store();
+  }
 }
 
 template <int BSRC, int EPI>
@@ -1175,7 +1212,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int gemm_rowprod_splits(int N) { return 2 * ((N + BN - 1) / BN); }
+int gemm_rowprod_splits(int N) { return (N + BN - 1) / BN; }
 
 int gemm_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);

@@ -99,10 +99,10 @@ struct GemmArgs {
   int64_t hdim;
   int act;
   // row product in the GATEUP / ACT_BWD epilogues (gemm_bf16_kernel only):
-  // with rp_r in 1..16, each wave multiplies the bf16 values it writes (H;
-  // dg and du) by a rank-r operand over its own columns and stores an fp32
-  // partial part[2 * tile_col + wave_col][row][j]; gemm_rowprod_splits(N)
-  // partials per row, summed by launch_rowdot_finish.
+  // with rp_r in 1..16, the bf16 values the epilogue writes (H; dg and du)
+  // are multiplied by a rank-r operand over the tile's columns into an fp32
+  // partial part[tile_col][row][j]; gemm_rowprod_splits(N) partials per row,
+  // summed by launch_rowdot_finish.
   //   GATEUP:  j < r: sum_c H[row][c] rp_l[j][c]                  (width r)
   //   ACT_BWD: j < r: sum_c dg[row][c] rp_l[j][c]; r + j: sum_c du[row][c]
   //            rp_l2[j][c]                                        (width 2r)

@@ -212,7 +212,7 @@ def test_mlp_fused_equals_staged_bitwise(cfg):
 
     The row products over the h-wide activations (Ud = H Ad^T, [Tg | Tu] =
     [dg | du] blockdiag(Bg, Bu)) are summed in a different grouping in the
-    two modes (staged, r <= 16: per-wave partials written by the GEMM
+    two modes (staged, r <= 16: per-tile partials written by the GEMM
     epilogues; fused: a separate pass), so what depends on them (Ud, Y; dX,
     dAg, dAu) may differ in the last bits; every other output must be equal.
     The backward runs from one saved set in both modes."""
