@@ -778,8 +778,8 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   const int chunks = colreduce_chunks((int)m);
   const float s = w->s;
 
-  // LoRA operand layouts (launched below: on the helper stream when staged,
-  // ahead of Td there; every reader waits for the helper stream)
+  // LoRA operand layouts (launched below on the caller's stream, before the
+  // helper stream forks: everything after reads them)
   PrepJobs bwd_jobs;
   {  // ltd = Bd^T; bextdh = [Ad^T | Ad^T | 0]; ltgu = blockdiag(Bg^T, Bu^T);
      // bextdx = [Ag^T | Au^T | Ag^T | Au^T | 0]
@@ -808,9 +808,8 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   Side side(st);
   QL_TRY(side.open(), "mlp_bwd: helper stream");
   hipStream_t ss = side.stream();
-  if (!staged) QL_TRY(launch_prep(bwd_jobs, st), "mlp_bwd: LoRA layouts");
+  QL_TRY(launch_prep(bwd_jobs, st), "mlp_bwd: LoRA layouts");
   QL_TRY(side.fork(0), "mlp_bwd: fork");
-  if (staged) QL_TRY(launch_prep(bwd_jobs, ss), "mlp_bwd: LoRA layouts");
   // Td = dY Bd: on the helper stream beside the caller's W_d^T when staged
   auto row_td = [&](hipStream_t q) {
     return launch_rowdot(dY, d, t.ltd, d, (int)m, (int)d, (int)r, s, t.td, nullptr, (int)r, r,
