@@ -12,8 +12,9 @@
 //                -> Ud = H Ad^T -> down GEMM
 //   MLP bwd    : Td = dY Bd, dBd -> dH GEMM with act' epilogue (dg, du) -> dAd (H recomputed)
 //                -> [Tg|Tu] = [dg|du] blockdiag(Bg,Bu), dBg, dBu -> dX GEMM (K = 2h) -> dAg, dAu
-//   (with a bf16 weight and r <= 16, Ud and [Tg|Tu] are formed in the epilogues
-//   that write H and dg, du, as per-wave partials, and only summed afterwards)
+//   (with a bf16 weight, r <= 16 and m <= 16384, Ud and [Tg|Tu] are formed in
+//   the epilogues that write H and dg, du, as per-tile partials, and only
+//   summed afterwards)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -87,9 +88,11 @@ bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE
 
 // The MLP's two row products over h-wide activations (Ud = H Ad^T and
 // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)) come from the epilogues of the
-// GEMMs that write those activations when the GEMM reads a bf16 weight and
-// r <= 16; otherwise a separate pass reads the activations back.
-bool rp_epilogue(int mode, int64_t r) { return staged_like(mode) && r <= 16; }
+// GEMMs that write those activations when the GEMM reads a bf16 weight,
+// r <= 16 and m <= 16384; otherwise a separate pass reads the activations
+// back. Measured on the Llama-7B MLP, the epilogue form gains 1.2% at 8192
+// tokens, breaks even at 16384 and loses 1-2% from 24576 tokens up.
+bool rp_epilogue(int mode, int64_t r, int64_t m) { return staged_like(mode) && r <= 16 && m <= 16384; }
 
 int resolve_mode(int mode) {
   if (mode == QLORA_DEQUANT_AUTO) return QLORA_DEQUANT_STAGED;
@@ -185,7 +188,7 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.H = c.take<uint16_t>(m * h);
   t.wgu = staged_like(mode) ? c.take<uint16_t>(2 * h * d) : nullptr;
   t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
-  t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(mode, r) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
+  t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
   t.kpart = c.take<float>(splitk_elems(m, d, h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
@@ -224,7 +227,7 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
   t.wdt = staged_like(mode) ? c.take<uint16_t>(h * d) : nullptr;
   t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
-  t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(mode, r) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
+  t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
   t.kpart = c.take<float>(splitk_elems(m, d, 2 * h, staged_like(mode)));
   if (w) *w = t;
   return c.off;
@@ -720,7 +723,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
   g.epi = EPI_GATEUP; g.g_out = g_save; g.u_out = u_save; g.h_out = t.H; g.hdim = h; g.act = w->act;
   // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
-  const bool rp = rp_epilogue(mode, r);
+  const bool rp = rp_epilogue(mode, r, m);
   if (rp) { g.rp_l = w->a_down; g.rp_ldl = h; g.rp_r = (int)r; g.rp_part = t.rpart; }
   if (staged) QL_TRY(side.wait(1), "mlp_fwd: wait");
   QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
@@ -862,7 +865,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
   // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu): in the epilogue, or below
-  const bool rp = rp_epilogue(mode, r);
+  const bool rp = rp_epilogue(mode, r, m);
   if (rp) {
     g.rp_l = t.ltgu; g.rp_l2 = t.ltgu + r * 2 * h + h; g.rp_ldl = 2 * h;
     g.rp_r = (int)r; g.rp_part = t.rpart;
