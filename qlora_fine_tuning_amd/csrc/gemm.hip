@@ -31,10 +31,11 @@
 // gemm_nt_kernel (B as NF4 codes, dequantized in the tile): 256 x 256 tile
 // per workgroup of 8 waves (2 per SIMD) laid out 2 x 4, each wave 128 x 64 =
 // 4 x 2 MFMA 32x32x16 tiles. K is walked in 64-wide steps through a 2-deep
-// LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4); LDS rows
-// are 128 B with the 16-byte chunk index XOR-swizzled by (row >> 1) & 7.
-// The feed carries the 4-bit codes and the fp32 absmax (8 KB + 1 KB per step
-// instead of 32 KB of bf16); the block dequantizes the next step's codes in
+// bf16 LDS ring; LDS rows are 128 B with the 16-byte chunk index
+// XOR-swizzled by (row >> 1) & 7. The feed carries the 4-bit codes and the
+// fp32 absmax (8 KB + 1 KB per step instead of 32 KB of bf16), brought by
+// direct-to-LDS loads (global_load_lds_dwordx4) two steps ahead into a
+// 3-deep ring of their own; the block dequantizes the next step's codes in
 // LDS, bf16_rne(fp32_rne(level[code] * absmax)) exactly as the standalone
 // dequant, while its matrix cores work on the current step. BSRC_NF4_T reads
 // the weight transposed (the backward dX = dY W): the tile's rows are input
@@ -47,6 +48,14 @@
 // activation as a compile-time constant (one branch per launch, none per
 // value): with one wave per SIMD the epilogue runs with the matrix cores
 // idle, so its instruction count matters.
+//
+// Row products (gemm_bf16_kernel, GATEUP and ACT_BWD, on request): the bf16
+// values the epilogue writes (H; dg and du) are also multiplied by a rank-r
+// operand (A_down; blockdiag(B_gate, B_up)) on MFMA 16x16x32, from a panel
+// that overwrites each staged row once it is read. The results are parked
+// in LDS per slab; after the last slab the two waves of a tile row add their
+// column halves and store one fp32 partial per tile column. The MLP's next
+// LoRA product then needs no pass that reads H or dg|du back.
 //
 // Split-K (gemm_bf16_kernel, store epilogues only): an output with fewer than
 // 256 tiles is computed as several K ranges that write fp32 partials;
