@@ -927,7 +927,11 @@ void gemm_bf16_kernel(GemmArgs p) {
   // acc[mt][nt][v]: MFMA row r = 8*(v/4) + 4*(lane/32) + v%4, col j = lane%32, i.e.
   // tile row wm*128 + 8*(r&15) + 2*mt + (r>>4), tile col wn*128 + 8*(j&15) + 2*nt + (j>>4).
   // Slab mt (32 rows) is staged through LDS as staged row s = 2*(r&15) + (r>>4)
-  // (tile row wm*128 + 8*(s>>1) + 2*mt + (s&1)) by 128 columns in tile order.
+  // (tile row wm*128 + 8*(s>>1) + 2*mt + (s&1)) by 128 columns. A lane writes
+  // its four nt values of one row as one 16-byte store, so within each group
+  // of 8 columns position 4*(j>>4) + nt holds tile column 2*nt + (j>>4):
+  // tile column 2e + t of a group is element e of the group's first (t = 0)
+  // or second (t = 1) 16 bytes. Readers restore tile order in registers.
   constexpr int SP = 132;  // floats per staged row
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);
   const int col0 = n0 + wn * 128;
@@ -1024,12 +1028,11 @@ void gemm_bf16_kernel(GemmArgs p) {
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
-        stage[(2 * (r & 15) + (r >> 4)) * SP + 8 * (j & 15) + 2 * nt + (j >> 4)] = acc[mt][nt][v];
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
+      *(f32x4_t*)&stage[(2 * (r & 15) + (r >> 4)) * SP + 8 * (j & 15) + 4 * (j >> 4)] =
+          f32x4_t{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]};
+    }
     wave_sync();   // the staging region is this wave's own
     if (EPI == EPI_STORE || EPI == EPI_STORE3 || EPI == EPI_ACT_BWD) {
       // lane: 8 consecutive columns of one staged row; 4 rows per pass
@@ -1043,15 +1046,14 @@ void gemm_bf16_kernel(GemmArgs p) {
           const float* x = &stage[s * SP + cc];
           if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1) {   // fp32 partial
             float* o = p.part + ((int64_t)ksp * p.M + row) * p.N + col;
-            *(f32x4_t*)o = *(const f32x4_t*)x;
-            *(f32x4_t*)(o + 4) = *(const f32x4_t*)(x + 4);
+            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
+            *(f32x4_t*)o = f32x4_t{x0[0], x1[0], x0[1], x1[1]};
+            *(f32x4_t*)(o + 4) = f32x4_t{x0[2], x1[2], x0[3], x1[3]};
           } else if (EPI == EPI_STORE || EPI == EPI_STORE3) {
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             u32x4_t o;
-            o[0] = pack_bf16x2(x0[0], x0[1]);
-            o[1] = pack_bf16x2(x0[2], x0[3]);
-            o[2] = pack_bf16x2(x1[0], x1[1]);
-            o[3] = pack_bf16x2(x1[2], x1[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x0[e], x1[e]);
             uint16_t* dst;
             if (EPI == EPI_STORE3)   // the 8 columns lie in one output (nc1, nc2 multiples of 8)
               dst = col < p.nc1   ? p.C + (int64_t)row * p.ldc + col
@@ -1071,7 +1073,7 @@ void gemm_bf16_kernel(GemmArgs p) {
                 const float u = bf16_to_f32(t ? (uw[q][e] >> 16) : (uw[q][e] & 0xFFFFu));
                 float a, da;
                 act_fwd_bwd_t<ACT>(g, &a, &da);
-                const float d = e < 2 ? x0[2 * e + t] : x1[2 * e - 4 + t];
+                const float d = t ? x1[e] : x0[e];
                 dg[t] = d * u * da;
                 du[t] = d * a;
               }
@@ -1110,11 +1112,16 @@ void gemm_bf16_kernel(GemmArgs p) {
         if (row < p.M && col0 < p.N) {
           const float* gs = &stage[s * SP + gcol];
           const float* us = gs + 32;
-          float gv[8], uv[8];
-          *(f32x4_t*)gv = *(const f32x4_t*)gs;
-          *(f32x4_t*)(gv + 4) = *(const f32x4_t*)(gs + 4);
-          *(f32x4_t*)uv = *(const f32x4_t*)us;
-          *(f32x4_t*)(uv + 4) = *(const f32x4_t*)(us + 4);
+          const f32x4_t g0 = *(const f32x4_t*)gs, g1 = *(const f32x4_t*)(gs + 4);
+          const f32x4_t u0 = *(const f32x4_t*)us, u1 = *(const f32x4_t*)(us + 4);
+          float gv[8], uv[8];   // tile order
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[2 * e] = g0[e];
+            gv[2 * e + 1] = g1[e];
+            uv[2 * e] = u0[e];
+            uv[2 * e + 1] = u1[e];
+          }
           u32x4_t og, ou;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
