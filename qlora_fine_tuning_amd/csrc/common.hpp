@@ -21,9 +21,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-// Two fp32 -> packed bf16x2 (lo in bits 0..15).
+// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even: one
+// two-source v_cvt_pk_bf16_f32 (two one-value conversions would also need a
+// shift and an OR).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }

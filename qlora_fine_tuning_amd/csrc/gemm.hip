@@ -1125,17 +1125,12 @@ void gemm_bf16_kernel(GemmArgs p) {
           u32x4_t og, ou;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float hv[2];
-            uint32_t gb[2], ub[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              gb[t] = f32_to_bf16(gv[2 * e + t]);
-              ub[t] = f32_to_bf16(uv[2 * e + t]);
-              hv[t] = act_fwd_t<ACT>(bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
-            }
-            og[e] = gb[0] | (gb[1] << 16);
-            ou[e] = ub[0] | (ub[1] << 16);
-            oh[e] = pack_bf16x2(hv[0], hv[1]);
+            og[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+            ou[e] = pack_bf16x2(uv[2 * e], uv[2 * e + 1]);
+            // H from the rounded g and u (the values the backward reads)
+            const float g0 = __uint_as_float(og[e] << 16), g1 = __uint_as_float(og[e] & 0xFFFF0000u);
+            const float u0 = __uint_as_float(ou[e] << 16), u1 = __uint_as_float(ou[e] & 0xFFFF0000u);
+            oh[e] = pack_bf16x2(act_fwd_t<ACT>(g0) * u0, act_fwd_t<ACT>(g1) * u1);
           }
           const int64_t o = (int64_t)row * p.hdim + j;
           *(u32x4_t*)(p.g_out + o) = og;
