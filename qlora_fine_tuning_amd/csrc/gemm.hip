@@ -1017,11 +1017,12 @@ void gemm_bf16_kernel(GemmArgs p) {
     if (EPI == EPI_ACT_BWD) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int row = grow(q * 4 + (lane >> 4)), col = col0 + (lane & 15) * 8;
+        // staged row q * 4 + lane / 16 is tile row grow(lane / 16) + 16 q
+        const int row = grow(lane >> 4) + 16 * q, col = col0 + (lane & 15) * 8;
         gw[q] = u32x4_t{0u, 0u, 0u, 0u};
         uw[q] = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col < p.N) {
-          const int64_t o = (int64_t)row * p.hdim + col;
+          const int64_t o = (int64_t)grow(lane >> 4) * p.hdim + col + (int64_t)(16 * q) * p.hdim;
           gw[q] = *(const u32x4_t*)(p.g_in + o);
           uw[q] = *(const u32x4_t*)(p.u_in + o);
         }
@@ -1035,17 +1036,29 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
     wave_sync();   // the staging region is this wave's own
     if (EPI == EPI_STORE || EPI == EPI_STORE3 || EPI == EPI_ACT_BWD) {
-      // lane: 8 consecutive columns of one staged row; 4 rows per pass
+      // lane: 8 consecutive columns of one staged row; 4 rows per pass.
+      // Staged row q * 4 + lane / 16 is tile row row0 + 16 q, so every output
+      // offset is the one of pass 0 plus q times a uniform stride.
       const int cc = (lane & 15) * 8;
+      const int row0 = grow(lane >> 4), col = col0 + cc;
+      uint16_t* cbase = p.C;
+      int64_t cld = p.ldc, ccol = col;
+      if (EPI == EPI_STORE3) {   // the 8 columns lie in one output (nc1, nc2 multiples of 8)
+        if (col >= p.nc2) { cbase = p.C2; cld = p.ldc2; ccol = col - p.nc2; }
+        else if (col >= p.nc1) { cbase = p.C1; cld = p.ldc1; ccol = col - p.nc1; }
+      }
+      const int64_t coff0 = (int64_t)row0 * cld + ccol;
+      const int64_t poff0 = ((int64_t)ksp * p.M + row0) * p.N + col;
+      const int64_t doff0 = (int64_t)row0 * (2 * p.hdim) + col;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int s = q * 4 + (lane >> 4);
-        const int row = grow(s), col = col0 + cc;
+        const int row = row0 + 16 * q;
         u32x4_t odg = u32x4_t{0u, 0u, 0u, 0u}, odu = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col < p.N) {
           const float* x = &stage[s * SP + cc];
           if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1) {   // fp32 partial
-            float* o = p.part + ((int64_t)ksp * p.M + row) * p.N + col;
+            float* o = p.part + poff0 + (int64_t)(16 * q) * p.N;
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             *(f32x4_t*)o = f32x4_t{x0[0], x1[0], x0[1], x1[1]};
             *(f32x4_t*)(o + 4) = f32x4_t{x0[2], x1[2], x0[3], x1[3]};
@@ -1054,14 +1067,7 @@ void gemm_bf16_kernel(GemmArgs p) {
             u32x4_t o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x0[e], x1[e]);
-            uint16_t* dst;
-            if (EPI == EPI_STORE3)   // the 8 columns lie in one output (nc1, nc2 multiples of 8)
-              dst = col < p.nc1   ? p.C + (int64_t)row * p.ldc + col
-                    : col < p.nc2 ? p.C1 + (int64_t)row * p.ldc1 + (col - p.nc1)
-                                  : p.C2 + (int64_t)row * p.ldc2 + (col - p.nc2);
-            else
-              dst = p.C + (int64_t)row * p.ldc + col;
-            *(u32x4_t*)dst = o;
+            *(u32x4_t*)(cbase + coff0 + (int64_t)(16 * q) * cld) = o;
           } else {  // staged values are dH
             const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
 #pragma unroll
@@ -1080,7 +1086,7 @@ void gemm_bf16_kernel(GemmArgs p) {
               odg[e] = pack_bf16x2(dg[0], dg[1]);
               odu[e] = pack_bf16x2(du[0], du[1]);
             }
-            const int64_t od = (int64_t)row * (2 * p.hdim) + col;
+            const int64_t od = doff0 + (int64_t)(16 * q) * (2 * p.hdim);
             *(u32x4_t*)(p.dgu + od) = odg;
             *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
           }
@@ -1104,10 +1110,13 @@ void gemm_bf16_kernel(GemmArgs p) {
       const int jj = (lane & 7) * 8;                       // 0..56: output index within 64
       const int gcol = (jj >> 5) * 64 + (jj & 31);         // staged gate column (up = +32)
       const int64_t j = (int64_t)(col0 >> 1) + jj;
+      // staged row q * 8 + lane / 8 is tile row row0 + 32 q
+      const int row0 = grow(lane >> 3);
+      const int64_t hoff0 = (int64_t)row0 * p.hdim + j;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int s = q * 8 + (lane >> 3);
-        const int row = grow(s);
+        const int row = row0 + 32 * q;
         u32x4_t oh = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col0 < p.N) {
           const float* gs = &stage[s * SP + gcol];
@@ -1132,7 +1141,7 @@ void gemm_bf16_kernel(GemmArgs p) {
             const float u0 = __uint_as_float(ou[e] << 16), u1 = __uint_as_float(ou[e] & 0xFFFF0000u);
             oh[e] = pack_bf16x2(act_fwd_t<ACT>(g0) * u0, act_fwd_t<ACT>(g1) * u1);
           }
-          const int64_t o = (int64_t)row * p.hdim + j;
+          const int64_t o = hoff0 + (int64_t)(32 * q) * p.hdim;
           *(u32x4_t*)(p.g_out + o) = og;
           *(u32x4_t*)(p.u_out + o) = ou;
           *(u32x4_t*)(p.h_out + o) = oh;
