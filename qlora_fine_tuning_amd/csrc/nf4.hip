@@ -48,23 +48,23 @@ __device__ __forceinline__ int64_t dest_row(int64_t n, int interleave) {
   return 64 * (n >> 5) + 32 * (interleave - 1) + (n & 31);
 }
 
-// One thread per 8 weights (4 code bytes in, 16 bf16 bytes out). Grid-stride
-// over n * k / 8 groups.
+// One thread per 16 weights of one row (8 code bytes and one absmax in, 32
+// bf16 bytes out); blockIdx.y walks the rows (strided when there are more
+// than the grid's y extent), blockIdx.x the 4096-weight chunks of a row.
 __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int interleave) {
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = __uint_as_float(c_nf4_levels[threadIdx.x]);
   __syncthreads();
-  const int64_t groups_per_row = k >> 3;
-  const int64_t total = n * groups_per_row;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = t / groups_per_row;
-    const int64_t grp = t - row * groups_per_row;
-    const uint32_t word = *(const uint32_t*)(codes + row * (k >> 1) + grp * 4);
-    const float amax = absmax[row * (k >> 6) + (grp >> 3)];
-    *(u32x4_t*)(out + dest_row(row, interleave) * ld_out + grp * 8) = dequant8(word, amax, lut);
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 16-weight group
+  if (g * 16 >= k) return;
+  for (int64_t row = blockIdx.y; row < n; row += gridDim.y) {
+    const uint2 cw = *(const uint2*)(codes + row * (k >> 1) + g * 8);
+    const float amax = absmax[row * (k >> 6) + (g >> 2)];
+    uint16_t* o = out + dest_row(row, interleave) * ld_out + g * 16;
+    *(u32x4_t*)o = dequant8(cw.x, amax, lut);
+    *(u32x4_t*)(o + 8) = dequant8(cw.y, amax, lut);
   }
 }
 
@@ -189,11 +189,10 @@ hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t*
 hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, int64_t n, int64_t k,
                                    uint16_t* out, int64_t ld_out, int interleave,
                                    hipStream_t stream) {
-  const int64_t total = n * (k >> 3);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  nf4_dequant_rows_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+  if (n == 0 || k == 0) return hipSuccess;
+  const int64_t gx = (k / 16 + 255) / 256;
+  const int64_t gy = n < 65535 ? n : 65535;
+  nf4_dequant_rows_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream>>>(
       codes, absmax, n, k, out, ld_out, interleave);
   return hipGetLastError();
 }
