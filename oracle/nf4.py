@@ -18,10 +18,15 @@ Readings taken where the pages are silent
   normal quantiles of 8 evenly spaced probabilities in (1/2, delta], 7 negative
   levels mirrored from 7 evenly spaced probabilities in (1/2, delta], an exact
   zero, all divided by Phi^-1(delta) so the ends are exactly -1 and +1.
-  delta = 31/32: the probability midpoint of the outermost of 16
-  equal-probability bins of the normal (Phi^-1(1) is infinite, so the last
-  level cannot sit at probability 1). Values are formed in fp64 and rounded
-  once to fp32.
+  Phi^-1(1) is infinite, so the outermost level cannot sit at probability 1;
+  it sits at the centre of the outermost equal-probability bin instead. The
+  positive half is cut as if into 16 bins (centre 1 - 1/32) and the negative
+  half as if into 15 (centre 1 - 1/30), and both halves share one outermost
+  probability, so delta is the mean of the two centres:
+  delta = ((1 - 1/30) + (1 - 1/32)) / 2 = 0.96770833... This is the offset of
+  the QLoRA paper's construction, so codes from a standard NF4 quantizer
+  decode to the same levels. Values are formed in fp64 and rounded once to
+  fp32.
 * Blocks: 64 consecutive weights along a row share one fp32 absmax.
 * Code choice: the level nearest to w/absmax (fp64), ties to the lower code.
 * All-zero block: absmax 0, every code 7 (the exact-zero level).
@@ -36,7 +41,7 @@ from __future__ import annotations
 import numpy as np
 from scipy.stats import norm
 
-NF4_DELTA = 31.0 / 32.0
+NF4_DELTA = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
 BLOCK = 64
 
 

@@ -18,7 +18,7 @@ def main():
     with open(path, "w") as f:
         f.write("# NF4 level table (fp32), written by tests/golden/make_golden.py from\n")
         f.write("# oracle.nf4.nf4_levels(): asymmetric normal-quantile construction with\n")
-        f.write("# delta = 31/32. Columns: index, fp32 bits (hex), value.\n")
+        f.write("# delta = ((1 - 1/30) + (1 - 1/32)) / 2. Columns: index, fp32 bits (hex), value.\n")
         for i, v in enumerate(levels):
             f.write(f"{i} {int(levels[i:i+1].view('uint32')[0]):08x} {float(v):.9g}\n")
     print("wrote", path)

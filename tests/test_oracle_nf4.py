@@ -86,11 +86,18 @@ def test_bf16_rounding_matches_torch():
 
 
 def _bf16_sweep():
-    # every positive normal bf16 value with exponent in [2^-24, 2^8)
-    exps = np.arange(127 - 24, 127 + 8, dtype=np.uint32)
-    mant = np.arange(128, dtype=np.uint32)
-    bits = ((exps[:, None] << 7) | mant[None, :]).reshape(-1).astype(np.uint16)
-    return (bits.astype(np.uint32) << 16).view(np.float32)
+    # every positive finite bf16 value: the 127 subnormals and all 254 normal
+    # binades (bit patterns 0x0001 .. 0x7F7F)
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    return (bits << 16).view(np.float32)
+
+
+def _single_rounding_to_bf16(x):
+    # one round-to-nearest-even of an fp64 value to the bf16 grid: 8
+    # significant bits for normal results, a fixed 2^-133 quantum below 2^-126
+    m, e = np.frexp(x)
+    q = np.exp2(np.maximum(e - 8, -133).astype(np.float64))
+    return np.round(x / q) * q
 
 
 def test_dequant_equals_torch_two_roundings_all_codes():
@@ -105,13 +112,23 @@ def test_dequant_equals_torch_two_roundings_all_codes():
     assert np.array_equal(got, want)
     # With this table a single rounding of the exact product (at most 32
     # significant bits: 24 from the level, 8 from the bf16 absmax) never lands
-    # differently from the two-step rounding on normal values: the contract
-    # holds whichever order an implementation takes.
+    # differently from the two-step rounding, over every finite positive bf16
+    # absmax including subnormal products: the contract holds whichever order
+    # an implementation takes.
     exact = nf4.nf4_levels().astype(np.float64)[codes] * absmax.astype(np.float64)[:, None]
-    mant, ex = np.frexp(exact)                       # exact = mant * 2^ex, |mant| in [0.5, 1)
-    single = np.round(mant * 256.0) * np.exp2(ex - 8.0)   # one rounding to 8 bits, ties to even
+    single = _single_rounding_to_bf16(exact)
     twice = nf4.bf16_bits_to_f64(want)
     assert np.array_equal(single, twice)
+
+
+def test_single_rounding_helper_on_known_values():
+    # the helper used above, on hand-checked values: a tie to even in the
+    # normal range (1 + 2^-8 lies halfway between 1 and 1 + 2^-7), one just
+    # past the tie, and the subnormal grid (2^-134 is a tie between 0 and
+    # 2^-133; 3 * 2^-134 rounds to 2 * 2^-133)
+    got = _single_rounding_to_bf16(np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30,
+                                             2.0 ** -134, 3 * 2.0 ** -134]))
+    assert list(got) == [1.0, 1 + 2.0 ** -7, 0.0, 2 * 2.0 ** -133]
 
 
 def test_zero_code_and_absmax_roundtrip():
