@@ -12,7 +12,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libqlora_mi355x.so")
+# QLORA_LIB_PATH selects another build of the same library (the host-code
+# sanitizer build that the tests make); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("QLORA_LIB_PATH") or os.path.join(PKG, "libqlora_mi355x.so")
 
 QLORA_OK = 0
 STATUS = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLORA_EWORKSPACE",

@@ -62,5 +62,35 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = True) -> str:
+    """A copy of the library whose host code (csrc/api.cpp: argument checks,
+    workspace carving, stream and event handling) is built by g++ with
+    AddressSanitizer and UndefinedBehaviorSanitizer. The kernels' objects are
+    the ones build() made, unchanged (no GPU code is instrumented). Load it
+    with QLORA_LIB_PATH=<path> and the ASan runtime preloaded."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build(verbose=False)
+    out = os.path.join(BUILD, "san")
+    os.makedirs(out, exist_ok=True)
+    api_o = os.path.join(out, "api.o")
+    cc = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+          "-c", os.path.join(CSRC, "api.cpp"), "-o", api_o]
+    res = subprocess.run(cc, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ (sanitized api.cpp) failed:\n{res.stderr}")
+    lib = os.path.join(out, "libqlora_mi355x.so")
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.cpp"]
+    link = ["g++", "-shared", "-fsanitize=address,undefined", "-o", lib, api_o] + objs + [
+        "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{res.stderr}")
+    if verbose:
+        print("built", lib)
+    return lib
+
+
 if __name__ == "__main__":
     build()

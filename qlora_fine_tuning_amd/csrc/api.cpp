@@ -83,6 +83,15 @@ WSrc src_w16(const uint16_t* w, int64_t n, int64_t k) {
   return s;
 }
 bool bad_src(const WSrc& w, int mode) { return mode == MODE_BF16 ? !w.w16 : (!w.codes || !w.absmax); }
+
+// Pointer alignment the kernels rely on (null passes: null checks are separate).
+// bf16 matrices and NF4 code arrays are read and written 16 bytes at a time,
+// fp32 arrays one value at a time, the bf16 LoRA gradients one value at a time.
+bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool al16(const void* p) { return al(p, 16); }
+bool al4(const void* p) { return al(p, 4); }
+bool al2(const void* p) { return al(p, 2); }
+bool src_aligned(const WSrc& w) { return al16(w.w16) && al16(w.codes) && al4(w.absmax); }
 // a bf16 copy of the weight (or of its transpose) lives in the workspace
 bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE_BF16; }
 
@@ -417,6 +426,7 @@ void qlora_nf4_levels(float out_host[16]) { nf4_levels_host(out_host); }
 int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream) {
   if (bad_nf4(w) || !out) return QLORA_EINVAL;
   if (!dims_ok(0, w.k, w.n)) return QLORA_ESHAPE;
+  if (!al16(w.codes) || !al4(w.absmax) || !al16(out)) return QLORA_ESHAPE;
   QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, w.n, w.k, out, w.k, 0, (hipStream_t)stream),
          "nf4_dequant");
   return QLORA_OK;
@@ -447,6 +457,8 @@ static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const ui
   if (r < 1 || r > 64 || !std::isfinite(s)) return QLORA_EINVAL;
   const int64_t k = w.k, n = w.n;
   if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
+  if (!src_aligned(w) || !al16(A) || !al16(B) || !al16(X) || !al16(Y) || !al4(U_save))
+    return QLORA_ESHAPE;
   const size_t need = linear_ws(m, k, n, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   if (m == 0) return QLORA_OK;
@@ -490,6 +502,9 @@ static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U
   if (r < 1 || r > 64 || !std::isfinite(s)) return QLORA_EINVAL;
   const int64_t k = w.k, n = w.n;
   if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
+  if (!src_aligned(w) || !al16(A) || !al16(B) || !al16(dY) || !al16(X) || !al4(U) || !al16(dX) ||
+      !al2(dA) || !al2(dB))
+    return QLORA_ESHAPE;
   const size_t need = linear_ws(m, k, n, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
@@ -621,6 +636,10 @@ static int check_mlp(const MlpSrc& w, int mode) {
   if (!dims_ok(0, d, h)) return QLORA_ESHAPE;
   if (w.gate.n != h || w.gate.k != d || w.up.n != h || w.up.k != d || w.down.n != d || w.down.k != h)
     return QLORA_ESHAPE;
+  if (!src_aligned(w.gate) || !src_aligned(w.up) || !src_aligned(w.down)) return QLORA_ESHAPE;
+  if (!al16(w.a_gate) || !al16(w.b_gate) || !al16(w.a_up) || !al16(w.b_up) || !al16(w.a_down) ||
+      !al16(w.b_down))
+    return QLORA_ESHAPE;
   return QLORA_OK;
 }
 
@@ -646,6 +665,8 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   if (m > 0 && (!X || !Y || !g_save || !u_save || !Ug || !Uu || !Ud)) return QLORA_EINVAL;
   const int64_t d = w->d, h = w->h, r = w->r;
   if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (!al16(X) || !al16(Y) || !al16(g_save) || !al16(u_save) || !al4(Ug) || !al4(Uu) || !al4(Ud))
+    return QLORA_ESHAPE;
   const size_t need = mlp_ws(m, d, h, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   if (m == 0) return QLORA_OK;
@@ -760,6 +781,10 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     return QLORA_EINVAL;
   const int64_t d = w->d, h = w->h, r = w->r;
   if (m < 0 || m >= ((int64_t)1 << 30)) return QLORA_ESHAPE;
+  if (!al16(dY) || !al16(X) || !al16(g_save) || !al16(u_save) || !al4(Ug) || !al4(Uu) ||
+      !al4(Ud) || !al16(dX) || !al2(gr->a_gate) || !al2(gr->b_gate) || !al2(gr->a_up) ||
+      !al2(gr->b_up) || !al2(gr->a_down) || !al2(gr->b_down))
+    return QLORA_ESHAPE;
   const size_t need = mlp_ws(m, d, h, r, mode);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   hipStream_t st = (hipStream_t)stream;
@@ -1006,6 +1031,8 @@ static int check_qkv(const QkvSrc& w, int mode) {
   const int64_t n[3] = {w.w[0].n, w.w[1].n, w.w[2].n};
   const int64_t d = w.w[0].k;
   if (w.w[1].k != d || w.w[2].k != d || !qkv_dims_ok(0, d, n)) return QLORA_ESHAPE;
+  for (int p = 0; p < 3; ++p)
+    if (!src_aligned(w.w[p]) || !al16(w.a[p]) || !al16(w.b[p])) return QLORA_ESHAPE;
   return QLORA_OK;
 }
 
@@ -1103,6 +1130,7 @@ static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t*
     if (!X || !U || !out[0] || !out[1] || !out[2]) return QLORA_EINVAL;
     for (int p = 0; p < 3; ++p)
       if (!pitch_ok(out[p], ld[p], n[p])) return QLORA_ESHAPE;
+    if (!al16(X) || !al4(U)) return QLORA_ESHAPE;
   }
   if (int e = check_ws(ws, ws_bytes, qkv_ws(m, d, n, r))) return e;
   if (m == 0) return QLORA_OK;
@@ -1184,7 +1212,10 @@ static int qkv_bwd_impl(const uint16_t* const dy[3], const int64_t lddy[3], cons
     if (!X || !U || !dy[0] || !dy[1] || !dy[2]) return QLORA_EINVAL;
     for (int p = 0; p < 3; ++p)
       if (!pitch_ok(dy[p], lddy[p], n[p])) return QLORA_ESHAPE;
+    if (!al16(X) || !al4(U) || !al16(dX)) return QLORA_ESHAPE;
   }
+  for (int p = 0; p < 3; ++p)
+    if (!al2(ga[p]) || !al2(gb[p])) return QLORA_ESHAPE;
   if (int e = check_ws(ws, ws_bytes, qkv_ws(m, d, n, r))) return e;
   hipStream_t st = (hipStream_t)stream;
   if (m == 0) {
@@ -1321,7 +1352,6 @@ int qlora_qkv16_bwd(const uint16_t* dQ, int64_t ld_dq, const uint16_t* dK, int64
 }
 
 // ---------------------------------------- RMS layernorm, RoPE, cross entropy --
-static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int qlora_rmsnorm_fwd(const uint16_t* X, int64_t m, int64_t d, const uint16_t* w, float eps,
                       int gemma, uint16_t* Y, float* rstd, void* stream) {

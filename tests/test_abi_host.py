@@ -131,7 +131,7 @@ def test_linear_validation_errors(L):
 def test_mlp_validation_errors(L):
     ws = ctypes.c_void_p(0x100000)
     big = 1 << 40
-    w = _lib.MlpWeights(_nf4(128, 64), _nf4(128, 64), _nf4(64, 128), 1, 1, 1, 1, 1, 1, 64, 128, 8,
+    w = _lib.MlpWeights(_nf4(128, 64), _nf4(128, 64), _nf4(64, 128), *([0x3000] * 6), 64, 128, 8,
                         1.0, 0)
     f = L.qlora_mlp_fwd
     args = lambda ww: (FAKE, 8, ctypes.byref(ww), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None)  # noqa: E731
@@ -149,6 +149,42 @@ def test_mlp_validation_errors(L):
     assert f(*args(bad)) == -1
     assert f(FAKE, 0, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == 0
     assert f(FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == -1
+    # misaligned: a bf16 matrix off its 16-byte grid, an fp32 U off 4 bytes,
+    # NF4 codes off 16 or absmax off 4 bytes, a LoRA factor off 16 bytes
+    odd8, odd2 = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    assert f(odd8, 8, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == -2
+    assert f(FAKE, 8, ctypes.byref(w), FAKE, odd8, FAKE, FAKE, FAKE, FAKE, 0, ws, big, None) == -2
+    assert f(FAKE, 8, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, odd2, FAKE, 0, ws, big, None) == -2
+    for field, val in (("gate", _lib.Nf4(0x1008, 0x2000, 128, 64)), ("down", _lib.Nf4(0x1000, 0x2002, 64, 128)),
+                       ("a_up", 0x3008)):
+        bad = _lib.MlpWeights.from_buffer_copy(w)
+        setattr(bad, field, val)
+        assert f(*args(bad)) == -2, field
+
+
+def test_alignment_errors_linear_and_dequant(L):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 40
+    odd8, odd2 = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    f = L.qlora_linear_fwd
+    ok = (FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, FAKE, 0, ws, big, None)
+    for i, bad in ((0, odd8), (3, odd8), (4, odd8), (7, odd8), (8, odd2)):
+        a = list(ok)
+        a[i] = bad
+        assert f(*a) == -2, i
+    a = list(ok)
+    a[2] = _lib.Nf4(0x1008, 0x2000, 64, 64)
+    assert f(*a) == -2
+    b = L.qlora_linear_bwd
+    okb = (FAKE, FAKE, FAKE, 8, _nf4(64, 64), FAKE, FAKE, 8, 1.0, FAKE, FAKE, FAKE, 0, ws, big, None)
+    for i, bad in ((0, odd8), (1, odd8), (2, odd2), (9, odd8), (10, ctypes.c_void_p(0x1001)),
+                   (11, ctypes.c_void_p(0x1001))):
+        a = list(okb)
+        a[i] = bad
+        assert b(*a) == -2, i
+    assert L.qlora_nf4_dequant(_lib.Nf4(0x1008, 0x2000, 64, 64), FAKE, None) == -2
+    assert L.qlora_nf4_dequant(_lib.Nf4(0x1000, 0x2002, 64, 64), FAKE, None) == -2
+    assert L.qlora_nf4_dequant(_nf4(64, 64), odd8, None) == -2
 
 
 def test_probe_validation_errors(L):
@@ -252,3 +288,46 @@ def test_norm_rope_xent_validation_errors(L):
     assert L.qlora_cross_entropy_fused(F_, 104, 4, 100, F_, f(float("nan")), F_, F_, F_, F_, F_, 104,
                                        None) == -1
     assert L.qlora_cross_entropy_fused(F_, 104, 4, 100, F_, f(1.0), F_, F_, F_, F_, F_, 100, None) == -2
+
+
+_NODEV_SCRIPT = r"""
+import ctypes, sys
+hip = ctypes.CDLL("libamdhip64.so")
+n = ctypes.c_int(0)
+hip.hipGetDeviceCount(ctypes.byref(n))
+if n.value > 0:
+    print("SKIP device visible")
+    sys.exit(0)
+from qlora_fine_tuning_amd import _lib
+L = _lib.lib()
+FAKE = ctypes.c_void_p(0x1000)
+ws = ctypes.c_void_p(0x100000)
+nf = lambda n, k: _lib.Nf4(0x1000, 0x2000, n, k)
+out = []
+out.append(L.qlora_nf4_dequant(nf(64, 64), FAKE, None))
+out.append(L.qlora_linear_fwd(FAKE, 8, nf(64, 64), FAKE, FAKE, 8, 1.0, FAKE, FAKE, 0, ws, 1 << 40, None))
+w = _lib.MlpWeights(nf(128, 64), nf(128, 64), nf(64, 128), *([0x3000] * 6), 64, 128, 8, 1.0, 0)
+out.append(L.qlora_mlp_fwd(FAKE, 8, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ws, 1 << 40, None))
+print("RC", *out)
+print("MSG", L.qlora_last_error().decode())
+"""
+
+
+def test_no_device_returns_ehip():
+    """With no GPU visible, a compute call fails at its first HIP call and
+    returns QLORA_EHIP with the failing step and HIP's message in
+    qlora_last_error (nothing is dereferenced: the pointers are never used).
+    Runs in a child process with every device hidden; it checks the device
+    count itself and skips the calls if one is still visible."""
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", PYTHONPATH=ROOT)
+    res = subprocess.run([sys.executable, "-c", _NODEV_SCRIPT], env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    if "SKIP" in res.stdout:
+        pytest.skip("a device is still visible")
+    rc = [ln for ln in res.stdout.splitlines() if ln.startswith("RC")][0].split()[1:]
+    assert rc == ["-4", "-4", "-4"]
+    msg = [ln for ln in res.stdout.splitlines() if ln.startswith("MSG")][0]
+    assert "mlp_fwd" in msg and "device" in msg
