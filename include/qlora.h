@@ -35,9 +35,16 @@
  *     failure returns QLORA_EHIP; qlora_last_error() then gives the HIP
  *     message (per thread).
  *   - Shape limits: k, n (and d, h) multiples of 64; m >= 0; 1 <= r <= 64
- *     (1 <= r <= 32 for the MLP). m == 0 writes only the LoRA gradients (as
- *     zeros); the per-token tensors may then be NULL. Output buffers must not
- *     alias inputs.
+ *     (the pages call 16 and 64 the usual ranks; Mistral benchmark page,
+ *     items 10-11). m == 0 writes only the LoRA gradients (as zeros); the
+ *     per-token tensors may then be NULL. Output buffers must not alias
+ *     inputs.
+ *   - Alignment: every bf16 matrix (X, Y, dY, dX, g, u, 16-bit base weights,
+ *     LoRA factors A and B) and every NF4 code array starts on a 16-byte
+ *     boundary; absmax and the fp32 U / T tensors on 4 bytes; the bf16 LoRA
+ *     gradients dA, dB on 2 bytes. A pointer off its boundary returns
+ *     QLORA_ESHAPE before anything is enqueued (device allocations and
+ *     contiguous tensors at offset 0 always qualify).
  *   - Results are deterministic: two identical calls give identical bits
  *     (no floating-point atomics; fixed reduction order).
  *   - Calls that share one workspace buffer must not overlap in time.

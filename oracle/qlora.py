@@ -120,6 +120,30 @@ def mlp_bwd(dY, X, saved, Wg, Wu, Wd, Ag, Bg, Au, Bu, Ad, Bd, s, act="swiglu"):
     return dict(dX=dXg + dXu, dAg=dAg, dBg=dBg, dAu=dAu, dBu=dBu, dAd=dAd, dBd=dBd)
 
 
+def mlp_lora_grads(X, dY, Wg, Wu, Wd, Ag, Bg, Au, Bu, Ad, Bd, s, act="swiglu"):
+    """The six LoRA weight gradients of the gated MLP alone.
+
+    The same definitions as mlp_fwd followed by mlp_bwd, with the two
+    products that feed only Y (H Wd^T) and dX (dg Wg, du Wu) left out. Every
+    gradient is a sum over tokens, so a long batch may be passed in row
+    blocks and the block results added. Returns dAg, dBg, dAu, dBu, dAd, dBd.
+    """
+    f, fprime = ACTS[act]
+    Ug, Uu = X @ Ag.T, X @ Au.T
+    g = X @ Wg.T + s * (Ug @ Bg.T)
+    u = X @ Wu.T + s * (Uu @ Bu.T)
+    a = f(g)
+    H = a * u
+    Ud = H @ Ad.T
+    Td = dY @ Bd
+    dH = dY @ Wd + s * (Td @ Ad)
+    dg = dH * u * fprime(g)
+    du = dH * a
+    Tg, Tu = dg @ Bg, du @ Bu
+    return dict(dAg=s * (Tg.T @ X), dBg=s * (dg.T @ Ug), dAu=s * (Tu.T @ X), dBu=s * (du.T @ Uu),
+                dAd=s * (Td.T @ H), dBd=s * (dY.T @ Ud))
+
+
 def mlp_rows(rows, X, dY, Wg, Wu, Wd, Ag, Bg, Au, Bu, Ad, Bd, s, act="swiglu"):
     """Per-token outputs for a subset of rows: Y, g, u, Ug, Uu, Ud and dX.
 

@@ -60,6 +60,15 @@ struct Carver {
 
 inline int64_t ceil16(int64_t x) { return (x + 15) / 16 * 16; }
 
+// The MLP's gate and up products share one K-extension. With 2r <= 64 one
+// row product forms [U_g | U_u] and the columns are
+// [hi(sU_g) hi(sU_u) | lo(sU_g) lo(sU_u) | 0 ...] (ceil16(4r) wide); above
+// that (r > 32) each projection has its own row product and its own
+// ceil16(2r)-wide segment [hi(sU_g) lo(sU_g) 0.. | hi(sU_u) lo(sU_u) 0..].
+// The same holds for [T_g | T_u] in the backward.
+inline bool mlp_wide(int64_t r) { return 2 * r > 64; }
+inline int64_t mlp_ke_gu(int64_t r) { return mlp_wide(r) ? 2 * ceil16(2 * r) : ceil16(4 * r); }
+
 bool bad_nf4(const qlora_nf4& w) { return !w.codes || !w.absmax; }
 
 // Base-weight source: NF4 (codes + absmax) or, in MODE_BF16, a bf16 matrix
@@ -187,7 +196,7 @@ struct MlpFwdWs {
 };
 
 size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpFwdWs* w) {
-  const int64_t KEgu = ceil16(4 * r), KEd = ceil16(2 * r);
+  const int64_t KEgu = mlp_ke_gu(r), KEd = ceil16(2 * r);
   MlpFwdWs t;
   t.lgu = c.take<uint16_t>(2 * r * d);
   t.bextgu = c.take<uint16_t>(2 * h * KEgu);
@@ -221,7 +230,7 @@ struct MlpBwdWs {
 };
 
 size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpBwdWs* w) {
-  const int64_t KEgu = ceil16(4 * r), KEd = ceil16(2 * r);
+  const int64_t KEgu = mlp_ke_gu(r), KEd = ceil16(2 * r);
   const int64_t chunks = colreduce_chunks((int)std::max<int64_t>(m, 1));
   MlpBwdWs t;
   t.ltd = c.take<uint16_t>(r * d);
@@ -630,7 +639,7 @@ static MlpSrc mlp_src16(const qlora_mlp16_weights* w) {
 static int check_mlp(const MlpSrc& w, int mode) {
   if (bad_src(w.gate, mode) || bad_src(w.up, mode) || bad_src(w.down, mode)) return QLORA_EINVAL;
   if (!w.a_gate || !w.b_gate || !w.a_up || !w.b_up || !w.a_down || !w.b_down) return QLORA_EINVAL;
-  if (w.r < 1 || w.r > 32 || !std::isfinite(w.s)) return QLORA_EINVAL;
+  if (w.r < 1 || w.r > 64 || !std::isfinite(w.s)) return QLORA_EINVAL;
   if (w.act != QLORA_ACT_SWIGLU && w.act != QLORA_ACT_GEGLU_TANH) return QLORA_EINVAL;
   const int64_t d = w.d, h = w.h;
   if (!dims_ok(0, d, h)) return QLORA_ESHAPE;
@@ -649,12 +658,12 @@ static size_t mlp_ws(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
 }
 
 size_t qlora_mlp_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r, int mode) {
-  if (!dims_ok(m, d, h) || r < 1 || r > 32 || !valid_mode(mode)) return 0;
+  if (!dims_ok(m, d, h) || r < 1 || r > 64 || !valid_mode(mode)) return 0;
   return mlp_ws(m, d, h, r, resolve_mode(mode));
 }
 
 size_t qlora_mlp16_workspace_bytes(int64_t m, int64_t d, int64_t h, int64_t r) {
-  if (!dims_ok(m, d, h) || r < 1 || r > 32) return 0;
+  if (!dims_ok(m, d, h) || r < 1 || r > 64) return 0;
   return mlp_ws(m, d, h, r, MODE_BF16);
 }
 
@@ -674,7 +683,9 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   Carver c(ws);
   MlpFwdWs t;
   plan_mlp_fwd(c, m, d, h, r, mode, &t);
-  const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
+  const int KEgu = (int)mlp_ke_gu(r), KEd = (int)ceil16(2 * r);
+  const bool wide = mlp_wide(r);
+  const int E = (int)ceil16(2 * r);   // wide: one projection's segment
   const float s = w->s;
 
   // LoRA operand layouts (launched below: on the helper stream when staged,
@@ -682,19 +693,30 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   // dequant; every reader of these layouts waits for the helper stream)
   PrepJobs fwd_jobs;
   {  // Lgu = [Ag; Au]; Bext_gu rows interleaved by 32 (gate: [Bg 0 Bg 0 0..],
-     // up: [0 Bu 0 Bu 0..]); Bext_d = [Bd | Bd | 0]
+     // up: [0 Bu 0 Bu 0..]; wide: gate [Bg Bg 0.. | 0..], up [0.. | Bu Bu 0..]);
+     // Bext_d = [Bd | Bd | 0]
     PrepJobs J;
     J.copy(w->a_gate, d, 1, r, d, t.lgu, d, 1);
     J.copy(w->a_up, d, 1, r, d, t.lgu + r * d, d, 1);
-    J.copy(w->b_gate, r, 1, h, r, t.bextgu, KEgu, 1, 1);
-    J.zero(h, r, t.bextgu + r, KEgu, 1, 1);
-    J.copy(w->b_gate, r, 1, h, r, t.bextgu + 2 * r, KEgu, 1, 1);
-    J.zero(h, KEgu - 3 * r, t.bextgu + 3 * r, KEgu, 1, 1);
-    J.zero(h, r, t.bextgu, KEgu, 1, 2);
-    J.copy(w->b_up, r, 1, h, r, t.bextgu + r, KEgu, 1, 2);
-    J.zero(h, r, t.bextgu + 2 * r, KEgu, 1, 2);
-    J.copy(w->b_up, r, 1, h, r, t.bextgu + 3 * r, KEgu, 1, 2);
-    J.zero(h, KEgu - 4 * r, t.bextgu + 4 * r, KEgu, 1, 2);
+    if (!wide) {
+      J.copy(w->b_gate, r, 1, h, r, t.bextgu, KEgu, 1, 1);
+      J.zero(h, r, t.bextgu + r, KEgu, 1, 1);
+      J.copy(w->b_gate, r, 1, h, r, t.bextgu + 2 * r, KEgu, 1, 1);
+      J.zero(h, KEgu - 3 * r, t.bextgu + 3 * r, KEgu, 1, 1);
+      J.zero(h, r, t.bextgu, KEgu, 1, 2);
+      J.copy(w->b_up, r, 1, h, r, t.bextgu + r, KEgu, 1, 2);
+      J.zero(h, r, t.bextgu + 2 * r, KEgu, 1, 2);
+      J.copy(w->b_up, r, 1, h, r, t.bextgu + 3 * r, KEgu, 1, 2);
+      J.zero(h, KEgu - 4 * r, t.bextgu + 4 * r, KEgu, 1, 2);
+    } else {
+      J.copy(w->b_gate, r, 1, h, r, t.bextgu, KEgu, 1, 1);
+      J.copy(w->b_gate, r, 1, h, r, t.bextgu + r, KEgu, 1, 1);
+      J.zero(h, KEgu - 2 * r, t.bextgu + 2 * r, KEgu, 1, 1);
+      J.zero(h, E, t.bextgu, KEgu, 1, 2);
+      J.copy(w->b_up, r, 1, h, r, t.bextgu + E, KEgu, 1, 2);
+      J.copy(w->b_up, r, 1, h, r, t.bextgu + E + r, KEgu, 1, 2);
+      J.zero(h, E - 2 * r, t.bextgu + E + 2 * r, KEgu, 1, 2);
+    }
     J.copy(w->b_down, r, 1, d, r, t.bextd, KEd, 1);
     J.copy(w->b_down, r, 1, d, r, t.bextd + r, KEd, 1);
     J.zero(d, KEd - 2 * r, t.bextd + 2 * r, KEd, 1);
@@ -706,10 +728,17 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   const bool staged = staged_like(mode);
   const bool w16 = mode == MODE_BF16;
   Side side(st);
-  // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections)
+  // [Ug | Uu] = X [Ag; Au]^T  (one read of X for both projections; two when
+  // 2r is wider than one row product)
   auto row_u = [&](hipStream_t q) {
-    return launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
-                         t.uextgu, KEgu, KEgu, t.rpart, q);
+    if (!wide)
+      return launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
+                           t.uextgu, KEgu, KEgu, t.rpart, q);
+    hipError_t e = launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)r, s, Ug, nullptr, (int)r, r,
+                                 t.uextgu, KEgu, E, t.rpart, q);
+    if (e != hipSuccess) return e;
+    return launch_rowdot(X, d, t.lgu + r * d, d, (int)m, (int)d, (int)r, s, Uu, nullptr, (int)r, r,
+                         t.uextgu + E, KEgu, E, t.rpart, q);
   };
   if (staged) {
     QL_TRY(side.open(), "mlp_fwd: helper stream");
@@ -802,7 +831,9 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   Carver c(ws);
   MlpBwdWs t;
   plan_mlp_bwd(c, m, d, h, r, mode, &t);
-  const int KEgu = (int)ceil16(4 * r), KEd = (int)ceil16(2 * r);
+  const int KEgu = (int)mlp_ke_gu(r), KEd = (int)ceil16(2 * r);
+  const bool wide = mlp_wide(r);
+  const int E = (int)ceil16(2 * r);   // wide: one projection's segment
   const int chunks = colreduce_chunks((int)m);
   const float s = w->s;
 
@@ -810,7 +841,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   // helper stream forks: everything after reads them)
   PrepJobs bwd_jobs;
   {  // ltd = Bd^T; bextdh = [Ad^T | Ad^T | 0]; ltgu = blockdiag(Bg^T, Bu^T);
-     // bextdx = [Ag^T | Au^T | Ag^T | Au^T | 0]
+     // bextdx = [Ag^T | Au^T | Ag^T | Au^T | 0] (wide: [Ag^T Ag^T 0.. | Au^T Au^T 0..])
     PrepJobs J;
     J.copy(w->b_down, 1, r, r, d, t.ltd, d, 1);
     J.copy(w->a_down, 1, h, h, r, t.bextdh, KEd, 1);
@@ -820,11 +851,20 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     J.zero(r, h, t.ltgu + h, 2 * h, 1);
     J.zero(r, h, t.ltgu + r * 2 * h, 2 * h, 1);
     J.copy(w->b_up, 1, r, r, h, t.ltgu + r * 2 * h + h, 2 * h, 1);
-    J.copy(w->a_gate, 1, d, d, r, t.bextdx, KEgu, 1);
-    J.copy(w->a_up, 1, d, d, r, t.bextdx + r, KEgu, 1);
-    J.copy(w->a_gate, 1, d, d, r, t.bextdx + 2 * r, KEgu, 1);
-    J.copy(w->a_up, 1, d, d, r, t.bextdx + 3 * r, KEgu, 1);
-    J.zero(d, KEgu - 4 * r, t.bextdx + 4 * r, KEgu, 1);
+    if (!wide) {
+      J.copy(w->a_gate, 1, d, d, r, t.bextdx, KEgu, 1);
+      J.copy(w->a_up, 1, d, d, r, t.bextdx + r, KEgu, 1);
+      J.copy(w->a_gate, 1, d, d, r, t.bextdx + 2 * r, KEgu, 1);
+      J.copy(w->a_up, 1, d, d, r, t.bextdx + 3 * r, KEgu, 1);
+      J.zero(d, KEgu - 4 * r, t.bextdx + 4 * r, KEgu, 1);
+    } else {
+      J.copy(w->a_gate, 1, d, d, r, t.bextdx, KEgu, 1);
+      J.copy(w->a_gate, 1, d, d, r, t.bextdx + r, KEgu, 1);
+      J.zero(d, E - 2 * r, t.bextdx + 2 * r, KEgu, 1);
+      J.copy(w->a_up, 1, d, d, r, t.bextdx + E, KEgu, 1);
+      J.copy(w->a_up, 1, d, d, r, t.bextdx + E + r, KEgu, 1);
+      J.zero(d, E - 2 * r, t.bextdx + E + 2 * r, KEgu, 1);
+    }
     bwd_jobs = J;
   }
   // The column reductions (dB, dA) and the transposed dequant of the gate/up
@@ -911,20 +951,42 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     QL_TRY(launch_rowdot_finish(t.rpart, gemm_rowprod_splits((int)h), (int)m, (int)(2 * r), s,
                                 t.tgu, nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, st),
            "mlp_bwd: Tg, Tu");
-  else
+  else if (!wide)
     QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s,
                          t.tgu, nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
            "mlp_bwd: Tg, Tu");
+  else {   // Tg = dg Bg, Tu = du Bu: one row product each, own K-extension segment
+    QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)h, (int)r, s, t.tgu, nullptr,
+                         (int)r, 2 * r, t.textgu, KEgu, E, t.rpart, st),
+           "mlp_bwd: Tg");
+    QL_TRY(launch_rowdot(t.dgu + h, 2 * h, t.ltgu + r * 2 * h + h, 2 * h, (int)m, (int)h, (int)r, s,
+                         t.tgu + r, nullptr, (int)r, 2 * r, t.textgu + E, KEgu, E, t.rpart, st),
+           "mlp_bwd: Tu");
+  }
   QL_TRY(side.fork(4), "mlp_bwd: fork");
   // dAg = s Tg^T X ; dAu = s Tu^T X (helper stream, beside the dX GEMM)
-  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),
-                          t.part, ss),
-         "mlp_bwd: dAg, dAu partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), 0, (int)r, s, gr->a_gate, 1, d, ss),
-         "mlp_bwd: dAg");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), (int)r, (int)r, s, gr->a_up, 1,
-                                 d, ss),
-         "mlp_bwd: dAu");
+  if (!wide) {
+    QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)(2 * r),
+                            t.part, ss),
+           "mlp_bwd: dAg, dAu partials");
+    QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), 0, (int)r, s, gr->a_gate, 1,
+                                   d, ss),
+           "mlp_bwd: dAg");
+    QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)(2 * r), (int)r, (int)r, s, gr->a_up,
+                                   1, d, ss),
+           "mlp_bwd: dAu");
+  } else {   // 2r wider than one column reduction: one per projection
+    QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu, 2 * r, (int)r, t.part,
+                            ss),
+           "mlp_bwd: dAg partials");
+    QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, gr->a_gate, 1, d, ss),
+           "mlp_bwd: dAg");
+    QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.tgu + r, 2 * r, (int)r,
+                            t.part, ss),
+           "mlp_bwd: dAu partials");
+    QL_TRY(launch_colreduce_finish(t.part, chunks, (int)d, (int)r, 0, (int)r, s, gr->a_up, 1, d, ss),
+           "mlp_bwd: dAu");
+  }
   // dX = [dg | du] [Wg; Wu] + s [Tg | Tu] [Ag; Au]
   if (dX) {
     GemmArgs g2 = gemm_args();

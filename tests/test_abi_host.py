@@ -64,7 +64,8 @@ def test_workspace_queries(L):
     assert L.qlora_linear_workspace_bytes(8, 64, 64, 0, 0) == 0
     assert L.qlora_linear_workspace_bytes(8, 64, 64, 65, 0) == 0
     assert L.qlora_linear_workspace_bytes(8, 64, 64, 8, 7) == 0
-    assert L.qlora_mlp_workspace_bytes(8, 64, 64, 33, 0) == 0
+    assert L.qlora_mlp_workspace_bytes(8, 64, 64, 65, 0) == 0
+    assert L.qlora_mlp_workspace_bytes(8, 64, 64, 64, 0) > 0
     # staged keeps a bf16 copy of the weight, fused does not
     assert L.qlora_mlp_workspace_bytes(8192, 4096, 11008, 16, 2) >= L.qlora_mlp_workspace_bytes(
         8192, 4096, 11008, 16, 1)
@@ -139,7 +140,7 @@ def test_mlp_validation_errors(L):
     bad.act = 5
     assert f(*args(bad)) == -1
     bad = _lib.MlpWeights.from_buffer_copy(w)
-    bad.r = 40
+    bad.r = 65
     assert f(*args(bad)) == -1
     bad = _lib.MlpWeights.from_buffer_copy(w)
     bad.down = _nf4(64, 64)          # down must be [d][h]
@@ -210,7 +211,8 @@ def test_w16_validation_errors(L):
     assert L.qlora_linear16_fwd(FAKE, 64, FAKE, 192, 128, FAKE, FAKE, 8, ctypes.c_float(1.0),
                                 FAKE, FAKE, FAKE, 256, None) == -3
     assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 8) > 0
-    assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 33) == 0          # MLP rank limit
+    assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 64) > 0
+    assert L.qlora_mlp16_workspace_bytes(64, 128, 192, 65) == 0          # MLP rank limit
     w = _lib.Mlp16Weights(None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
                           128, 192, 8, 1.0, 0)
     assert L.qlora_mlp16_fwd(FAKE, 64, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,

@@ -142,3 +142,29 @@ def test_per_row_helper_matches_full():
     assert np.allclose(pr["dX"], gr["dX"][rows], rtol=1e-13, atol=1e-14)
     for k in ("g", "u", "Ug", "Uu", "Ud"):
         assert np.allclose(pr[k], sv[k][rows], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_lora_grads_helper_matches_torch_autograd_and_adds_over_blocks(act):
+    """mlp_lora_grads (the six LoRA gradients alone, for long batches in row
+    blocks) against torch fp64 autograd of <dY, Y>, and the sum of its results
+    over two row blocks against the whole batch."""
+    X, W, L, dY = _mlp_case(m=10, d=32, h=48, r=3, seed=5)
+    s = 1.25
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in L.items()}
+    tX = torch.tensor(X)
+    Wt = {k: torch.tensor(v) for k, v in W.items()}
+    actf = (torch.nn.functional.silu if act == "swiglu"
+            else (lambda z: torch.nn.functional.gelu(z, approximate="tanh")))
+    g = tX @ Wt["Wg"].T + s * (tX @ t["Ag"].T) @ t["Bg"].T
+    u = tX @ Wt["Wu"].T + s * (tX @ t["Au"].T) @ t["Bu"].T
+    H = actf(g) * u
+    Y = H @ Wt["Wd"].T + s * (H @ t["Ad"].T) @ t["Bd"].T
+    (Y * torch.tensor(dY)).sum().backward()
+    args = (W["Wg"], W["Wu"], W["Wd"], L["Ag"], L["Bg"], L["Au"], L["Bu"], L["Ad"], L["Bd"], s, act)
+    full = Q.mlp_lora_grads(X, dY, *args)
+    for k in L:
+        assert np.allclose(full["d" + k], t[k].grad.numpy(), rtol=1e-11, atol=1e-12), k
+    parts = [Q.mlp_lora_grads(X[a:b], dY[a:b], *args) for a, b in ((0, 3), (3, 10))]
+    for k in full:
+        assert np.allclose(parts[0][k] + parts[1][k], full[k], rtol=1e-12, atol=1e-13), k
