@@ -172,6 +172,29 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w,
                      uint16_t* Y, float* U_save, int mode,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* No-allocation variant of qlora_linear_fwd, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same computation, arguments, layouts, modes and errors as
+ * qlora_linear_fwd, without ws / ws_bytes. Its scratch is a device array
+ * inside the library, qlora_linear_fwd_noalloc_max_bytes() bytes (64 MiB) on
+ * every GPU the library runs on, held from the library's load until the
+ * process ends. A call whose forward needs more scratch than that (the
+ * forward's share of qlora_linear_workspace_bytes(): in staged mode mostly
+ * the bf16 weight copy, n * k * 2 bytes, plus fp32 K-split partials when the
+ * output has fewer than 256 tiles of 256 x 256) returns QLORA_EWORKSPACE
+ * before anything is enqueued, and qlora_last_error gives both sizes. The
+ * 8192-token Llama-7B q_proj fits in both modes (41 MiB staged). All
+ * calls on one GPU share its array and leave their contents in it: calls
+ * that overlap in time on one GPU (two streams, two threads) race, and the
+ * caller must order them. Nothing in the array needs to start at zero. The
+ * call allocates nothing (no hipMalloc / hipFree, no stream or event); its
+ * first call on a device looks up that device's copy of the array. */
+size_t qlora_linear_fwd_noalloc_max_bytes(void);
+
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t m, qlora_nf4 w,
+                             const uint16_t* A, const uint16_t* B, int64_t r, float s,
+                             uint16_t* Y, float* U_save, int mode, void* stream);
+
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U,
                      int64_t m, qlora_nf4 w,
                      const uint16_t* A, const uint16_t* B, int64_t r, float s,

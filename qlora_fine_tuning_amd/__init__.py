@@ -8,7 +8,8 @@ the library; the first call does, and fails loudly if it was not built.
 
 __all__ = [
     "NF4Weight", "MlpWeights", "version", "nf4_levels", "gemm_split_count", "nf4_dequant", "nf4_quantize",
-    "linear_workspace_bytes", "linear_fwd", "linear_bwd",
+    "linear_workspace_bytes", "linear_fwd", "linear_bwd", "linear_fwd_noalloc",
+    "linear_fwd_noalloc_max_bytes",
     "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read", "probe_mfma_peak",
     "linear16_workspace_bytes", "linear16_fwd", "linear16_bwd",
     "Mlp16Weights", "mlp16_workspace_bytes", "mlp16_fwd", "mlp16_bwd",

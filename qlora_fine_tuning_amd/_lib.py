@@ -98,6 +98,11 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_fwd.restype = ctypes.c_int
         L.qlora_linear_fwd.argtypes = [c_vp, c_i64, Nf4, c_vp, c_vp, c_i64, ctypes.c_float,
                                        c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+        L.qlora_linear_fwd_noalloc_max_bytes.restype = ctypes.c_size_t
+        L.qlora_linear_fwd_noalloc_max_bytes.argtypes = []
+        L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+        L.qlora_linear_fwd_noalloc.argtypes = [c_vp, c_i64, Nf4, c_vp, c_vp, c_i64, ctypes.c_float,
+                                               c_vp, c_vp, ctypes.c_int, c_vp]
         L.qlora_linear_bwd.restype = ctypes.c_int
         L.qlora_linear_bwd.argtypes = [c_vp, c_vp, c_vp, c_i64, Nf4, c_vp, c_vp, c_i64,
                                        ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_int, c_vp,
@@ -181,6 +186,7 @@ EXPORTED = [
     "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
     "qlora_gemm_split_count",
     "qlora_nf4_dequant", "qlora_nf4_quantize", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_fwd_noalloc_max_bytes", "qlora_linear_fwd_noalloc",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",
     "qlora_linear16_workspace_bytes", "qlora_linear16_fwd", "qlora_linear16_bwd",

@@ -159,6 +159,33 @@ def linear_fwd(X, w: NF4Weight, A, B, s: float, mode="auto", ws=None):
     return Y, U
 
 
+def linear_fwd_noalloc(X, w: NF4Weight, A, B, s: float, mode="auto", out=None):
+    """The linear forward on the library's own per-device scratch (no
+    workspace, nothing allocated by the call itself). out: optional (Y, U)
+    to write into; returns (Y [m][n] bf16, U [m][r] fp32)."""
+    m, k, n, r = X.shape[0], w.k, w.n, A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(A, "A", torch.bfloat16, (r, k))
+    _need(B, "B", torch.bfloat16, (n, r))
+    if out is None:
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=X.device)
+        U = torch.empty((m, r), dtype=torch.float32, device=X.device)
+    else:
+        Y, U = out
+        _need(Y, "Y", torch.bfloat16, (m, n))
+        _need(U, "U", torch.float32, (m, r))
+    st = _lib.lib().qlora_linear_fwd_noalloc(_ptr(X), m, w.c_struct(), _ptr(A), _ptr(B), r, float(s),
+                                             _ptr(Y), _ptr(U), _lib.MODE[mode], _stream())
+    if st == -3:
+        raise RuntimeError("qlora_linear_fwd_noalloc: " + _lib.lib().qlora_last_error().decode())
+    _lib.check(st, "qlora_linear_fwd_noalloc")
+    return Y, U
+
+
+def linear_fwd_noalloc_max_bytes() -> int:
+    return int(_lib.lib().qlora_linear_fwd_noalloc_max_bytes())
+
+
 def linear_bwd(dY, X, U, w: NF4Weight, A, B, s: float, need_dx=True, mode="auto", ws=None):
     """Returns (dX [m][k] or None, dA [r][k], dB [n][r]), all bf16."""
     m, k, n, r = X.shape[0], w.k, w.n, A.shape[0]

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora_mi355x.so")
-SOURCES = ["nf4.hip", "w16.hip", "gemm.hip", "lora.hip", "probe.hip", "fast.hip", "api.cpp"]
+SOURCES = ["nf4.hip", "w16.hip", "gemm.hip", "lora.hip", "probe.hip", "fast.hip", "scratch.hip", "api.cpp"]
 
 
 def hipcc() -> str:

@@ -442,6 +442,12 @@ int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream) {
 }
 
 // ------------------------------------------------------------ linear layer --
+// what the forward alone carves (the workspace query covers both directions)
+static size_t linear_fwd_ws(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
+  Carver a(nullptr);
+  return plan_linear_fwd(a, m, k, n, r, mode, nullptr);
+}
+
 static size_t linear_ws(int64_t m, int64_t k, int64_t n, int64_t r, int mode) {
   Carver a(nullptr), b(nullptr);
   return std::max(plan_linear_fwd(a, m, k, n, r, mode, nullptr), plan_linear_bwd(b, m, k, n, r, mode, nullptr));
@@ -457,19 +463,28 @@ size_t qlora_linear16_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t r
   return linear_ws(m, k, n, r, MODE_BF16);
 }
 
-// mode: QLORA_DEQUANT_STAGED, QLORA_DEQUANT_FUSED or MODE_BF16 (resolved)
-static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const uint16_t* A,
-                           const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save,
-                           int mode, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of the linear forward (everything but the workspace).
+static int linear_fwd_check(const uint16_t* X, int64_t m, const WSrc& w, const uint16_t* A,
+                            const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save,
+                            int mode) {
   if (!A || !B || bad_src(w, mode)) return QLORA_EINVAL;
   if (m > 0 && (!X || !Y)) return QLORA_EINVAL;   // per-token tensors may be NULL when m == 0
   if (r < 1 || r > 64 || !std::isfinite(s)) return QLORA_EINVAL;
-  const int64_t k = w.k, n = w.n;
-  if (!dims_ok(m, k, n)) return QLORA_ESHAPE;
+  if (!dims_ok(m, w.k, w.n)) return QLORA_ESHAPE;
   if (!src_aligned(w) || !al16(A) || !al16(B) || !al16(X) || !al16(Y) || !al4(U_save))
     return QLORA_ESHAPE;
-  const size_t need = linear_ws(m, k, n, r, mode);
-  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  return QLORA_OK;
+}
+
+// mode: QLORA_DEQUANT_STAGED, QLORA_DEQUANT_FUSED or MODE_BF16 (resolved).
+// traced: the base GEMM may be timed by the optional launch trace (which
+// creates HIP events); the no-allocation entry point passes false.
+static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const uint16_t* A,
+                           const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save,
+                           int mode, void* ws, size_t ws_bytes, void* stream, bool traced = true) {
+  if (int e = linear_fwd_check(X, m, w, A, B, r, s, Y, U_save, mode)) return e;
+  const int64_t k = w.k, n = w.n;
+  if (int e = check_ws(ws, ws_bytes, linear_fwd_ws(m, k, n, r, mode))) return e;
   if (m == 0) return QLORA_OK;
   hipStream_t st = (hipStream_t)stream;
   Carver c(ws);
@@ -498,7 +513,7 @@ static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const ui
   g.M = (int)m; g.N = (int)n; g.K = (int)k; g.KE = KE;
   g.epi = EPI_STORE; g.C = Y; g.ldc = n;
   use_splitk(g, t.kpart);
-  QL_TRY(run_gemm(g, r, st), "linear_fwd: GEMM");
+  QL_TRY(traced ? run_gemm(g, r, st) : launch_gemm(g, st), "linear_fwd: GEMM");
   return QLORA_OK;
 }
 
@@ -581,6 +596,29 @@ int qlora_linear_fwd(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* 
   if (!valid_mode(mode)) return QLORA_EINVAL;
   return linear_fwd_impl(X, m, src_nf4(w), A, B, r, s, Y, U_save, resolve_mode(mode), ws, ws_bytes,
                          stream);
+}
+
+size_t qlora_linear_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t m, qlora_nf4 w, const uint16_t* A,
+                             const uint16_t* B, int64_t r, float s, uint16_t* Y, float* U_save,
+                             int mode, void* stream) {
+  if (!valid_mode(mode)) return QLORA_EINVAL;
+  const int md = resolve_mode(mode);
+  const WSrc src = src_nf4(w);
+  if (int e = linear_fwd_check(X, m, src, A, B, r, s, Y, U_save, md)) return e;
+  const size_t need = linear_fwd_ws(m, w.k, w.n, r, md);
+  if (need > kScratchBytes) {
+    g_last_error = "linear_fwd_noalloc: this call needs " + std::to_string(need) +
+                   " bytes of scratch, more than the " + std::to_string(kScratchBytes) +
+                   " the library holds per device (use qlora_linear_fwd with a workspace)";
+    return QLORA_EWORKSPACE;
+  }
+  if (m == 0) return QLORA_OK;
+  void* ws = nullptr;
+  QL_TRY(scratch_device_ptr(&ws), "linear_fwd_noalloc: scratch address");
+  return linear_fwd_impl(X, m, src, A, B, r, s, Y, U_save, md, ws, kScratchBytes, stream, false);
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* U, int64_t m, qlora_nf4 w,

@@ -213,6 +213,13 @@ hipError_t launch_xent_bwd(const uint16_t* X, int64_t ld, int64_t m, int64_t V, 
                            const float* lse, const float* dloss, const int32_t* n_valid, uint16_t* dX,
                            int64_t ldd, hipStream_t stream);
 
+// ---- scratch of the no-allocation entry point (scratch.hip) ----
+// A file-scope device array of kScratchBytes per GPU, held from module load
+// until the process ends; scratch_device_ptr gives the current device's copy
+// (looked up once per device). Calls that use it must not overlap on a GPU.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_device_ptr(void** out);
+
 // ---- diagnostics (probe.hip) ----
 // Sustained dense bf16 MFMA TFLOP/s and the shader clock (GHz) under that
 // load; synchronizes the host.
