@@ -35,6 +35,10 @@ Readings taken where the pages are silent
 * Dequant: W = bf16_rne(fp32_rne(L[c] * absmax)). The product is exact in
   fp64 (24 x 24 significant bits), then rounded to fp32, then to bf16; the
   order of the two roundings is part of the contract.
+* Double quantization (optional): the absmax array itself stored as 8-bit
+  codes with one fp32 scale and one fp32 offset per 256 values; see
+  absmax_dq_quantize. A double-quantized weight dequantizes with the
+  reconstructed absmax in place of the stored one.
 """
 from __future__ import annotations
 
@@ -143,3 +147,51 @@ def dequant_bf16_bits(packed: np.ndarray, absmax: np.ndarray) -> np.ndarray:
 def dequant_f64(packed: np.ndarray, absmax: np.ndarray) -> np.ndarray:
     """Dequantized weights as fp64 values (exactly the bf16 weights)."""
     return bf16_bits_to_f64(dequant_bf16_bits(packed, absmax))
+
+
+# ------------------------------------------------ double quantization -----
+# The pages link the QLoRA paper for the 4-bit format but print no
+# second-level format. Reading (listed in the design notes): the first-level
+# constants (the fp32 absmax array, flattened row-major) are quantized again
+# in groups of DQ_GROUP = 256 consecutive values (the last group may be
+# shorter) with the paper's own absmax scheme, applied to the constants after
+# subtracting their mean (they are all >= 0, so the mean centres them):
+#   offset  mu = fp32( (a_0 + a_1 + ... + a_{n-1}) / n )   fp64 sum, index order
+#   scale   c  = fp32( max_i |a_i - mu| / 127 )             fp64
+#   code    q_i = clamp(rne((a_i - mu) / c), -127, 127)    int8; all 0 if c == 0
+#   value   a'_i = fp32( fp32(q_i * c) + mu )               two fp32 roundings
+# Storage: 1 byte per 64-weight block plus 8 bytes per 256 blocks.
+DQ_GROUP = 256
+
+
+def absmax_dq_quantize(absmax):
+    """fp32 absmax (any shape, read flattened) -> (q int8 [n], scale f32 [g], offset f32 [g])."""
+    a = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    n = a.size
+    ng = (n + DQ_GROUP - 1) // DQ_GROUP
+    q = np.zeros(n, dtype=np.int8)
+    scale = np.zeros(ng, dtype=np.float32)
+    offset = np.zeros(ng, dtype=np.float32)
+    for j in range(ng):
+        grp = a[j * DQ_GROUP:(j + 1) * DQ_GROUP].astype(np.float64)
+        total = 0.0
+        for v in grp:                      # plain sequential fp64 sum
+            total += float(v)
+        mu = np.float32(total / grp.size)
+        dev = np.abs(grp - np.float64(mu))
+        c = np.float32(dev.max() / 127.0)
+        offset[j], scale[j] = mu, c
+        if c > 0:
+            x = (grp - np.float64(mu)) / np.float64(c)
+            q[j * DQ_GROUP:j * DQ_GROUP + grp.size] = np.clip(np.rint(x), -127, 127).astype(np.int8)
+    return q, scale, offset
+
+
+def absmax_dq_dequant(q, scale, offset):
+    """Reconstructed fp32 absmax [n] = fp32(fp32(q * c) + mu) per group."""
+    q = np.asarray(q, dtype=np.int8).reshape(-1)
+    g = np.arange(q.size) // DQ_GROUP
+    c = np.asarray(scale, dtype=np.float32)[g].astype(np.float64)
+    mu = np.asarray(offset, dtype=np.float32)[g].astype(np.float64)
+    prod = (q.astype(np.float64) * c).astype(np.float32)             # exact product, one rounding
+    return (prod.astype(np.float64) + mu).astype(np.float32)        # sum, one rounding

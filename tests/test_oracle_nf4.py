@@ -235,3 +235,80 @@ def test_quantize_is_exact_nearest_level_for_every_significand_pair():
     packed, absmax = nf4.quantize(bits)
     assert np.array_equal(absmax[:, 0], w[:, 0])
     assert np.array_equal(nf4.unpack_codes(packed), np.array(want, dtype=np.uint8))
+
+
+# ------------------------------------------------ double quantization -----
+def test_dq_exact_at_grid_points():
+    """A group built on the grid (mean mu, step c, codes symmetric about 0 with
+    extremes +-127) is recovered exactly: the same mean, step, codes and
+    values. mu and c are powers of two apart, so every mu + k c is an fp32
+    value and the mean of the group is mu exactly."""
+    g = np.random.default_rng(7)
+    k = g.integers(-126, 127, 127).astype(np.int64)
+    codes = np.concatenate([k, -k, [127, -127]])            # 256 codes, sum 0
+    g.shuffle(codes)
+    mu, c = np.float32(0.375), np.float32(2.0 ** -12)
+    a = (mu + codes * np.float64(c)).astype(np.float32)
+    assert np.array_equal(a.astype(np.float64), 0.375 + codes * 2.0 ** -12)
+    q, scale, offset = nf4.absmax_dq_quantize(a)
+    assert offset[0] == mu and scale[0] == c
+    assert np.array_equal(q.astype(np.int64), codes)
+    assert np.array_equal(nf4.absmax_dq_dequant(q, scale, offset), a)
+
+
+def test_dq_round_trip_error_bound_and_ragged_groups():
+    """Random absmax of N(0, 0.02) weight blocks over 1000 blocks (three full
+    groups and a ragged one of 232): every reconstructed value lies within
+    half a step of its group (plus the two fp32 roundings), codes stay in
+    [-127, 127], the extreme deviation of each group takes code +-127, and
+    mean and step agree with numpy's mean and max to 1 fp32 ulp."""
+    g = np.random.default_rng(8)
+    w = np.abs(g.standard_normal((1000, 64))) * 0.02
+    a = nf4.bf16_bits_to_f64(nf4.f32_to_bf16_bits(w.max(axis=1).astype(np.float32))).astype(np.float32)
+    q, scale, offset = nf4.absmax_dq_quantize(a)
+    assert q.shape == (1000,) and scale.shape == (4,) and offset.shape == (4,)
+    back = nf4.absmax_dq_dequant(q, scale, offset)
+    for j in range(4):
+        grp = a[j * 256:(j + 1) * 256].astype(np.float64)
+        mu_ref = np.float32(np.mean(grp))
+        assert abs(float(offset[j]) - float(mu_ref)) <= float(np.spacing(mu_ref))
+        c_ref = np.float32(np.max(np.abs(grp - np.float64(offset[j]))) / 127)
+        assert scale[j] == c_ref
+        qq = q[j * 256:(j + 1) * 256].astype(np.int64)
+        assert qq.min() >= -127 and qq.max() <= 127 and np.abs(qq).max() == 127
+        err = np.abs(back[j * 256:(j + 1) * 256].astype(np.float64) - grp)
+        bound = 0.5 * float(scale[j]) + 2 * float(np.spacing(np.float32(grp.max())))
+        assert err.max() <= bound
+    # the code is the nearest integer step (brute force on the first group)
+    mu, c = float(offset[0]), float(scale[0])
+    for i in range(0, 256, 17):
+        dist = [abs(float(a[i]) - mu - t * c) for t in range(-127, 128)]
+        assert abs(float(a[i]) - mu - int(q[i]) * c) <= min(dist) + 1e-15
+
+
+def test_dq_zero_and_constant_groups():
+    a = np.zeros(300, dtype=np.float32)
+    a[256:] = np.float32(0.0625)                              # ragged group: all equal
+    q, scale, offset = nf4.absmax_dq_quantize(a)
+    assert np.all(q == 0) and scale[0] == 0 and offset[0] == 0 and scale[1] == 0
+    assert offset[1] == np.float32(0.0625)
+    back = nf4.absmax_dq_dequant(q, scale, offset)
+    assert np.array_equal(back, a) and not np.any(np.signbit(back))
+
+
+def test_dq_weight_dequant_uses_reconstructed_absmax():
+    """A double-quantized weight dequantizes exactly as the NF4 weight whose
+    absmax is the reconstructed array (the second level only replaces the
+    constants)."""
+    g = np.random.default_rng(9)
+    w = nf4.f32_to_bf16_bits(g.standard_normal((8, 512)).astype(np.float32) * np.float32(0.02))
+    packed, absmax = nf4.quantize(w)
+    q, scale, offset = nf4.absmax_dq_quantize(absmax)
+    back = nf4.absmax_dq_dequant(q, scale, offset).reshape(absmax.shape)
+    # relative change of the constants is small: within a step of 1/127 of the group's spread
+    assert np.max(np.abs(back - absmax)) <= 0.5 * scale.max() + 1e-9
+    deq = nf4.dequant_bf16_bits(packed, back)
+    L = nf4.nf4_levels().astype(np.float64)
+    codes = nf4.unpack_codes(packed)
+    want = nf4.f32_to_bf16_bits((L[codes] * np.repeat(back.astype(np.float64), 64, axis=1)).astype(np.float32))
+    assert np.array_equal(deq, want)
