@@ -83,12 +83,23 @@ typedef enum {
   QLORA_DEQUANT_STAGED = 2
 } qlora_dequant_mode;
 
-/* An NF4-quantized weight of shape [n][k] (device pointers). */
+/* An NF4-quantized weight of shape [n][k] (device pointers).
+ * Its per-block constants are either the fp32 absmax array, or (absmax NULL)
+ * that array double-quantized by qlora_absmax_dq_quantize: one int8 code per
+ * 64-weight block and one fp32 scale and offset per 256 consecutive blocks
+ * (flattened row-major), absmax[i] = fp32(fp32(q[i] * scale[i/256]) +
+ * offset[i/256]). Every entry point that takes a qlora_nf4 accepts both forms
+ * and dequantizes with the reconstructed absmax; the trailing fields may stay
+ * zero (NULL) for a plain weight. The QLoRA paper, which the pages link for
+ * the 4-bit format, stores its constants this way ("double quantization"). */
 typedef struct qlora_nf4 {
-  const uint8_t* codes; /* [n][k/2] */
-  const float* absmax;  /* [n][k/64] */
+  const uint8_t* codes;        /* [n][k/2] */
+  const float* absmax;         /* [n][k/64], or NULL when double-quantized */
   int64_t n;
   int64_t k;
+  const int8_t* absmax_q;      /* [n*k/64] codes (double-quantized form) */
+  const float* absmax_scale;   /* [ceil(n*k/64 / 256)] */
+  const float* absmax_offset;  /* [ceil(n*k/64 / 256)] */
 } qlora_nf4;
 
 /* The three projections of a gated MLP with hidden width d and MLP width h
@@ -141,8 +152,28 @@ void qlora_nf4_levels(float out_host[16]);
 int qlora_gemm_split_count(int64_t m, int64_t n, int64_t k);
 
 /* Standalone dequantization: out [n][k] bf16 = dequant(W). Bit-exact
- * contract: bf16_rne(fp32_rne(level[code] * absmax)). */
+ * contract: bf16_rne(fp32_rne(level[code] * absmax)), with the reconstructed
+ * absmax for a double-quantized weight. */
 int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);
+
+/* Double quantization of the absmax constants (the second level of the QLoRA
+ * paper's storage, which the pages link): nb fp32 values (the [n][k/64] array,
+ * flattened) in groups of 256 consecutive values, the last group possibly
+ * shorter. Per group: offset = fp32(sum / count), the sum taken in fp64 in
+ * index order; scale = fp32(max |a - offset| / 127) in fp64; each value's code
+ * q = clamp(rne((a - offset) / scale), -127, 127) in fp64 (0 when scale is 0).
+ * Outputs q int8 [nb], scale and offset fp32 [ceil(nb / 256)], all device
+ * buffers owned by the caller; 1 byte per 64 weights plus 8 bytes per 16384.
+ * Errors: QLORA_EINVAL for a NULL pointer with nb > 0, QLORA_ESHAPE for
+ * nb < 0 or fp32 pointers off 4 bytes; nb == 0 does nothing. */
+int qlora_absmax_dq_quantize(const float* absmax, int64_t nb, int8_t* q, float* scale,
+                             float* offset, void* stream);
+
+/* The reconstructed constants: out[i] = fp32(fp32(q[i] * scale[i/256]) +
+ * offset[i/256]) (two roundings, no fused multiply-add), i < nb. Errors as
+ * for qlora_absmax_dq_quantize. */
+int qlora_absmax_dq_dequant(const int8_t* q, const float* scale, const float* offset, int64_t nb,
+                            float* out, void* stream);
 
 /* Quantizer: bf16 W [n][k] (k a multiple of 64, finite values) -> NF4 codes
  * [n][k/2] and absmax [n][k/64], the inverse direction of the dequant above
@@ -150,7 +181,8 @@ int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream);
  * 64-block: absmax = max |w| (exact); each weight takes the nearest level to
  * x = w / absmax, x and the distances formed in fp64, ties to the lower
  * code; an all-zero block gets absmax 0 and code 7 (the level 0) throughout.
- * The absmax values stay fp32 (no second-level quantization). Layout and
+ * The absmax values are fp32 (qlora_absmax_dq_quantize adds the second
+ * level). Layout and
  * ownership as for qlora_nf4_dequant (device pointers owned by the caller).
  * Errors: QLORA_ESHAPE if k % 64 != 0 or a size is negative or >= 2^31;
  * n*k == 0 returns QLORA_OK and touches nothing (pointers may be NULL);

@@ -7,7 +7,8 @@ the library; the first call does, and fails loudly if it was not built.
 """
 
 __all__ = [
-    "NF4Weight", "MlpWeights", "version", "nf4_levels", "gemm_split_count", "nf4_dequant", "nf4_quantize",
+    "NF4Weight", "AbsmaxDQ", "absmax_dq_quantize", "absmax_dq_dequant", "nf4_double_quantize",
+    "MlpWeights", "version", "nf4_levels", "gemm_split_count", "nf4_dequant", "nf4_quantize",
     "linear_workspace_bytes", "linear_fwd", "linear_bwd", "linear_fwd_noalloc",
     "linear_fwd_noalloc_max_bytes",
     "mlp_workspace_bytes", "mlp_fwd", "mlp_bwd", "trace_enable", "trace_read", "probe_mfma_peak",

@@ -27,7 +27,8 @@ c_vp = ctypes.c_void_p
 
 
 class Nf4(ctypes.Structure):
-    _fields_ = [("codes", c_vp), ("absmax", c_vp), ("n", c_i64), ("k", c_i64)]
+    _fields_ = [("codes", c_vp), ("absmax", c_vp), ("n", c_i64), ("k", c_i64),
+                ("absmax_q", c_vp), ("absmax_scale", c_vp), ("absmax_offset", c_vp)]
 
 
 class MlpWeights(ctypes.Structure):
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.qlora_nf4_dequant.restype = ctypes.c_int
         L.qlora_nf4_dequant.argtypes = [Nf4, c_vp, c_vp]
+        L.qlora_absmax_dq_quantize.restype = ctypes.c_int
+        L.qlora_absmax_dq_quantize.argtypes = [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]
+        L.qlora_absmax_dq_dequant.restype = ctypes.c_int
+        L.qlora_absmax_dq_dequant.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]
         L.qlora_nf4_quantize.restype = ctypes.c_int
         L.qlora_nf4_quantize.argtypes = [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]
         L.qlora_linear_workspace_bytes.restype = ctypes.c_size_t
@@ -185,7 +190,7 @@ def check(status: int, what: str) -> None:
 EXPORTED = [
     "qlora_status_string", "qlora_last_error", "qlora_version", "qlora_nf4_levels",
     "qlora_gemm_split_count",
-    "qlora_nf4_dequant", "qlora_nf4_quantize", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_nf4_dequant", "qlora_nf4_quantize", "qlora_absmax_dq_quantize", "qlora_absmax_dq_dequant", "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_noalloc_max_bytes", "qlora_linear_fwd_noalloc",
     "qlora_mlp_workspace_bytes", "qlora_mlp_fwd", "qlora_mlp_bwd",
     "qlora_trace_enable", "qlora_trace_read", "qlora_probe_mfma_peak",

@@ -55,10 +55,24 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 @dataclasses.dataclass
+class AbsmaxDQ:
+    """Double-quantized absmax of nb = n*k/64 blocks: q int8 [nb], scale and
+    offset float32 [ceil(nb/256)]."""
+    q: torch.Tensor
+    scale: torch.Tensor
+    offset: torch.Tensor
+
+    def to(self, device):
+        return AbsmaxDQ(self.q.to(device), self.scale.to(device), self.offset.to(device))
+
+
+@dataclasses.dataclass
 class NF4Weight:
-    """NF4 weight of shape [n][k]: codes uint8 [n][k/2], absmax float32 [n][k/64]."""
+    """NF4 weight of shape [n][k]: codes uint8 [n][k/2] and either absmax
+    float32 [n][k/64] or its double-quantized form `dq` (absmax None)."""
     codes: torch.Tensor
-    absmax: torch.Tensor
+    absmax: Optional[torch.Tensor]
+    dq: Optional[AbsmaxDQ] = None
 
     @property
     def n(self) -> int:
@@ -70,11 +84,53 @@ class NF4Weight:
 
     def c_struct(self) -> _lib.Nf4:
         _need(self.codes, "codes", torch.uint8, (self.n, self.k // 2))
-        _need(self.absmax, "absmax", torch.float32, (self.n, self.k // 64))
-        return _lib.Nf4(self.codes.data_ptr(), self.absmax.data_ptr(), self.n, self.k)
+        if self.absmax is not None:
+            _need(self.absmax, "absmax", torch.float32, (self.n, self.k // 64))
+            return _lib.Nf4(self.codes.data_ptr(), self.absmax.data_ptr(), self.n, self.k)
+        if self.dq is None:
+            raise ValueError("NF4Weight needs absmax or its double-quantized form")
+        nb = self.n * (self.k // 64)
+        ng = (nb + 255) // 256
+        _need(self.dq.q, "dq.q", torch.int8, (nb,))
+        _need(self.dq.scale, "dq.scale", torch.float32, (ng,))
+        _need(self.dq.offset, "dq.offset", torch.float32, (ng,))
+        return _lib.Nf4(self.codes.data_ptr(), None, self.n, self.k, self.dq.q.data_ptr(),
+                        self.dq.scale.data_ptr(), self.dq.offset.data_ptr())
 
     def to(self, device):
-        return NF4Weight(self.codes.to(device), self.absmax.to(device))
+        return NF4Weight(self.codes.to(device), None if self.absmax is None else self.absmax.to(device),
+                         None if self.dq is None else self.dq.to(device))
+
+
+def absmax_dq_quantize(absmax: torch.Tensor) -> AbsmaxDQ:
+    """Double quantization of an fp32 absmax array (read flattened)."""
+    if absmax.dtype != torch.float32 or not absmax.is_contiguous():
+        raise ValueError("absmax must be a contiguous float32 tensor")
+    nb = absmax.numel()
+    ng = (nb + 255) // 256
+    dev = absmax.device
+    out = AbsmaxDQ(torch.empty(nb, dtype=torch.int8, device=dev),
+                   torch.empty(ng, dtype=torch.float32, device=dev),
+                   torch.empty(ng, dtype=torch.float32, device=dev))
+    _lib.check(_lib.lib().qlora_absmax_dq_quantize(_ptr(absmax), nb, _ptr(out.q), _ptr(out.scale),
+                                                   _ptr(out.offset), _stream()),
+               "qlora_absmax_dq_quantize")
+    return out
+
+
+def absmax_dq_dequant(dq: AbsmaxDQ) -> torch.Tensor:
+    """The reconstructed fp32 absmax [nb] of a double-quantized array."""
+    nb = dq.q.numel()
+    out = torch.empty(nb, dtype=torch.float32, device=dq.q.device)
+    _lib.check(_lib.lib().qlora_absmax_dq_dequant(_ptr(dq.q), _ptr(dq.scale), _ptr(dq.offset), nb,
+                                                  _ptr(out), _stream()),
+               "qlora_absmax_dq_dequant")
+    return out
+
+
+def nf4_double_quantize(w: NF4Weight) -> NF4Weight:
+    """The same weight with its absmax double-quantized (absmax dropped)."""
+    return NF4Weight(w.codes, None, absmax_dq_quantize(w.absmax))
 
 
 def version() -> str:

@@ -69,7 +69,16 @@ inline int64_t ceil16(int64_t x) { return (x + 15) / 16 * 16; }
 inline bool mlp_wide(int64_t r) { return 2 * r > 64; }
 inline int64_t mlp_ke_gu(int64_t r) { return mlp_wide(r) ? 2 * ceil16(2 * r) : ceil16(4 * r); }
 
-bool bad_nf4(const qlora_nf4& w) { return !w.codes || !w.absmax; }
+// the weight's absmax: the fp32 array when given, else the double-quantized form
+AbsmaxSrc absmax_src(const qlora_nf4& w) {
+  if (w.absmax) return AbsmaxSrc{w.absmax, nullptr, nullptr, nullptr};
+  return AbsmaxSrc{nullptr, w.absmax_q, w.absmax_scale, w.absmax_offset};
+}
+bool bad_absmax(const AbsmaxSrc& a) { return !a.f32 && (!a.q || !a.scale || !a.offset); }
+bool absmax_aligned(const AbsmaxSrc& a) {
+  return ((uintptr_t)a.f32 & 3) == 0 && ((uintptr_t)a.scale & 3) == 0 && ((uintptr_t)a.offset & 3) == 0;
+}
+bool bad_nf4(const qlora_nf4& w) { return !w.codes || bad_absmax(absmax_src(w)); }
 
 // Base-weight source: NF4 (codes + absmax) or, in MODE_BF16, a bf16 matrix
 // used as it is (16-bit LoRA: the dequantization step becomes nothing, a copy
@@ -77,13 +86,13 @@ bool bad_nf4(const qlora_nf4& w) { return !w.codes || !w.absmax; }
 constexpr int MODE_BF16 = 3;
 struct WSrc {
   const uint8_t* codes = nullptr;
-  const float* absmax = nullptr;
+  AbsmaxSrc amax = AbsmaxSrc{nullptr, nullptr, nullptr, nullptr};
   const uint16_t* w16 = nullptr;
   int64_t n = 0, k = 0;
 };
 WSrc src_nf4(const qlora_nf4& w) {
   WSrc s;
-  s.codes = w.codes; s.absmax = w.absmax; s.n = w.n; s.k = w.k;
+  s.codes = w.codes; s.amax = absmax_src(w); s.n = w.n; s.k = w.k;
   return s;
 }
 WSrc src_w16(const uint16_t* w, int64_t n, int64_t k) {
@@ -91,7 +100,7 @@ WSrc src_w16(const uint16_t* w, int64_t n, int64_t k) {
   s.w16 = w; s.n = n; s.k = k;
   return s;
 }
-bool bad_src(const WSrc& w, int mode) { return mode == MODE_BF16 ? !w.w16 : (!w.codes || !w.absmax); }
+bool bad_src(const WSrc& w, int mode) { return mode == MODE_BF16 ? !w.w16 : (!w.codes || bad_absmax(w.amax)); }
 
 // Pointer alignment the kernels rely on (null passes: null checks are separate).
 // bf16 matrices and NF4 code arrays are read and written 16 bytes at a time,
@@ -100,7 +109,21 @@ bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 bool al16(const void* p) { return al(p, 16); }
 bool al4(const void* p) { return al(p, 4); }
 bool al2(const void* p) { return al(p, 2); }
-bool src_aligned(const WSrc& w) { return al16(w.w16) && al16(w.codes) && al4(w.absmax); }
+bool src_aligned(const WSrc& w) { return al16(w.w16) && al16(w.codes) && absmax_aligned(w.amax); }
+
+// absmax values of a weight [n][k]
+inline int64_t absmax_count(const WSrc& w) { return w.n * (w.k / 64); }
+
+// The fused-dequant GEMM reads fp32 absmax: the stored array, or the
+// double-quantized one decoded into `buf` (absmax_count floats of workspace).
+hipError_t fused_absmax(const WSrc& w, float* buf, hipStream_t st, const float** out) {
+  if (w.amax.f32) {
+    *out = w.amax.f32;
+    return hipSuccess;
+  }
+  *out = buf;
+  return launch_absmax_dq_dequant(w.amax.q, w.amax.scale, w.amax.offset, absmax_count(w), buf, st);
+}
 // a bf16 copy of the weight (or of its transpose) lives in the workspace
 bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE_BF16; }
 
@@ -140,6 +163,7 @@ struct LinearFwdWs {
   uint16_t* wbf;   // [n][k] (staged)
   float* rpart;    // row-product split partials
   float* kpart;    // split-K partials of the GEMM
+  float* amx;      // fused: fp32 absmax decoded from a double-quantized weight
 };
 
 size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearFwdWs* w) {
@@ -150,6 +174,7 @@ size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.wbf = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(n * k) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
   t.kpart = c.take<float>(splitk_elems(m, n, k, staged_like(mode)));
+  t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? n * (k / 64) : 0);
   if (w) *w = t;
   return c.off;
 }
@@ -163,6 +188,7 @@ struct LinearBwdWs {
   uint16_t* wt;    // [k][n]   dequantized W^T
   float* rpart;    // row-product split partials
   float* kpart;    // split-K partials of the dX GEMM
+  float* amx;      // fused: fp32 absmax decoded from a double-quantized weight
 };
 
 size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, int mode, LinearBwdWs* w) {
@@ -177,6 +203,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.wt = staged_like(mode) ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
   t.kpart = c.take<float>(splitk_elems(m, k, n, staged_like(mode)));
+  t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? n * (k / 64) : 0);
   if (w) *w = t;
   return c.off;
 }
@@ -193,6 +220,8 @@ struct MlpFwdWs {
   uint16_t* wd;      // [d][h]  staged
   float* rpart;      // row-product split partials
   float* kpart;      // split-K partials of the down GEMM
+  float* amx;        // fused: fp32 absmax of gate, up, down decoded from a
+                     // double-quantized form ([h][d/64], [h][d/64], [d][h/64])
 };
 
 size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpFwdWs* w) {
@@ -208,6 +237,7 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
   t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
   t.kpart = c.take<float>(splitk_elems(m, d, h, staged_like(mode)));
+  t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? 3 * h * (d / 64) : 0);
   if (w) *w = t;
   return c.off;
 }
@@ -227,6 +257,7 @@ struct MlpBwdWs {
   uint16_t* wgut;    // [d][2h]
   float* rpart;      // row-product split partials
   float* kpart;      // split-K partials of the dX GEMM
+  float* amx;        // fused: decoded fp32 absmax of gate, up, down (as forward)
 };
 
 size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int mode, MlpBwdWs* w) {
@@ -247,6 +278,7 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
   t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
   t.kpart = c.take<float>(splitk_elems(m, d, 2 * h, staged_like(mode)));
+  t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? 3 * h * (d / 64) : 0);
   if (w) *w = t;
   return c.off;
 }
@@ -435,9 +467,31 @@ void qlora_nf4_levels(float out_host[16]) { nf4_levels_host(out_host); }
 int qlora_nf4_dequant(qlora_nf4 w, uint16_t* out, void* stream) {
   if (bad_nf4(w) || !out) return QLORA_EINVAL;
   if (!dims_ok(0, w.k, w.n)) return QLORA_ESHAPE;
-  if (!al16(w.codes) || !al4(w.absmax) || !al16(out)) return QLORA_ESHAPE;
-  QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, w.n, w.k, out, w.k, 0, (hipStream_t)stream),
+  const AbsmaxSrc amax = absmax_src(w);
+  if (!al16(w.codes) || !absmax_aligned(amax) || !al16(out)) return QLORA_ESHAPE;
+  QL_TRY(launch_nf4_dequant_rows(w.codes, amax, w.n, w.k, out, w.k, 0, (hipStream_t)stream),
          "nf4_dequant");
+  return QLORA_OK;
+}
+
+int qlora_absmax_dq_quantize(const float* absmax, int64_t nb, int8_t* q, float* scale,
+                             float* offset, void* stream) {
+  if (nb < 0) return QLORA_ESHAPE;
+  if (nb == 0) return QLORA_OK;
+  if (!absmax || !q || !scale || !offset) return QLORA_EINVAL;
+  if (!al4(absmax) || !al4(scale) || !al4(offset)) return QLORA_ESHAPE;
+  QL_TRY(launch_absmax_dq_quantize(absmax, nb, q, scale, offset, (hipStream_t)stream),
+         "absmax_dq_quantize");
+  return QLORA_OK;
+}
+
+int qlora_absmax_dq_dequant(const int8_t* q, const float* scale, const float* offset, int64_t nb,
+                            float* out, void* stream) {
+  if (nb < 0) return QLORA_ESHAPE;
+  if (nb == 0) return QLORA_OK;
+  if (!q || !scale || !offset || !out) return QLORA_EINVAL;
+  if (!al4(out) || !al4(scale) || !al4(offset)) return QLORA_ESHAPE;
+  QL_TRY(launch_absmax_dq_dequant(q, scale, offset, nb, out, (hipStream_t)stream), "absmax_dq_dequant");
   return QLORA_OK;
 }
 
@@ -500,7 +554,7 @@ static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const ui
     QL_TRY(launch_prep(J, st), "linear_fwd: LoRA layouts");
   }
   if (mode == QLORA_DEQUANT_STAGED)
-    QL_TRY(launch_nf4_dequant_rows(w.codes, w.absmax, n, k, t.wbf, k, 0, st), "linear_fwd: dequant");
+    QL_TRY(launch_nf4_dequant_rows(w.codes, w.amax, n, k, t.wbf, k, 0, st), "linear_fwd: dequant");
   QL_TRY(launch_rowdot(X, k, A, k, (int)m, (int)k, (int)r, s, U_save, nullptr, (int)r, r, t.uext,
                        KE, KE, t.rpart, st),
          "linear_fwd: U = X A^T");
@@ -508,7 +562,10 @@ static int linear_fwd_impl(const uint16_t* X, int64_t m, const WSrc& w, const ui
   g.A = X; g.lda = k;
   if (mode == QLORA_DEQUANT_STAGED) { g.bsrc = BSRC_BF16; g.B = t.wbf; g.ldb = k; }
   else if (mode == MODE_BF16) { g.bsrc = BSRC_BF16; g.B = w.w16; g.ldb = k; }
-  else { g.bsrc = BSRC_NF4; g.codes0 = w.codes; g.absmax0 = w.absmax; }
+  else {
+    g.bsrc = BSRC_NF4; g.codes0 = w.codes;
+    QL_TRY(fused_absmax(w, t.amx, st, &g.absmax0), "linear_fwd: absmax");
+  }
   g.Ae = t.uext; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
   g.M = (int)m; g.N = (int)n; g.K = (int)k; g.KE = KE;
   g.epi = EPI_STORE; g.C = Y; g.ldc = n;
@@ -570,11 +627,12 @@ static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U
       if (mode == MODE_BF16)
         QL_TRY(launch_w16_transpose(w.w16, n, k, t.wt, n, 0, st), "linear_bwd: W^T");
       else
-        QL_TRY(launch_nf4_dequant_transpose(w.codes, w.absmax, n, k, t.wt, n, 0, st),
+        QL_TRY(launch_nf4_dequant_transpose(w.codes, w.amax, n, k, t.wt, n, 0, st),
                "linear_bwd: dequant W^T");
       g.bsrc = BSRC_BF16; g.B = t.wt; g.ldb = n;
     } else {
-      g.bsrc = BSRC_NF4_T; g.codes0 = w.codes; g.absmax0 = w.absmax;
+      g.bsrc = BSRC_NF4_T; g.codes0 = w.codes;
+      QL_TRY(fused_absmax(w, t.amx, st, &g.absmax0), "linear_bwd: absmax");
     }
     g.Ae = t.text; g.ldae = KE; g.Be = t.bext; g.ldbe = KE;
     g.M = (int)m; g.N = (int)k; g.K = (int)n; g.KE = KE;
@@ -789,9 +847,9 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
       QL_TRY(launch_w16_rows(w->gate.w16, h, d, t.wgu, d, 1, st), "mlp_fwd: gate/up copy");
       QL_TRY(launch_w16_rows(w->up.w16, h, d, t.wgu, d, 2, st), "mlp_fwd: gate/up copy");
     } else {
-      QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.absmax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
-      QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.absmax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
-      QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.absmax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
+      QL_TRY(launch_nf4_dequant_rows(w->gate.codes, w->gate.amax, h, d, t.wgu, d, 1, st), "mlp_fwd: dequant");
+      QL_TRY(launch_nf4_dequant_rows(w->up.codes, w->up.amax, h, d, t.wgu, d, 2, st), "mlp_fwd: dequant");
+      QL_TRY(launch_nf4_dequant_rows(w->down.codes, w->down.amax, d, h, t.wd, h, 0, ss), "mlp_fwd: dequant");
     }
     QL_TRY(side.mark(2), "mlp_fwd: mark");
   } else {
@@ -804,8 +862,9 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   if (staged) { g.bsrc = BSRC_BF16; g.B = t.wgu; g.ldb = d; }
   else {
     g.bsrc = BSRC_NF4_PAIR;
-    g.codes0 = w->gate.codes; g.absmax0 = w->gate.absmax;
-    g.codes1 = w->up.codes; g.absmax1 = w->up.absmax;
+    g.codes0 = w->gate.codes; g.codes1 = w->up.codes;
+    QL_TRY(fused_absmax(w->gate, t.amx, st, &g.absmax0), "mlp_fwd: absmax");
+    QL_TRY(fused_absmax(w->up, t.amx + h * (d / 64), st, &g.absmax1), "mlp_fwd: absmax");
   }
   g.Ae = t.uextgu; g.ldae = KEgu; g.Be = t.bextgu; g.ldbe = KEgu;
   g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
@@ -827,7 +886,10 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   g2.A = t.H; g2.lda = h;
   if (w16) { g2.bsrc = BSRC_BF16; g2.B = w->down.w16; g2.ldb = h; }
   else if (staged) { g2.bsrc = BSRC_BF16; g2.B = t.wd; g2.ldb = h; }
-  else { g2.bsrc = BSRC_NF4; g2.codes0 = w->down.codes; g2.absmax0 = w->down.absmax; }
+  else {
+    g2.bsrc = BSRC_NF4; g2.codes0 = w->down.codes;
+    QL_TRY(fused_absmax(w->down, t.amx + 2 * h * (d / 64), st, &g2.absmax0), "mlp_fwd: absmax");
+  }
   g2.Ae = t.uextd; g2.ldae = KEd; g2.Be = t.bextd; g2.ldbe = KEd;
   g2.M = (int)m; g2.N = (int)d; g2.K = (int)h; g2.KE = KEd;
   g2.epi = EPI_STORE; g2.C = Y; g2.ldc = d;
@@ -929,9 +991,9 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     QL_TRY(launch_w16_transpose(w->gate.w16, h, d, t.wgut, 2 * h, 0, ss), "mlp_bwd: Wg^T");
     QL_TRY(launch_w16_transpose(w->up.w16, h, d, t.wgut, 2 * h, h, ss), "mlp_bwd: Wu^T");
   } else if (staged) {
-    QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.absmax, h, d, t.wgut, 2 * h, 0, ss),
+    QL_TRY(launch_nf4_dequant_transpose(w->gate.codes, w->gate.amax, h, d, t.wgut, 2 * h, 0, ss),
            "mlp_bwd: dequant Wg^T");
-    QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.absmax, h, d, t.wgut, 2 * h, h, ss),
+    QL_TRY(launch_nf4_dequant_transpose(w->up.codes, w->up.amax, h, d, t.wgut, 2 * h, h, ss),
            "mlp_bwd: dequant Wu^T");
   }
   QL_TRY(side.mark(1), "mlp_bwd: mark");
@@ -945,7 +1007,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   if (w16)
     QL_TRY(launch_w16_transpose(w->down.w16, d, h, t.wdt, d, 0, st), "mlp_bwd: Wd^T");
   else if (staged)
-    QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.absmax, d, h, t.wdt, d, 0, st),
+    QL_TRY(launch_nf4_dequant_transpose(w->down.codes, w->down.amax, d, h, t.wdt, d, 0, st),
            "mlp_bwd: dequant Wd^T");
   if (staged) {
     QL_TRY(side.wait(2), "mlp_bwd: wait");
@@ -963,7 +1025,10 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   GemmArgs g = gemm_args();
   g.A = dY; g.lda = d;
   if (staged) { g.bsrc = BSRC_BF16; g.B = t.wdt; g.ldb = d; }
-  else { g.bsrc = BSRC_NF4_T; g.codes0 = w->down.codes; g.absmax0 = w->down.absmax; }
+  else {
+    g.bsrc = BSRC_NF4_T; g.codes0 = w->down.codes;
+    QL_TRY(fused_absmax(w->down, t.amx + 2 * h * (d / 64), st, &g.absmax0), "mlp_bwd: absmax");
+  }
   g.Ae = t.textd; g.ldae = KEd; g.Be = t.bextdh; g.ldbe = KEd;
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
@@ -1032,8 +1097,9 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     if (staged) { g2.bsrc = BSRC_BF16; g2.B = t.wgut; g2.ldb = 2 * h; }
     else {
       g2.bsrc = BSRC_NF4_T;
-      g2.codes0 = w->gate.codes; g2.absmax0 = w->gate.absmax;
-      g2.codes1 = w->up.codes; g2.absmax1 = w->up.absmax;
+      g2.codes0 = w->gate.codes; g2.codes1 = w->up.codes;
+      QL_TRY(fused_absmax(w->gate, t.amx, st, &g2.absmax0), "mlp_bwd: absmax");
+      QL_TRY(fused_absmax(w->up, t.amx + h * (d / 64), st, &g2.absmax1), "mlp_bwd: absmax");
       g2.ksplit = (int)h;
     }
     g2.Ae = t.textgu; g2.ldae = KEgu; g2.Be = t.bextdx; g2.ldbe = KEgu;
@@ -1267,7 +1333,7 @@ static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t*
     if (w16)
       QL_TRY(launch_w16_rows(w.w[p].w16, n[p], d, dst, d, 0, ss), "qkv_fwd: weight copy");
     else
-      QL_TRY(launch_nf4_dequant_rows(w.w[p].codes, w.w[p].absmax, n[p], d, dst, d, 0, ss),
+      QL_TRY(launch_nf4_dequant_rows(w.w[p].codes, w.w[p].amax, n[p], d, dst, d, 0, ss),
              "qkv_fwd: dequant");
   }
   QL_TRY(side.mark(1), "qkv_fwd: mark");
@@ -1358,7 +1424,7 @@ static int qkv_bwd_impl(const uint16_t* const dy[3], const int64_t lddy[3], cons
       if (w16)
         QL_TRY(launch_w16_transpose(w.w[p].w16, n[p], d, t.wt, nt, off[p], ss), "qkv_bwd: W^T");
       else
-        QL_TRY(launch_nf4_dequant_transpose(w.w[p].codes, w.w[p].absmax, n[p], d, t.wt, nt, off[p],
+        QL_TRY(launch_nf4_dequant_transpose(w.w[p].codes, w.w[p].amax, n[p], d, t.wt, nt, off[p],
                                             ss),
                "qkv_bwd: dequant W^T");
     }

@@ -8,16 +8,37 @@ namespace qlora {
 
 void nf4_levels_host(float out[16]);
 
+// fp32 absmax of an NF4 weight [n][k/64] (flattened index i = row * k/64 +
+// block), stored as it is (f32) or double-quantized: 8-bit codes q with one
+// fp32 scale and offset per 256 consecutive values,
+//   absmax[i] = fp32(fp32(q[i] * scale[i / 256]) + offset[i / 256]).
+struct AbsmaxSrc {
+  const float* f32;      // plain fp32 array, or null when double-quantized
+  const int8_t* q;
+  const float* scale;
+  const float* offset;
+};
+constexpr int kDqGroup = 256;
+
 // ---- NF4 dequant (nf4.hip) ----
 // out[dest_row(i)][j] = W[i][j]; interleave 0: dest_row(i) = i; 1/2: the 32-row
 // interleave of a gate (1) / up (2) pair: 64*(i/32) + 32*(interleave-1) + i%32.
-hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, int64_t n, int64_t k,
+hipError_t launch_nf4_dequant_rows(const uint8_t* codes, AbsmaxSrc absmax, int64_t n, int64_t k,
                                    uint16_t* out, int64_t ld_out, int interleave,
                                    hipStream_t stream);
 // out[j][col_ofs + i] = W[i][j]   (n, k multiples of 64)
-hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, const float* absmax, int64_t n,
+hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, AbsmaxSrc absmax, int64_t n,
                                         int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
                                         hipStream_t stream);
+
+// Double quantization of an fp32 absmax array of nb values (groups of 256):
+// offset = fp32(sequential fp64 sum / count), scale = fp32(max |a - offset| /
+// 127) in fp64, q = clamp(rne((a - offset) / scale), -127, 127) (0 if scale is 0).
+hipError_t launch_absmax_dq_quantize(const float* absmax, int64_t nb, int8_t* q, float* scale,
+                                     float* offset, hipStream_t stream);
+// out[i] = the reconstructed absmax (fp32), i < nb
+hipError_t launch_absmax_dq_dequant(const int8_t* q, const float* scale, const float* offset,
+                                    int64_t nb, float* out, hipStream_t stream);
 
 // NF4 quantizer: codes [n][k/2] and absmax [n][k/64] from bf16 W [n][k]
 hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,

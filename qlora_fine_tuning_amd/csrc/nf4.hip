@@ -41,6 +41,19 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t word, float amax, const flo
   return o;
 }
 
+// One reconstructed absmax: the stored fp32 value, or the double-quantized
+// one. The product and the sum are rounded separately, which is the format's
+// definition: contraction into a fused multiply-add is switched off here
+// (HIP compiles with fp-contract=fast, and __fmul_rn / __fadd_rn are plain
+// operators that it would still fuse).
+__device__ __forceinline__ float load_absmax(const AbsmaxSrc& a, int64_t i) {
+#pragma clang fp contract(off)
+  if (a.f32) return a.f32[i];
+  const int64_t g = i / kDqGroup;
+  const float p = (float)a.q[i] * a.scale[g];
+  return p + a.offset[g];
+}
+
 // out row for weight row n: plain (n) or, with interleave32 = 1 + which,
 // the 32-row interleave of two matrices: 64 * (n / 32) + 32 * which + n % 32.
 __device__ __forceinline__ int64_t dest_row(int64_t n, int interleave) {
@@ -52,7 +65,7 @@ __device__ __forceinline__ int64_t dest_row(int64_t n, int interleave) {
 // bf16 bytes out); blockIdx.y walks the rows (strided when there are more
 // than the grid's y extent), blockIdx.x the 4096-weight chunks of a row.
 __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int64_t n, int64_t k,
+    const uint8_t* __restrict__ codes, const AbsmaxSrc absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int interleave) {
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = __uint_as_float(c_nf4_levels[threadIdx.x]);
@@ -61,7 +74,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
   if (g * 16 >= k) return;
   for (int64_t row = blockIdx.y; row < n; row += gridDim.y) {
     const uint2 cw = *(const uint2*)(codes + row * (k >> 1) + g * 8);
-    const float amax = absmax[row * (k >> 6) + (g >> 2)];
+    const float amax = load_absmax(absmax, row * (k >> 6) + (g >> 2));
     uint16_t* o = out + dest_row(row, interleave) * ld_out + g * 16;
     *(u32x4_t*)o = dequant8(cw.x, amax, lut);
     *(u32x4_t*)(o + 8) = dequant8(cw.y, amax, lut);
@@ -73,7 +86,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
 // thread t dequantizes 8 weight rows x 4 features and writes 4 output rows
 // of 8 consecutive values; 8 lanes cover one 128-byte output row segment.
 __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int64_t n, int64_t k,
+    const uint8_t* __restrict__ codes, const AbsmaxSrc absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t col_ofs) {
   __shared__ float lut[16];
   __shared__ __attribute__((aligned(16))) uint8_t ct[64 * 64];
@@ -87,7 +100,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
     if (2 * c < kvalid)
       *(u32x4_t*)&ct[r * 64 + c] = *(const u32x4_t*)(codes + (n0 + r) * (k >> 1) + (k0 >> 1) + c);
     if (tid < 128 && 64 * (tid & 1) < kvalid)
-      at[tid >> 1][tid & 1] = absmax[(n0 + (tid >> 1)) * (k >> 6) + (k0 >> 6) + (tid & 1)];
+      at[tid >> 1][tid & 1] = load_absmax(absmax, (n0 + (tid >> 1)) * (k >> 6) + (k0 >> 6) + (tid & 1));
   }
   __syncthreads();
   const int qg = tid & 7, kq = tid >> 3;          // rows 8qg..8qg+7, features 4kq..4kq+3
@@ -186,7 +199,7 @@ hipError_t launch_nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t*
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, int64_t n, int64_t k,
+hipError_t launch_nf4_dequant_rows(const uint8_t* codes, AbsmaxSrc absmax, int64_t n, int64_t k,
                                    uint16_t* out, int64_t ld_out, int interleave,
                                    hipStream_t stream) {
   if (n == 0 || k == 0) return hipSuccess;
@@ -197,13 +210,86 @@ hipError_t launch_nf4_dequant_rows(const uint8_t* codes, const float* absmax, in
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, const float* absmax, int64_t n,
+hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, AbsmaxSrc absmax, int64_t n,
                                         int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
                                         hipStream_t stream) {
   if (n == 0 || k == 0) return hipSuccess;
   dim3 grid((unsigned)((k + 127) / 128), (unsigned)(n / 64));
   nf4_dequant_transpose_kernel<<<grid, dim3(256), 0, stream>>>(codes, absmax, n, k, out, ld_out,
                                                               col_ofs);
+  return hipGetLastError();
+}
+
+// ---- double quantization of the absmax constants ----
+// One 256-thread block per group of 256 constants (the last group may be
+// shorter). The mean is the sequential fp64 sum in index order, which thread
+// 0 forms from the group staged in LDS; the largest deviation from it is a
+// max-reduction (order-free); each thread then codes its own value.
+__global__ __launch_bounds__(256) void absmax_dq_quantize_kernel(const float* __restrict__ absmax,
+                                                                 int64_t nb, int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale,
+                                                                 float* __restrict__ offset) {
+  __shared__ float a[kDqGroup];
+  __shared__ double red[kDqGroup / 64];
+  __shared__ float mu_s;
+  const int tid = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * kDqGroup;
+  const int cnt = (int)min((int64_t)kDqGroup, nb - g0);
+  const bool in = tid < cnt;
+  const float v = in ? absmax[g0 + tid] : 0.0f;
+  a[tid] = v;
+  __syncthreads();
+  if (tid == 0) {
+    double sum = 0.0;
+    for (int i = 0; i < cnt; ++i) sum += (double)a[i];
+    mu_s = (float)(sum / (double)cnt);
+  }
+  __syncthreads();
+  const float mu = mu_s;
+  double dev = in ? fabs((double)v - (double)mu) : 0.0;
+  for (int o = 32; o > 0; o >>= 1) dev = fmax(dev, __shfl_xor(dev, o));
+  if ((tid & 63) == 0) red[tid >> 6] = dev;
+  __syncthreads();
+  const double dmax = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  const float c = (float)(dmax / 127.0);
+  if (in) {
+    int code = 0;
+    if (c > 0.0f) {
+      const double x = rint(((double)v - (double)mu) / (double)c);
+      code = (int)fmin(127.0, fmax(-127.0, x));
+    }
+    q[g0 + tid] = (int8_t)code;
+  }
+  if (tid == 0) {
+    scale[blockIdx.x] = c;
+    offset[blockIdx.x] = mu;
+  }
+}
+
+__global__ __launch_bounds__(256) void absmax_dq_dequant_kernel(const int8_t* __restrict__ q,
+                                                                const float* __restrict__ scale,
+                                                                const float* __restrict__ offset,
+                                                                int64_t nb, float* __restrict__ out) {
+  const AbsmaxSrc src{nullptr, q, scale, offset};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nb; i += (int64_t)gridDim.x * 256)
+    out[i] = load_absmax(src, i);
+}
+
+hipError_t launch_absmax_dq_quantize(const float* absmax, int64_t nb, int8_t* q, float* scale,
+                                     float* offset, hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
+  const int64_t groups = (nb + kDqGroup - 1) / kDqGroup;
+  absmax_dq_quantize_kernel<<<dim3((unsigned)groups), dim3(256), 0, stream>>>(absmax, nb, q, scale,
+                                                                            offset);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax_dq_dequant(const int8_t* q, const float* scale, const float* offset,
+                                    int64_t nb, float* out, hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
+  int64_t blocks = (nb + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  absmax_dq_dequant_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(q, scale, offset, nb, out);
   return hipGetLastError();
 }
 

@@ -233,6 +233,27 @@ def test_quantize_validation_errors(L):
     assert L.qlora_nf4_quantize(ctypes.c_void_p(0x1008), 4, 64, FAKE, FAKE, None) == -2   # misaligned
 
 
+def test_absmax_dq_validation_errors(L):
+    FAKE = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    q = L.qlora_absmax_dq_quantize
+    assert q(None, 0, None, None, None, None) == 0                         # empty: no work
+    assert q(FAKE, -1, FAKE, FAKE, FAKE, None) == -2
+    assert q(None, 10, FAKE, FAKE, FAKE, None) == -1
+    assert q(FAKE, 10, FAKE, None, FAKE, None) == -1
+    assert q(odd, 10, FAKE, FAKE, FAKE, None) == -2
+    dq = L.qlora_absmax_dq_dequant
+    assert dq(None, None, None, 0, None, None) == 0
+    assert dq(FAKE, FAKE, FAKE, -5, FAKE, None) == -2
+    assert dq(FAKE, FAKE, None, 10, FAKE, None) == -1
+    assert dq(FAKE, FAKE, FAKE, 10, odd, None) == -2
+    # a weight with neither fp32 absmax nor the double-quantized triple is rejected
+    w = _lib.Nf4(0x1000, None, 64, 64, 0x3000, None, 0x3000)
+    assert L.qlora_nf4_dequant(w, FAKE, None) == -1
+    w = _lib.Nf4(0x1000, None, 64, 64, 0x3001, 0x3000, 0x3002)            # offset off 4 bytes
+    assert L.qlora_nf4_dequant(w, FAKE, None) == -2
+
+
 def test_qkv_validation_errors(L):
     FAKE = 0x1000   # never dereferenced: validation fails first
     F = ctypes.c_void_p(FAKE)
