@@ -120,6 +120,23 @@ def gemm_traffic(lib_src_dir, workload, mode):
     return None
 
 
+def host_cpu():
+    """(model name, logical CPUs the process may run on) of the host."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
 def cpu_baseline(cfg, d, tokens):
     """fp64 oracle (as it stands) on the first `tokens` tokens of the same workload."""
     import numpy as np
@@ -143,8 +160,9 @@ def cpu_baseline(cfg, d, tokens):
     t = time.perf_counter() - t0 + t_dq     # a step dequantizes its weights too
     flops = oq.mlp_algorithmic_flops(tokens, cfg.d, cfg.h, cfg.r)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model, nproc = host_cpu()
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": f"{tokens} of {cfg.m} tokens with the full {cfg.name} weights, fp64 numpy: "
                       f"weight dequant {t_dq:.2f} s + fwd/bwd {t - t_dq:.2f} s",
             "tokens_per_s": round(tokens / t, 3), "seconds": round(t, 3)}
@@ -173,8 +191,9 @@ def cpu_baseline_qkv(cfg, d, tokens):
     t = time.perf_counter() - t0 + t_dq
     flops = oq.qkv_algorithmic_flops(tokens, cfg.d, (cfg.n_q, cfg.n_k, cfg.n_v), cfg.r)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model, nproc = host_cpu()
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": f"{tokens} of {cfg.m} tokens with the full {cfg.name} weights, fp64 numpy: "
                       f"weight dequant {t_dq:.2f} s + fwd/bwd {t - t_dq:.2f} s",
             "tokens_per_s": round(tokens / t, 3), "seconds": round(t, 3)}
@@ -235,8 +254,10 @@ def bench_quantize(a):
         t0 = time.perf_counter()
         onf4.quantize(bits)
         t = time.perf_counter() - t0
+        model, nproc = host_cpu()
         out["cpu_baseline"] = {"value": round(rows * cfg.d * QUANT_BYTES_PER_WEIGHT / t / 1e9, 4),
-                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": model,
+                               "nproc": nproc,
                                "sample": f"{rows} of {cfg.h} gate rows ({rows * cfg.d} weights), fp64 numpy",
                                "seconds": round(t, 3)}
     print(json.dumps(out), flush=True)
@@ -366,8 +387,9 @@ def bench_fast(a):
         loss, ce, lse, n = F.cross_entropy_fwd(l64, lab_np[:rows])
         F.cross_entropy_bwd(l64, lab_np[:rows], lse, n)
         t = time.perf_counter() - t0
+        model, nproc = host_cpu()
         out["cpu_baseline"] = {"value": round(total * rows / m / t / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "kind": "oracle", "cpu_model": model, "nproc": nproc,
                                "sample": f"{rows} of {m} tokens, fp64 numpy (device-to-host copies included)",
                                "seconds": round(t, 3)}
     print(json.dumps(out), flush=True)
