@@ -129,23 +129,51 @@ __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
 // and 8 lanes a 64-weight block, so a wave reads 1 KB contiguously. Per
 // block: absmax = max |w| (exact: a bf16 value, stored as fp32), reduced over
 // the block's 8 lanes. The code of w is the level nearest to w / absmax with
-// ties to the lower code, found as the number of level midpoints
-// mu_i = (L_i + L_{i+1}) / 2 with w > mu_i * absmax, compared in fp64: both
-// mu_i and the product are exact there (24 + 8 significant bits), so the
-// comparison is the exact one. A quotient of two bf16 values is either on a
-// midpoint or at least 2^-34 (relative) away from it, so a nearest-level search
-// on the fp64 quotient gives the same codes. An all-zero block gets absmax 0
-// and code 7 (the exact zero) everywhere. Weights must be finite. Packing as
-// for the dequant: element 2j in the high nibble of byte j.
+// ties to the lower code, i.e. the number of level midpoints
+// mu_i = (L_i + L_{i+1}) / 2 with w > mu_i * absmax. Both mu_i and the
+// product t_i = mu_i * absmax are exact in fp64 (24 + 8 significant bits).
+// Because w is a bf16 value, w > t_i exactly when w >= T_i, where T_i is the
+// smallest bf16 value above t_i; T_i and w are exact in fp32, so the count
+// is taken with fp32 compares. Each lane of a block forms two of the 15
+// thresholds (one fp64 product each) and the block's 8 lanes exchange them;
+// each weight then takes a 4-step binary search over the sorted T_i. A
+// quotient of two bf16 values is either on a midpoint or at least 2^-34
+// (relative) away from it, so a nearest-level search on the fp64 quotient
+// gives the same codes. An all-zero block gets absmax 0 and code 7 (the
+// exact zero) everywhere. Weights must be finite. Packing as for the
+// dequant: element 2j in the high nibble of byte j.
+
+// Smallest bf16 value strictly above t (t finite; +inf past the largest).
+__device__ __forceinline__ float bf16_above(double t) {
+  float x = (float)t;                                   // round to nearest fp32
+  if ((double)x <= t) {                                  // step up to the next fp32
+    uint32_t b = __float_as_uint(x);
+    if (x == 0.0f) b = 0x00000001u;                      // +/-0 -> smallest positive
+    else b = (x > 0.0f) ? b + 1u : b - 1u;
+    x = __uint_as_float(b);
+  }
+  // now x is the smallest fp32 above t; round it up to the bf16 grid
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0xFFFFu) != 0u) {
+    if (x > 0.0f) b = (b + 0x10000u) & 0xFFFF0000u;      // away from zero = up
+    else b &= 0xFFFF0000u;                                // toward zero = up
+  }
+  return __uint_as_float(b);
+}
+
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t* __restrict__ w,
                                                            int64_t nblocks,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax) {
-  double mu[15];
-#pragma unroll
-  for (int i = 0; i < 15; ++i)
-    mu[i] = 0.5 * ((double)__uint_as_float(c_nf4_levels[i]) + (double)__uint_as_float(c_nf4_levels[i + 1]));
   const int lane = threadIdx.x & 63;
+  const int sub = lane & 7;            // lane within the block's 8
+  // this lane's two midpoints: mu_{2 sub} and mu_{2 sub + 1} (index 15 unused)
+  double mu2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = min(2 * sub + h, 14);
+    mu2[h] = 0.5 * ((double)__uint_as_float(c_nf4_levels[i]) + (double)__uint_as_float(c_nf4_levels[i + 1]));
+  }
   const int64_t groups = nblocks * 8;   // 8-weight groups
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   // base is wave-aligned, so the loop condition is uniform across the wave and
@@ -168,16 +196,32 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t* __res
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     amax = fmaxf(amax, __shfl_xor(amax, 4));
-    double t[15];
+    // thresholds T_0..T_14 of this block, ascending (amax > 0); two per lane
+    const float ta = bf16_above(mu2[0] * (double)amax);
+    const float tb = bf16_above(mu2[1] * (double)amax);
+    float T[16];
+    const int gl = lane & ~7;
 #pragma unroll
-    for (int i = 0; i < 15; ++i) t[i] = mu[i] * (double)amax;
+    for (int s2 = 0; s2 < 8; ++s2) {
+      T[2 * s2] = __shfl(ta, gl + s2);
+      T[2 * s2 + 1] = __shfl(tb, gl + s2);
+    }
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double x = (double)wf[e];
-      uint32_t c = 0;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) c += x > t[i] ? 1u : 0u;
+      const float x = wf[e];
+      // c = #{i : x >= T_i} over the 15 sorted thresholds, by binary search:
+      // each step compares against the threshold that halves the candidates
+      const bool b3 = x >= T[7];
+      const uint32_t c3 = b3 ? 8u : 0u;
+      const bool b2 = x >= (b3 ? T[11] : T[3]);
+      const uint32_t c2 = c3 + (b2 ? 4u : 0u);
+      const float t1 = b3 ? (b2 ? T[13] : T[9]) : (b2 ? T[5] : T[1]);
+      const bool b1 = x >= t1;
+      const uint32_t c1 = c2 + (b1 ? 2u : 0u);
+      const float t0a = b3 ? (b2 ? (b1 ? T[14] : T[12]) : (b1 ? T[10] : T[8]))
+                           : (b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]));
+      uint32_t c = c1 + (x >= t0a ? 1u : 0u);
       if (amax == 0.0f) c = 7;
       // element 2j -> high nibble of byte j
       word |= c << (8 * (e >> 1) + ((e & 1) ? 0 : 4));
