@@ -9,13 +9,10 @@
 // hi/lo is a two-term bf16 split of the fp32 product, which keeps the LoRA
 // term accurate to ~2^-17 relative on bf16 matrix cores.
 //
-// Two kernels share the arguments (GemmArgs) and the epilogues.
-//
-// gemm_bf16_kernel (B in bf16: a staged dequant, or 16-bit base weights):
-// 256 x 256 output tile per workgroup of 4 waves (one per SIMD) laid out
-// 2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256 fp32
-// accumulators per lane). K is walked in 64-wide steps. Operands reach LDS
-// through buffer loads straight into LDS (one buffer resource per operand
+// gemm_bf16_kernel: 256 x 256 output tile per workgroup of 4 waves (one per
+// SIMD) laid out 2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32x16 tiles (256
+// fp32 accumulators per lane). K is walked in 64-wide steps. Operands reach
+// LDS through buffer loads straight into LDS (one buffer resource per operand
 // tile, so rows past M or N read as zeros), into a ring of five 32 KB
 // half-stage slots (one operand of one step each): while a step reads two
 // slots, the next step and a half are in flight. The 1 KB load blocks are
@@ -28,21 +25,18 @@
 // dY_p W_p over separately stored dY_p), and an epilogue that writes column
 // ranges to three outputs (q, k, v from one GEMM).
 //
-// gemm_nt_kernel (B as NF4 codes, dequantized in the tile): 256 x 256 tile
-// per workgroup of 8 waves (2 per SIMD) laid out 2 x 4, each wave 128 x 64 =
-// 4 x 2 MFMA 32x32x16 tiles. K is walked in 64-wide steps through a 2-deep
-// bf16 LDS ring; LDS rows are 128 B with the 16-byte chunk index
-// XOR-swizzled by (row >> 1) & 7. The feed carries the 4-bit codes and the
-// fp32 absmax (8 KB + 1 KB per step instead of 32 KB of bf16), brought by
-// direct-to-LDS loads (global_load_lds_dwordx4) two steps ahead into a
-// 3-deep ring of their own; the block dequantizes the next step's codes in
-// LDS, bf16_rne(fp32_rne(level[code] * absmax)) exactly as the standalone
-// dequant, while its matrix cores work on the current step. BSRC_NF4_T reads
-// the weight transposed (the backward dX = dY W): the tile's rows are input
-// features, its K runs over output features, and the dequant writes the
-// transposed bf16 tile.
+// B operand: bf16 rows (a staged dequant, or 16-bit base weights), or NF4
+// codes dequantized into the ring by the workgroup itself (BSRC_NF4,
+// BSRC_NF4_PAIR, BSRC_NF4_T): 4-bit codes and an absmax per 64 weights
+// (8 KB + 1 KB per step instead of 32 KB of bf16) come into registers a step
+// ahead, and each thread forms bf16_rne(fp32_rne(level[code] * absmax)) for
+// its 64 weights with byte permutes from a per-step table, exactly as the
+// standalone dequant. The order of every instruction of such a step is fixed
+// in the source, so that the dequant work sits between the MFMAs. BSRC_NF4_T
+// reads the weight transposed (the backward dX = dY W): its slot is k-major,
+// and the B fragments come from LDS transpose reads.
 //
-// Epilogues (both kernels): each wave stages a 32-row slab of its
+// Epilogues: each wave stages a 32-row slab of its
 // accumulators through its own LDS region, so only wave-local ordering is
 // needed, and stores 16 bytes per lane. The gated epilogues take the
 // activation as a compile-time constant (one branch per launch, none per
@@ -74,26 +68,7 @@ namespace qlora {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
-constexpr int NSTAGE = 2;
-
-// Per-stage LDS layout (bytes): A [256][64] bf16, B [256][64] bf16, then (NF4
-// modes) the raw codes of the step (8 KB) and 256 fp32 absmax (+ a spare copy).
-constexpr int A_BYTES = BM * BK * 2;
-constexpr int B_BYTES = BN * BK * 2;
-constexpr int C_BYTES = 8192;
-constexpr int S_BYTES = 2048;
-constexpr int STAGE_BF16 = A_BYTES + B_BYTES;
-// NF4 modes: the raw codes and absmax of a k-step (C_BYTES + S_BYTES) have a
-// ring of their own, 3 deep, so that they are fetched two steps ahead: they
-// are needed in the middle of the step before theirs (for the dequant).
-constexpr int RAW_BYTES = C_BYTES + S_BYTES;
-constexpr int NRAW = 3;
-
-// element offset of (row, 16-byte chunk) in a [rows][64] bf16 LDS tile
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
-}
+constexpr int BM = 256, BN = 256, BK = 64;
 
 __device__ __forceinline__ int xcd_remap(int pid, int n) {
   const int X = 8;
@@ -103,15 +78,6 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// 16 bytes per lane from global memory straight into LDS at base + 16*lane.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
-}
-// 4 bytes per lane into LDS at base + 4*lane.
-__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
-}
 
 // LDS store the compiler does not track: it is not ordered against the DMA
 // still in flight to other LDS regions (the compiler would otherwise wait for
@@ -164,438 +130,7 @@ __device__ __forceinline__ int lane_here() {
 
 }  // namespace
 
-__constant__ uint32_t c_nf4_levels_gemm[16] = {QLORA_NF4_LEVEL_BITS};
-
-template <int BSRC, int EPI>
-__global__ __launch_bounds__(NTHR)
-void gemm_nt_kernel(GemmArgs p) {
-  constexpr bool NF4 = BSRC != BSRC_BF16;
-  constexpr int STAGE = STAGE_BF16;
-  constexpr int RAW = NF4 ? NRAW * RAW_BYTES : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE + RAW + (NF4 ? 64 : 0)];
-  float* lut = reinterpret_cast<float*>(smem + NSTAGE * STAGE + RAW);  // NF4 only
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  if (NF4) {
-    if (tid < 16) lut[tid] = __uint_as_float(c_nf4_levels_gemm[tid]);
-  }
-
-  const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
-  const int pid = xcd_remap(blockIdx.x, ntm * ntn);
-  const int GM = 8;
-  const int per_group = GM * ntn;
-  const int group = pid / per_group;
-  const int first_m = group * GM;
-  const int gsz = min(ntm - first_m, GM);
-  const int tm = first_m + (pid % per_group) % gsz;
-  const int tn = (pid % per_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = p.K / BK;
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // ---- per-lane DMA sources (row and swizzled chunk fixed; k advances) ----
-  // A/B tile: wave w, instruction j fills LDS slots (w*4 + j)*64 + lane of the
-  // [256][8 x 16 B] tile; slot -> (row, physical chunk) -> logical chunk.
-  const uint16_t* srcA[4];
-  const uint16_t* srcB[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int slot = (wave * 4 + j) * 64 + lane;
-    const int row = slot >> 3, phys = slot & 7;
-    const int chunk = phys ^ ((row >> 1) & 7);
-    srcA[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + chunk * 8;
-    if (!NF4) srcB[j] = p.B + (int64_t)min(n0 + row, p.N - 1) * p.ldb + chunk * 8;
-  }
-  // NF4 raw data of one k-step: 8 KB of codes + 256 absmax; wave w moves one
-  // 1 KB piece of codes and one 256 B piece of absmax (waves 4-7 duplicate
-  // the absmax pieces of waves 0-3 into a spare copy, so every wave issues
-  // the same number of loads).
-  //   BSRC_NF4 / _PAIR: codes piece = rows w*32 .. w*32+31 of the tile
-  //     (32 B = 64 codes each), absmax = one value per tile row.
-  //   BSRC_NF4_T: the tile's K runs over weight rows: codes piece = weight
-  //     rows k0 + w*8 .. +7, 128 B each (the tile's 256 input features);
-  //     absmax = 64 weight rows x 4 blocks of 64 input features.
-  const uint8_t* srcC = nullptr;
-  const float* srcS = nullptr;
-  const uint8_t* srcC1 = nullptr;  // transposed mode: second stacked weight
-  const float* srcS1 = nullptr;
-  int64_t cstep = 0, sstep = 0;    // source advance per k-step (bytes / floats)
-  if (NF4) {
-    if (BSRC == BSRC_NF4_T) {
-      // weight [Nw][Kw]: Nw = GEMM K (reduction) rows, Kw = GEMM N features
-      const int64_t kw = p.N;
-      const int crow = wave * 8 + (lane >> 3);                        // weight row in step
-      const int ccol = min(n0 + (lane & 7) * 32, p.N - 32);           // first feature of the piece
-      srcC = p.codes0 + (int64_t)crow * (kw >> 1) + (ccol >> 1);
-      srcC1 = p.codes1 ? p.codes1 + (int64_t)crow * (kw >> 1) + (ccol >> 1) : nullptr;
-      cstep = (int64_t)BK * (kw >> 1);
-      const int srow = (wave & 3) * 16 + (lane >> 2);                 // weight row in step
-      const int sblk = min((n0 >> 6) + (lane & 3), (p.N >> 6) - 1);   // 64-feature block
-      srcS = p.absmax0 + (int64_t)srow * (kw >> 6) + sblk;
-      srcS1 = p.absmax1 ? p.absmax1 + (int64_t)srow * (kw >> 6) + sblk : nullptr;
-      sstep = (int64_t)BK * (kw >> 6);
-    } else {
-      const int r = wave * 32 + (lane >> 1);
-      int gn = min(n0 + r, p.N - 1);
-      const uint8_t* codes = p.codes0;
-      const float* amax = p.absmax0;
-      int64_t wrow = gn;
-      if (BSRC == BSRC_NF4_PAIR) {
-        const int which = (gn >> 5) & 1;
-        wrow = (int64_t)((gn >> 6) << 5) + (gn & 31);
-        codes = which ? p.codes1 : p.codes0;
-        amax = which ? p.absmax1 : p.absmax0;
-      }
-      srcC = codes + wrow * (int64_t)(p.K >> 1) + (lane & 1) * 16;
-      cstep = BK >> 1;
-      const int r2 = (wave & 3) * 64 + lane;
-      gn = min(n0 + r2, p.N - 1);
-      codes = p.codes0;
-      amax = p.absmax0;
-      wrow = gn;
-      if (BSRC == BSRC_NF4_PAIR) {
-        const int which = (gn >> 5) & 1;
-        wrow = (int64_t)((gn >> 6) << 5) + (gn & 31);
-        amax = which ? p.absmax1 : p.absmax0;
-      }
-      srcS = amax + wrow * (int64_t)(p.K >> 6);
-      sstep = 1;
-    }
-  }
-
-  auto stage_ptr = [&](int kt) { return smem + (kt % NSTAGE) * STAGE; };
-  auto raw_ptr = [&](int kt) { return smem + NSTAGE * STAGE + (kt % NRAW) * RAW_BYTES; };
-  // NF4: codes and absmax of step kt into its raw slot (2 loads per wave)
-  auto issue_raw = [&](int kt) {
-    uint8_t* rw = raw_ptr(kt);
-    const uint8_t* c = srcC;
-    const float* sc = srcS;
-    int kl = kt;
-    if (BSRC == BSRC_NF4_T && p.ksplit > 0 && kt * BK >= p.ksplit) {
-      c = srcC1;
-      sc = srcS1;
-      kl = kt - p.ksplit / BK;
-    }
-    dma16(c + kl * cstep, rw + wave * 1024);
-    dma4(sc + kl * sstep, rw + C_BYTES + wave * 256);
-  };
-  // the bf16 operands of step kt (A; B too when it is not NF4): 4 or 8 loads per wave
-  auto issue = [&](int kt) {
-    uint8_t* st = stage_ptr(kt);
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(srcA[j] + k0, st + (wave * 4 + j) * 1024);
-    if (!NF4) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(srcB[j] + k0, st + A_BYTES + (wave * 4 + j) * 1024);
-    }
-  };
-
-  // NF4: dequantize the raw codes of a landed k-step into its bf16 B tile.
-  auto dequant_stage = [&](int kt) {
-    uint8_t* st = stage_ptr(kt);
-    const uint8_t* cb = raw_ptr(kt);
-    const float* sb = (const float*)(raw_ptr(kt) + C_BYTES);
-    uint16_t* bt = (uint16_t*)(st + A_BYTES);
-    if (BSRC != BSRC_NF4_T) {
-      // thread t: tile row t/2, 32 weights (k half t&1) = chunks 4*(t&1) .. +3
-      const int row = tid >> 1, half = tid & 1;
-      const u32x4_t w = *(const u32x4_t*)(cb + row * 32 + half * 16);
-      const float amax = sb[row];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4_t o;
-        const uint32_t word = w[c];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t byte = (word >> (8 * b)) & 0xFFu;
-          o[b] = pack_bf16x2(lut[byte >> 4] * amax, lut[byte & 0xFu] * amax);
-        }
-        lds_store16(&bt[swz(row, half * 4 + c)], o);
-      }
-    } else {
-      // thread t: tile rows (input features) f0 .. f0+3, f0 = 4*(t & 63),
-      // K (weight rows) q0 .. q0+7, q0 = 8*(t >> 6). Codes of weight row q,
-      // features f0..f0+3 are 2 bytes at q*128 + f0/2; absmax of (q, f0/64).
-      const int f0 = 4 * (tid & 63), q0 = 8 * (tid >> 6);
-      float w[8][4];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t two = *(const uint16_t*)(cb + (q0 + q) * 128 + (f0 >> 1));
-        const float amax = sb[(q0 + q) * 4 + (f0 >> 6)];
-        w[q][0] = lut[(two >> 4) & 0xFu] * amax;   // byte 0 high nibble: feature f0
-        w[q][1] = lut[two & 0xFu] * amax;          // byte 0 low nibble: f0 + 1
-        w[q][2] = lut[(two >> 12) & 0xFu] * amax;  // byte 1 high nibble: f0 + 2
-        w[q][3] = lut[(two >> 8) & 0xFu] * amax;   // byte 1 low nibble: f0 + 3
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        u32x4_t o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(w[2 * e][f], w[2 * e + 1][f]);
-        lds_store16(&bt[swz(f0 + f, q0 >> 3)], o);
-      }
-    }
-  };
-
-  // Fragments of one 16-wide K substep: 4 A (rows of the wave) + 2 B (columns).
-  struct Frag {
-    bf16x8_t a[4], b[2];
-  };
-  auto load_frag = [&](Frag& f, const uint8_t* st, int ks) {
-    const uint16_t* sa = (const uint16_t*)st;
-    const uint16_t* sb = (const uint16_t*)(st + A_BYTES);
-    const int ch = 2 * ks + (lane >> 5);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      f.a[mt] = *(const bf16x8_t*)&sa[swz(wm * 128 + mt * 32 + (lane & 31), ch)];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      f.b[nt] = *(const bf16x8_t*)&sb[swz(wn * 64 + nt * 32 + (lane & 31), ch)];
-  };
-  auto mma = [&](const Frag& f) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
-  };
-  auto compute = [&](const uint8_t* st, int nsub) {
-    for (int ks = 0; ks < nsub; ++ks) {
-      Frag f;
-      load_frag(f, st, ks);
-      mma(f);
-    }
-  };
-
-  // ---- main K loop: 2-deep ring, DMA of step kt+1 in flight during step kt ----
-  // Iteration kt: issue step kt+1; (NF4) once its codes land, dequantize
-  // them; the MFMAs of step kt run meanwhile, with the fragments of the next
-  // substep (and, across the barrier, of step kt+1's first substep) loaded
-  // ahead. The closing barrier publishes step kt+1 and retires step kt.
-  // NF4 issue order inside step kt: A of kt+1 (4 loads), then codes and
-  // absmax of kt+2 (2 loads). Mid-step the codes of kt+1 (issued a step
-  // earlier, older than both) must have landed: wait_vm<4 + 2>; at the end
-  // A of kt+1 must have: wait_vm<2> (the codes of kt+2 may still fly).
-  if (NF4) {
-    issue_raw(0);
-    issue(0);
-    if (nk > 1) issue_raw(1);
-    if (nk > 1) wait_vm<2>(); else wait_vm<0>();
-  } else {
-    issue(0);
-    wait_vm<0>();
-  }
-  ring_barrier();   // step 0 raw data (and lut) visible
-  if (NF4) {
-    dequant_stage(0);
-    if (nk > 1) wait_vm<2>(); else wait_vm<0>();   // its LDS stores done (codes of step 1 may fly)
-    ring_barrier();
-  }
-  Frag f0, f1;
-  load_frag(f0, stage_ptr(0), 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    const bool more2 = kt + 2 < nk;
-    if (more) issue(kt + 1);
-    if (NF4 && more2) issue_raw(kt + 2);
-    const uint8_t* st = stage_ptr(kt);
-    load_frag(f1, st, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frag(f0, st, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (NF4 && more) {
-      if (more2) wait_vm<6>(); else wait_vm<4>();   // codes + absmax of step kt+1 landed
-      ring_barrier();  // ... for every wave
-      dequant_stage(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    load_frag(f1, st, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (NF4 && more2) wait_vm<2>();   // step kt+1 landed (codes of kt+2 may fly); LDS done
-    else wait_vm<0>();
-    ring_barrier();
-    load_frag(f0, stage_ptr(more ? kt + 1 : kt), 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();
-
-  // ---- K-extension (LoRA up-projection), bf16 both sides, via registers ----
-  for (int e = 0; e * BK < p.KE; ++e) {
-    const int c0 = e * BK;
-    const int nch = min(BK, p.KE - c0) >> 3;
-    uint16_t* sa = (uint16_t*)smem;
-    uint16_t* sb = (uint16_t*)(smem + A_BYTES);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 64 * i, chunk = tid & 7;
-      const int ga = min(m0 + row, p.M - 1), gb = min(n0 + row, p.N - 1);
-      u32x4_t za = {0u, 0u, 0u, 0u}, zb = {0u, 0u, 0u, 0u};
-      if (chunk < nch) {
-        za = *(const u32x4_t*)(p.Ae + (int64_t)ga * p.ldae + c0 + chunk * 8);
-        zb = *(const u32x4_t*)(p.Be + (int64_t)gb * p.ldbe + c0 + chunk * 8);
-      }
-      *(u32x4_t*)&sa[swz(row, chunk)] = za;
-      *(u32x4_t*)&sb[swz(row, chunk)] = zb;
-    }
-    __syncthreads();
-    compute(smem, (nch * 8 + 15) >> 4);
-    __syncthreads();
-  }
-
-  // ---- epilogue ----
-  // acc[mt][nt][v] holds C[row][col] with
-  //   row = wm*128 + mt*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*64 + nt*32 + lane%32.
-  // Each 32-row slab (one mt) of a wave's 128 x 64 tile goes through LDS
-  // (fp32, padded pitch) so that the global side moves 16 contiguous bytes
-  // per lane; register indices stay compile-time constants.
-  constexpr int SP = 72;  // floats per staged row: 4*SP = 32 mod 64 banks
-  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SP);  // fits in the ring
-  const int row0 = m0 + wm * 128;
-  const int col0 = n0 + wn * 64;
-  // the activation is fixed per launch: one branch here, none per value
-  auto slabs = [&](auto act_c) {
-    constexpr int ACT = decltype(act_c)::value;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      // ACT_BWD: this slab's g and u are fetched before the staging so that
-      // their latency overlaps it (rows past M read nothing)
-      u32x4_t gw[4], uw[4];
-      if (EPI == EPI_ACT_BWD) {
-        const int cc = (lane & 7) * 8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = row0 + mt * 32 + q * 8 + (lane >> 3), col = col0 + cc;
-          gw[q] = u32x4_t{0u, 0u, 0u, 0u};
-          uw[q] = u32x4_t{0u, 0u, 0u, 0u};
-          if (row < p.M && col < p.N) {
-            const int64_t o = (int64_t)row * p.hdim + col;
-            gw[q] = *(const u32x4_t*)(p.g_in + o);
-            uw[q] = *(const u32x4_t*)(p.u_in + o);
-          }
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * SP + nt * 32 + (lane & 31)] = acc[mt][nt][v];
-      wave_sync();   // the staging region is this wave's own
-      if (EPI == EPI_STORE) {
-        // lane: 8 consecutive columns of one row per step, 8 rows per step
-        const int cc = (lane & 7) * 8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rr = q * 8 + (lane >> 3);
-          const int row = row0 + mt * 32 + rr;
-          const int col = col0 + cc;
-          const f32x4_t x0 = *(const f32x4_t*)&stage[rr * SP + cc];
-          const f32x4_t x1 = *(const f32x4_t*)&stage[rr * SP + cc + 4];
-          if (row < p.M && col < p.N) {
-            u32x4_t o;
-            o[0] = pack_bf16x2(x0[0], x0[1]);
-            o[1] = pack_bf16x2(x0[2], x0[3]);
-            o[2] = pack_bf16x2(x1[0], x1[1]);
-            o[3] = pack_bf16x2(x1[2], x1[3]);
-            *(u32x4_t*)(p.C + (int64_t)row * p.ldc + col) = o;
-          }
-        }
-      } else if (EPI == EPI_GATEUP) {
-        // staged columns: [gate j0..j0+31 | up j0..j0+31], j0 = col0 / 2
-        const int jj = (lane & 3) * 8;
-        const int64_t j = (int64_t)(col0 >> 1) + jj;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int rr = q * 16 + (lane >> 2);
-          const int row = row0 + mt * 32 + rr;
-          const float* gs = &stage[rr * SP + jj];
-          const float* us = gs + 32;
-          if (row < p.M && col0 < p.N) {
-            float gv[8], uv[8];
-            *(f32x4_t*)gv = *(const f32x4_t*)gs;
-            *(f32x4_t*)(gv + 4) = *(const f32x4_t*)(gs + 4);
-            *(f32x4_t*)uv = *(const f32x4_t*)us;
-            *(f32x4_t*)(uv + 4) = *(const f32x4_t*)(us + 4);
-            u32x4_t og, ou, oh;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float hv[2];
-              uint32_t gb[2], ub[2];
-#pragma unroll
-              for (int t = 0; t < 2; ++t) {
-                gb[t] = f32_to_bf16(gv[2 * e + t]);
-                ub[t] = f32_to_bf16(uv[2 * e + t]);
-                hv[t] = act_fwd_t<ACT>(bf16_to_f32(gb[t])) * bf16_to_f32(ub[t]);
-              }
-              og[e] = gb[0] | (gb[1] << 16);
-              ou[e] = ub[0] | (ub[1] << 16);
-              oh[e] = pack_bf16x2(hv[0], hv[1]);
-            }
-            const int64_t o = (int64_t)row * p.hdim + j;
-            *(u32x4_t*)(p.g_out + o) = og;
-            *(u32x4_t*)(p.u_out + o) = ou;
-            *(u32x4_t*)(p.h_out + o) = oh;
-          }
-        }
-      } else {  // EPI_ACT_BWD: staged values are dH
-        const int cc = (lane & 7) * 8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rr = q * 8 + (lane >> 3);
-          const int row = row0 + mt * 32 + rr;
-          const int col = col0 + cc;
-          if (row < p.M && col < p.N) {
-            float dh[8];
-            *(f32x4_t*)dh = *(const f32x4_t*)&stage[rr * SP + cc];
-            *(f32x4_t*)(dh + 4) = *(const f32x4_t*)&stage[rr * SP + cc + 4];
-            u32x4_t odg, odu;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float dg[2], du[2];
-#pragma unroll
-              for (int t = 0; t < 2; ++t) {
-                const float g = bf16_to_f32(t ? (gw[q][e] >> 16) : (gw[q][e] & 0xFFFFu));
-                const float u = bf16_to_f32(t ? (uw[q][e] >> 16) : (uw[q][e] & 0xFFFFu));
-                float a, da;
-                act_fwd_bwd_t<ACT>(g, &a, &da);
-                const float d = dh[2 * e + t];
-                dg[t] = d * u * da;
-                du[t] = d * a;
-              }
-              odg[e] = pack_bf16x2(dg[0], dg[1]);
-              odu[e] = pack_bf16x2(du[0], du[1]);
-            }
-            const int64_t od = (int64_t)row * (2 * p.hdim) + col;
-            *(u32x4_t*)(p.dgu + od) = odg;
-            *(u32x4_t*)(p.dgu + od + p.hdim) = odu;
-          }
-        }
-      }
-      wave_sync();
-    }
-  };
-  if ((EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.act != 0)
-    slabs(std::integral_constant<int, 1>());
-  else
-    slabs(std::integral_constant<int, 0>());
-}
-
+constexpr uint32_t kNf4Lev[16] = {QLORA_NF4_LEVEL_BITS};
 
 // ===========================================================================
 // bf16-B GEMM: one 256 x 256 tile per workgroup of 4 waves (1 per SIMD), each
@@ -644,9 +179,25 @@ __device__ __forceinline__ int rec_bytes(int64_t rows, int64_t ld) {
 
 // offset that no buffer covers: the load returns zeros
 constexpr uint32_t OOB = 0x80000000u;
+
+// buffer resource over nrec bytes at base (uniform values, kept in SGPRs)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, int nrec) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding; LDS
+// operations are not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 }  // namespace
 
-template <int EPI, bool SEGA>
+template <int EPI, bool SEGA, int BSRC>
 __global__ __launch_bounds__(256)
 void gemm_bf16_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * G_SLOT];   // all 160 KB of LDS
@@ -695,6 +246,213 @@ void gemm_bf16_kernel(GemmArgs p) {
   const uint64_t bA = (uint64_t)(p.A + (int64_t)m0 * p.lda), bB = (uint64_t)(p.B + (int64_t)n0 * p.ldb);
   const int nA = rec_bytes(rowsA, p.lda);
   const int nB = rec_bytes(rowsB, p.ldb);
+
+  // ---- NF4 B operand (BSRC other than BSRC_BF16) ----
+  // The B half-stage of a step is written, not loaded: each thread turns the
+  // 64 codes of one weight row and one 64-wide block (one absmax; brought
+  // into registers a step ahead) into bf16 and stores them in LDS. Values are
+  // bf16_rne(fp32_rne(level * absmax)), the contract of the dequant kernels:
+  // the 16 possible values of the thread's block are formed once per step
+  // (that product and rounding, for each level) and each code selects one
+  // with byte permutes.
+  //   Row-major (NF4, NF4_PAIR): a thread owns one tile row R (the weight row
+  //     of output column n0 + R, 64 codes of the step); its stores fill the
+  //     slot layout above, chunk (j + f) & 7 in store j with f = 2 ((lane >> 1)
+  //     & 3) so that the 16 lanes of each store phase hit 16 different
+  //     positions. Waves 0, 1 own gate rows, waves 2, 3 up rows (in pair mode
+  //     they read different weights).
+  //   Transposed (NF4_T): the tile's K rows are weight rows, its columns the
+  //     weight's features. Lane l owns weight row l of the step, wave w
+  //     features 64 w .. 64 w + 63 of the tile. The slot is k-major: row k
+  //     (512 bytes) holds feature n = 8 x + y at position p = 32 y + x, and
+  //     16-byte chunk c of the row at physical chunk c ^ sw(k). A thread's
+  //     store y writes its 8 features 8 x + y (x = 8 w .. 8 w + 7). The B
+  //     fragments are read with the LDS transpose read (ds_read_b64_tr_b16),
+  //     which gives each lane of a 16-lane group 4 consecutive K values of
+  //     its own column; the swizzle keeps both the stores and these reads
+  //     free of bank conflicts.
+  constexpr bool NF4 = BSRC != BSRC_BF16;
+  constexpr bool NT = BSRC == BSRC_NF4_T;
+  constexpr int NQ = NT ? 3 : 5;      // loads per thread per step
+  constexpr int NPART = NT ? 44 : 40; // dequant parts per step
+  struct QRegs {
+    uint32_t c[8];
+    float a[1];
+  };
+  uint64_t qcb0 = 0, qsb0 = 0, qcb1 = 0, qsb1 = 0;   // codes / absmax bases (NF4_T: weights 0, 1)
+  int qcn0 = 0, qsn0 = 0, qcn1 = 0, qsn1 = 0;        // their buffer sizes in bytes
+  uint32_t qvo[4] = {0u, 0u, 0u, 0u}, qso = 0u;      // per-lane byte offsets of the loads
+  uint32_t woff[8];                                 // byte offsets of the 8 stores in a slot
+  uint32_t tboff[2][4];                             // NF4_T: B fragment read offsets [half][tile]
+  int kq1 = nk;                                     // NF4_T: first k-step of weight 1
+  const int qk2 = p.K / 2, qn2 = p.N / 2;
+  auto tsw = [](int k) { return 2 * (k & 1) + 8 * ((k >> 1) & 1) + ((k >> 2) & 1) + 4 * ((k >> 3) & 1); };
+  if constexpr (NF4) {
+    if constexpr (!NT) {
+      const int R = 128 * (wave & 1) + 64 * (lane >> 5) + 32 * (wave >> 1) + (lane & 31);
+      const int gn = n0 + R;
+      int64_t wrow = gn, wrows = p.N;
+      const uint8_t* codes = p.codes0;
+      const float* am = p.absmax0;
+      if (BSRC == BSRC_NF4_PAIR) {
+        wrow = (int64_t)(gn >> 6) * 32 + (gn & 31);
+        wrows = p.N / 2;
+        if (wave >= 2) { codes = p.codes1; am = p.absmax1; }
+      }
+      // rows at or past the weight's end read as zeros: level 0 times absmax 0
+      qcb0 = (uint64_t)codes;
+      qcn0 = (int)min<int64_t>(wrows * qk2, 0x7fffffff);
+      qsb0 = (uint64_t)am;
+      qsn0 = (int)min<int64_t>(wrows * (p.K / 64) * 4, 0x7fffffff);
+      const bool in = wrow < wrows;
+      const int f = 2 * ((lane >> 1) & 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qvo[i] = in ? (uint32_t)(wrow * qk2) + (uint32_t)(((f + 2 * i) & 7) * 4) : OOB;
+      qso = in ? (uint32_t)(wrow * (p.K / 64) * 4) : OOB;
+      const int q = R >> 3, u = (R & 7) >> 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) woff[j] = q * 1024 + u * 256 + ((((R & 1) * 8 + ((j + f) & 7)) ^ (q & 15)) * 16);
+    } else {
+      const int64_t rows0 = p.ksplit > 0 ? p.ksplit : p.K;
+      kq1 = p.ksplit > 0 ? p.ksplit / BK : nk;
+      qcb0 = (uint64_t)p.codes0;
+      qcn0 = (int)min<int64_t>(rows0 * qn2, 0x7fffffff);
+      qsb0 = (uint64_t)p.absmax0;
+      qsn0 = (int)min<int64_t>(rows0 * (p.N / 64) * 4, 0x7fffffff);
+      if (p.ksplit > 0) {
+        qcb1 = (uint64_t)p.codes1;
+        qcn1 = (int)min<int64_t>((p.K - rows0) * qn2, 0x7fffffff);
+        qsb1 = (uint64_t)p.absmax1;
+        qsn1 = (int)min<int64_t>((p.K - rows0) * (p.N / 64) * 4, 0x7fffffff);
+      }
+      // features at or past N (a whole wave's block, N being a multiple of
+      // 64) read as zeros
+      const int f0 = n0 + 64 * wave;
+      const bool in = f0 < p.N;
+      qvo[0] = in ? (uint32_t)lane * (uint32_t)qn2 + (uint32_t)(f0 / 2) : OOB;
+      qvo[1] = qvo[0] + (in ? 16u : 0u);
+      qso = in ? ((uint32_t)lane * (uint32_t)(p.N / 64) + (uint32_t)(f0 / 64)) * 4u : OOB;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) woff[y] = lane * 512 + (((4 * y + wave) ^ tsw(lane)) << 4);
+      // fragment reads: lane L of a 16-lane group g supplies, for the group's
+      // element e = (L & 15) >> 2, the 4 columns starting at 16 wn + 4 (L & 3)
+      // of feature class y = 2 nt + (g & 1), K row 8 (L >> 5) + 4 half + e
+      const int e = (lane & 15) >> 2, a4 = lane & 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int k = 8 * (lane >> 5) + 4 * h + e;
+          const int pos = (2 * nt + ((lane >> 4) & 1)) * 32 + 16 * wn + 4 * a4;
+          tboff[h][nt] = k * 512 + ((((pos >> 3) ^ tsw(k)) << 4) | ((pos & 7) << 1));
+        }
+    }
+  }
+  // codes and absmax of k-step kt into r
+  auto issue_q = [&](int kt, QRegs& r) {
+    if constexpr (!NT) {
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(qcb0, qcn0), rs = make_rsrc(qsb0, qsn0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, qvo[i], kt * 32, 0);
+        r.c[2 * i] = v[0];
+        r.c[2 * i + 1] = v[1];
+      }
+      r.a[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, qso, kt * 4, 0));
+    } else {
+      const bool w1 = kt >= kq1;
+      const int kl = w1 ? kt - kq1 : kt;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(w1 ? qcb1 : qcb0, w1 ? qcn1 : qcn0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(w1 ? qsb1 : qsb0, w1 ? qsn1 : qsn0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, qvo[i], kl * BK * qn2, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r.c[4 * i + t] = v[t];
+      }
+      r.a[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, qso, kl * BK * (p.N / 64) * 4, 0));
+    }
+  };
+  // byte b of the result: plane byte s_b of value (s_b + 8 * bit 3) where the
+  // selector bytes s hold the low 3 bits and m holds b + 4 * bit 3. P[0..3]
+  // hold the low bytes of the 16 values (4 per register), P[4..7] the high.
+  auto qlook = [](const uint32_t* P, uint32_t sel, uint32_t m) {
+    return __builtin_amdgcn_perm(__builtin_amdgcn_perm(P[3], P[2], sel), __builtin_amdgcn_perm(P[1], P[0], sel), m);
+  };
+  // The table in parts: parts 0-3 form two of its bf16 pairs each, parts 4-5
+  // two plane registers each.
+  auto qtable_part = [&](int part, const QRegs& r, uint32_t (&D)[8], uint32_t (&P)[8]) {
+    if (part < 4) {
+#pragma unroll
+      for (int i = 2 * part; i < 2 * part + 2; ++i)
+        D[i] = pack_bf16x2(__builtin_bit_cast(float, kNf4Lev[2 * i]) * r.a[0],
+                           __builtin_bit_cast(float, kNf4Lev[2 * i + 1]) * r.a[0]);
+    } else {
+#pragma unroll
+      for (int k = 2 * (part - 4); k < 2 * (part - 4) + 2; ++k) {
+        P[k] = __builtin_amdgcn_perm(D[2 * k + 1], D[2 * k], 0x06040200u);
+        P[4 + k] = __builtin_amdgcn_perm(D[2 * k + 1], D[2 * k], 0x07050301u);
+      }
+    }
+  };
+  // A step's dequant in NPART parts, which the main loop places one per MFMA.
+  // Code dword c holds elements 8 c .. 8 c + 7 of the thread's block (element
+  // 2 m in the high nibble of byte m). Per dword: part 0 the selectors, 1 the
+  // low-byte lookups, 2 the high-byte lookups; row-major then 3 the
+  // interleave into bf16 pairs and 4 the store (chunk = dword); transposed
+  // 3 the pairs (element y, element y + 2) of the dword, then 4 parts
+  // joining dwords 2 q, 2 q + 1 into the pairs of the stores, then the 8
+  // stores (store y: elements 8 x + y).
+  struct QStep {
+    uint32_t s0[8], s1[8], m0[8], m1[8], a0[8], a1[8], b0[8], b1[8];
+    uint32_t ev[8][4];
+    u32x4_t o[8];
+  };
+  auto qpart = [&](QStep& S, int pp, const QRegs& r, const uint32_t (&P)[8], uint8_t* sbase) {
+    const int c = NT ? (pp < 32 ? pp >> 2 : 0) : pp / 5, part = NT ? (pp < 32 ? pp & 3 : 5) : pp % 5;
+    if (part == 0) {
+      const uint32_t d = r.c[c];
+      S.s0[c] = d & 0x07070707u;                          // low nibbles: elements 1, 3, 5, 7
+      S.s1[c] = (d >> 4) & 0x07070707u;                   // high nibbles: elements 0, 2, 4, 6
+      S.m0[c] = ((d >> 1) & 0x04040404u) | 0x03020100u;
+      S.m1[c] = ((d >> 5) & 0x04040404u) | 0x03020100u;
+    } else if (part == 1) {
+      S.a0[c] = qlook(P, S.s0[c], S.m0[c]);
+      S.a1[c] = qlook(P, S.s1[c], S.m1[c]);
+    } else if (part == 2) {
+      S.b0[c] = qlook(P + 4, S.s0[c], S.m0[c]);
+      S.b1[c] = qlook(P + 4, S.s1[c], S.m1[c]);
+    } else if (!NT && part == 3) {
+      const uint32_t u0 = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x05010400u);
+      const uint32_t v0 = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x05010400u);
+      const uint32_t u1 = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x07030602u);
+      const uint32_t v1 = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x07030602u);
+      S.o[c][0] = __builtin_amdgcn_perm(v0, u0, 0x05010400u);
+      S.o[c][1] = __builtin_amdgcn_perm(v0, u0, 0x07030602u);
+      S.o[c][2] = __builtin_amdgcn_perm(v1, u1, 0x05010400u);
+      S.o[c][3] = __builtin_amdgcn_perm(v1, u1, 0x07030602u);
+    } else if (!NT && part == 4) {
+      lds_store16(sbase + woff[c], S.o[c]);
+    } else if (NT && part == 3) {
+      // bf16 pairs of one dword: elements (0, 2), (4, 6), (1, 3), (5, 7)
+      S.ev[c][0] = __builtin_amdgcn_perm(S.b1[c], S.a1[c], 0x05010400u);
+      S.ev[c][1] = __builtin_amdgcn_perm(S.b1[c], S.a1[c], 0x07030602u);
+      S.ev[c][2] = __builtin_amdgcn_perm(S.b0[c], S.a0[c], 0x05010400u);
+      S.ev[c][3] = __builtin_amdgcn_perm(S.b0[c], S.a0[c], 0x07030602u);
+    } else if (NT && pp < 36) {
+      // dwords 2 q, 2 q + 1 -> word q of store y: (element y of 2 q, of 2 q + 1)
+      const int q = pp - 32;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int src = (y & 1) ? 2 + ((y >> 2) & 1) : ((y >> 2) & 1);   // ev index
+        const uint32_t sel = ((y >> 1) & 1) ? 0x07060302u : 0x05040100u;
+        S.o[y][q] = __builtin_amdgcn_perm(S.ev[2 * q + 1][src], S.ev[2 * q][src], sel);
+      }
+    } else if (NT) {
+      const int y = pp - 36;
+      lds_store16(sbase + woff[y], S.o[y]);
+    }
+  };
   // DMA: wave w, load j (0..7) fills block q = 8w + j; lane l writes position
   // l of it. Tile row and first column of that position:
   auto drow = [&](int j) {
@@ -759,13 +517,28 @@ void gemm_bf16_kernel(GemmArgs p) {
   struct Frag {
     bf16x8_t a[4], b[4];
   };
-  auto load_frag_at = [&](Frag& f, const uint8_t* sa, const uint8_t* sb, int ks) {
+  // NF4_T: B tile nt of substep ks from the k-major slot, 4 K values per
+  // transpose read
+  auto trb = [&](const uint8_t* sb, int ks, int nt) -> bf16x8_t {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(lds_ptr_t)(sb + tboff[0][nt] + ks * 8192));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(lds_ptr_t)(sb + tboff[1][nt] + ks * 8192));
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  // (B in the k-major NF4_T layout when bt, else in the DMA layout)
+  auto load_frag_at = [&](Frag& f, const uint8_t* sa, const uint8_t* sb, int ks, bool bt) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) f.a[mt] = *(const bf16x8_t*)(sa + fq + mt * 256 + fpos(ks));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) f.b[nt] = *(const bf16x8_t*)(sb + gq + nt * 256 + fpos(ks));
+    for (int nt = 0; nt < 4; ++nt) {
+      if (NT && bt) f.b[nt] = trb(sb, ks, nt);
+      else f.b[nt] = *(const bf16x8_t*)(sb + gq + nt * 256 + fpos(ks));
+    }
   };
-  auto load_frag = [&](Frag& f, int st, int ks) { load_frag_at(f, slot(2 * st), slot(2 * st + 1), ks); };
+  auto load_frag = [&](Frag& f, int st, int ks) { load_frag_at(f, slot(2 * st), slot(2 * st + 1), ks, true); };
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -796,6 +569,126 @@ void gemm_bf16_kernel(GemmArgs p) {
   // s+1's A and B; A of step s+2, issued last, may stay in flight (vmcnt
   // retires in order).
   const int ns = kt1 - kt0, nh = 2 * ns;
+  if constexpr (NF4) {
+    // NF4 B operand. The B half-stage of step s+1 goes to the slot of A of
+    // step s-1, free from the barrier that ends step s-1's third substep; it
+    // is dequantized from there (the fourth substep of step s-1) through the
+    // third substep of step s, i.e. beside 64 MFMAs. Codes of step s+2 are
+    // waited for, copied out and the codes of step s+3 issued in that fourth
+    // substep of step s: a full step of latency. A of step s+2 is loaded in
+    // the first two substeps of step s, as for bf16 B. Load order per step:
+    // A[0-3], A[4-7], codes; so the end of step s waits for A of s+1 with the
+    // codes of s+2 and A of s+2 behind it, and the fourth substep waits for
+    // the codes of s+2 with A of s+2 behind them.
+    QRegs cq, wq;
+    uint32_t P[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, D[8];
+    auto bslot = [&](int s_) { return slot(2 * s_ + 1); };
+    // the codes in cq have landed: move them to wq and issue step kt's into
+    // cq (if `next`). The moves are explicit (early-clobber outputs), so that
+    // wq never shares registers with cq: the loads into cq then reuse cq's
+    // registers and nothing in flight is copied at the loop's back edge.
+    auto take_q = [&](int kt, auto next_c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("v_mov_b32 %0, %1" : "=&v"(wq.c[i]) : "v"(cq.c[i]));
+      asm volatile("v_mov_b32 %0, %1" : "=&v"(wq.a[0]) : "v"(cq.a[0]));
+      if constexpr (decltype(next_c)::value) issue_q(kt, cq);
+    };
+    auto table_all = [&]() {
+#pragma unroll
+      for (int t = 0; t < 6; ++t) qtable_part(t, wq, D, P);
+    };
+    // Prologue, branch-free: the loads of steps 1 and 2 are issued even when
+    // the job has fewer steps (they then read rows past the end, or zeros,
+    // into slots nothing reads), so every path reaches the loop with the
+    // same loads in flight.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_half(0, j);
+    issue_q(kt0, cq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_half(2, j);
+    wait_vmem<4>();
+    take_q(kt0 + 1, std::true_type());
+    table_all();
+#pragma unroll
+    for (int j = 4; j < 8; ++j) issue_half(2, j);
+    {
+      QStep S0;
+#pragma unroll
+      for (int pp = 0; pp < NPART; ++pp) qpart(S0, pp, wq, P, bslot(0));
+    }
+    wait_vmem<4>();   // codes of step 1 (A[4-7] of step 1 behind them)
+    take_q(kt0 + 2, std::true_type());
+    table_all();
+    wait_vm<4 + NQ>();
+    ring_barrier();
+    Frag f0, f1;
+    load_frag(f0, 0, 0);
+    // one fragment register (0-3: A tiles, 4-7: B tiles) of substep ks of step st
+    auto frag1 = [&](Frag& f, int st, int ks, int idx) {
+      if (idx < 4) f.a[idx] = *(const bf16x8_t*)(slot(2 * st) + fq + idx * 256 + fpos(ks));
+      else if constexpr (NT) f.b[idx - 4] = trb(slot(2 * st + 1), ks, idx - 4);
+      else f.b[idx - 4] = *(const bf16x8_t*)(slot(2 * st + 1) + gq + (idx - 4) * 256 + fpos(ks));
+    };
+    // MFMA q of a substep: tile (q / 4, q % 4)
+    auto mma1 = [&](const Frag& f, int q) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+    };
+    // Step st, with the order of its instructions fixed: each MFMA is followed
+    // by its share of the other work. Substeps 0-2 dequantize B of step st+1
+    // (its NPART parts over their 48 MFMAs) into the slot of A of step st-1,
+    // read the next substep's fragments (one after each of the first 8 MFMAs)
+    // and load A of step st+2 (substeps 0-1, after MFMAs 8-11). Substep 3
+    // (after the barrier) takes the codes of step st+2, issues those of step
+    // st+3 and forms the table for B of step st+2.
+    // b1: B of step st+1 to write (st+1 < ns); b2: codes of step st+2 to take
+    // and A of step st+2 to load (st+2 < ns); c3: codes of step st+3 to load.
+    auto stepq = [&](int st, auto b1_c, auto b2_c, auto c3_c) {
+      constexpr bool b1 = decltype(b1_c)::value, b2 = decltype(b2_c)::value;
+      uint8_t* sb = bslot(st + 1);
+      QStep S;
+#pragma unroll
+      for (int ss = 0; ss < 3; ++ss) {
+        Frag& cur = (ss & 1) ? f1 : f0;
+        Frag& nxt = (ss & 1) ? f0 : f1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          mma1(cur, i);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < 8) frag1(nxt, st, ss + 1, i);
+          if (b2 && ss < 2 && i >= 8 && i < 12) issue_half(2 * st + 4, 4 * ss + i - 8);
+          if (b1) {
+            const int sl = 16 * ss + i;
+#pragma unroll
+            for (int pp = 0; pp < NPART; ++pp)
+              if ((pp * 48) / NPART == sl) qpart(S, pp, wq, P, sb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (b1) {
+        if (b2) wait_vm<NQ + 8>(); else wait_vm<0>();
+      }
+      ring_barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mma1(f1, i);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b1 && i < 8) frag1(f0, st + 1, 0, i);
+        if (b2) {
+          if (i == 1) take_q(kt0 + st + 3, c3_c);
+          if (i >= 2 && i < 8) qtable_part(i - 2, wq, D, P);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    int st = 0;
+    for (; st < ns - 3; ++st) stepq(st, T_(), T_(), T_());
+    if (ns >= 3) stepq(st++, T_(), T_(), F_());
+    if (ns >= 2) stepq(st++, T_(), F_(), F_());
+    stepq(st, F_(), F_(), F_());
+  } else {
   for (int i = 0; i < 4 && i < nh; ++i) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) issue_half(i, j);
@@ -848,6 +741,7 @@ void gemm_bf16_kernel(GemmArgs p) {
   } else {
     for (int st = 0; st < ns; ++st) step(st, F_(), F_());
   }
+  }   // bf16 B
   // GATEUP row product: the rank-r fragments of the wave's 64 H columns,
   // loaded here so that the wait below covers them. Waited for later, behind
   // the epilogue's conditional stores, they would cost a wait for all of those.
@@ -911,7 +805,7 @@ void gemm_bf16_kernel(GemmArgs p) {
       const int nsub = (min(BK, p.KE - e * BK) + 15) >> 4;
       for (int ks = 0; ks < nsub; ++ks) {
         Frag f;
-        load_frag_at(f, slot(0), slot(1), ks);
+        load_frag_at(f, slot(0), slot(1), ks, false);
         mma(f);
       }
       __syncthreads();
@@ -1176,13 +1070,6 @@ void gemm_bf16_kernel(GemmArgs p) {
   }
 }
 
-template <int BSRC, int EPI>
-static hipError_t launch_t(const GemmArgs& a, hipStream_t stream) {
-  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
-  gemm_nt_kernel<BSRC, EPI><<<dim3(ntm * ntn), dim3(NTHR), 0, stream>>>(a);
-  return hipGetLastError();
-}
-
 // Split-K reduction: C = bf16(sum_s part[s]) in fixed order; a thread takes 8
 // columns of one row. EPI_STORE3 routes the columns as the GEMM epilogue does.
 template <int EPI>
@@ -1213,7 +1100,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   *(u32x4_t*)dst = o;
 }
 
-template <int EPI, bool SEGA>
+template <int EPI, bool SEGA, int BSRC = BSRC_BF16>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
   const int nsplit = a.splits > 1 ? a.splits : 1;
@@ -1222,7 +1109,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream) {
     if ((EPI != EPI_STORE && EPI != EPI_STORE3) || !a.part || a.N % 8 || (nsplit - 1) * kper >= nk)
       return hipErrorInvalidValue;
   }
-  gemm_bf16_kernel<EPI, SEGA><<<dim3(ntm * ntn * nsplit), dim3(256), 0, stream>>>(a);
+  gemm_bf16_kernel<EPI, SEGA, BSRC><<<dim3(ntm * ntn * nsplit), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   if (EPI == EPI_STORE || EPI == EPI_STORE3) {
@@ -1263,11 +1150,14 @@ static hipError_t launch_b(const GemmArgs& a, hipStream_t stream) {
     }
     return hipErrorInvalidValue;
   }
-  if (a.A1 || a.splits > 1) return hipErrorInvalidValue;
+  if (a.A1 || a.splits > 1 || !a.codes0 || !a.absmax0 || a.N % 64 || a.K % BK) return hipErrorInvalidValue;
+  if (BSRC == BSRC_NF4_PAIR && (!a.codes1 || !a.absmax1)) return hipErrorInvalidValue;
+  if (BSRC == BSRC_NF4_T && a.ksplit > 0 && (a.ksplit % BK || a.ksplit >= a.K || !a.codes1 || !a.absmax1))
+    return hipErrorInvalidValue;
   switch (a.epi) {
-    case EPI_STORE: return launch_t<BSRC, EPI_STORE>(a, stream);
-    case EPI_GATEUP: return launch_t<BSRC, EPI_GATEUP>(a, stream);
-    case EPI_ACT_BWD: return launch_t<BSRC, EPI_ACT_BWD>(a, stream);
+    case EPI_STORE: return launch_bf16<EPI_STORE, false, BSRC>(a, stream);
+    case EPI_GATEUP: return launch_bf16<EPI_GATEUP, false, BSRC>(a, stream);
+    case EPI_ACT_BWD: return launch_bf16<EPI_ACT_BWD, false, BSRC>(a, stream);
   }
   return hipErrorInvalidValue;
 }
