@@ -129,11 +129,11 @@ bool staged_like(int mode) { return mode == QLORA_DEQUANT_STAGED || mode == MODE
 
 // The MLP's two row products over h-wide activations (Ud = H Ad^T and
 // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu)) come from the epilogues of the
-// GEMMs that write those activations when the GEMM reads a bf16 weight,
-// r <= 16 and m <= 16384; otherwise a separate pass reads the activations
-// back. Measured on the Llama-7B MLP, the epilogue form gains 1.2% at 8192
-// tokens, breaks even at 16384 and loses 1-2% from 24576 tokens up.
-bool rp_epilogue(int mode, int64_t r, int64_t m) { return staged_like(mode) && r <= 16 && m <= 16384; }
+// GEMMs that write those activations (any weight source) when r <= 16 and
+// m <= 16384; otherwise a separate pass reads the activations back. Measured
+// on the Llama-7B MLP, the epilogue form gains 1.2% at 8192 tokens, breaks
+// even at 16384 and loses 1-2% from 24576 tokens up.
+bool rp_epilogue(int64_t r, int64_t m) { return r <= 16 && m <= 16384; }
 
 int resolve_mode(int mode) {
   if (mode == QLORA_DEQUANT_AUTO) return QLORA_DEQUANT_STAGED;
@@ -142,16 +142,15 @@ int resolve_mode(int mode) {
 
 bool valid_mode(int mode) { return mode >= QLORA_DEQUANT_AUTO && mode <= QLORA_DEQUANT_STAGED; }
 
-// Split-K partials of a store GEMM (M x N, depth K) on a bf16 B operand: the
-// launch gives a small output several K ranges when it has too few tiles to
-// fill the chip. Fused-dequant launches never split.
-int64_t splitk_elems(int64_t M, int64_t N, int64_t K, bool bf16_b) {
-  if (!bf16_b || M <= 0) return 0;
+// Split-K partials of a store GEMM (M x N, depth K): the launch gives a small
+// output several K ranges when it has too few tiles to fill the chip (bf16 or
+// NF4 B operand alike).
+int64_t splitk_elems(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0) return 0;
   const int sp = gemm_splits((int)M, (int)N, (int)K);
   return sp > 1 ? sp * M * N : 0;
 }
 void use_splitk(GemmArgs& g, float* part) {
-  if (g.bsrc != BSRC_BF16) return;
   const int sp = gemm_splits(g.M, g.N, g.K);
   if (sp > 1) { g.splits = sp; g.part = part; }
 }
@@ -173,7 +172,7 @@ size_t plan_linear_fwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.uext = c.take<uint16_t>(m * KE);
   t.wbf = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(n * k) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
-  t.kpart = c.take<float>(splitk_elems(m, n, k, staged_like(mode)));
+  t.kpart = c.take<float>(splitk_elems(m, n, k));
   t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? n * (k / 64) : 0);
   if (w) *w = t;
   return c.off;
@@ -202,7 +201,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.part = c.take<float>(chunks * std::max(n, k) * r);
   t.wt = staged_like(mode) ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
-  t.kpart = c.take<float>(splitk_elems(m, k, n, staged_like(mode)));
+  t.kpart = c.take<float>(splitk_elems(m, k, n));
   t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? n * (k / 64) : 0);
   if (w) *w = t;
   return c.off;
@@ -235,8 +234,8 @@ size_t plan_mlp_fwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.H = c.take<uint16_t>(m * h);
   t.wgu = staged_like(mode) ? c.take<uint16_t>(2 * h * d) : nullptr;
   t.wd = mode == QLORA_DEQUANT_STAGED ? c.take<uint16_t>(d * h) : nullptr;
-  t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
-  t.kpart = c.take<float>(splitk_elems(m, d, h, staged_like(mode)));
+  t.rpart = c.take<float>(std::max<int64_t>(16 * 2 * r, rp_epilogue(r, m) ? gemm_rowprod_splits((int)(2 * h)) * r : 0) * m);
+  t.kpart = c.take<float>(splitk_elems(m, d, h));
   t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? 3 * h * (d / 64) : 0);
   if (w) *w = t;
   return c.off;
@@ -276,8 +275,8 @@ size_t plan_mlp_bwd(Carver& c, int64_t m, int64_t d, int64_t h, int64_t r, int m
   t.part = c.take<float>(chunks * std::max(d, h) * 2 * r);
   t.wdt = staged_like(mode) ? c.take<uint16_t>(h * d) : nullptr;
   t.wgut = staged_like(mode) ? c.take<uint16_t>(d * 2 * h) : nullptr;
-  t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(mode, r, m) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
-  t.kpart = c.take<float>(splitk_elems(m, d, 2 * h, staged_like(mode)));
+  t.rpart = c.take<float>(std::max<int64_t>(16, rp_epilogue(r, m) ? gemm_rowprod_splits((int)h) : 0) * 2 * r * m);
+  t.kpart = c.take<float>(splitk_elems(m, d, 2 * h));
   t.amx = c.take<float>(mode == QLORA_DEQUANT_FUSED ? 3 * h * (d / 64) : 0);
   if (w) *w = t;
   return c.off;
@@ -870,7 +869,7 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
   g.M = (int)m; g.N = (int)(2 * h); g.K = (int)d; g.KE = KEgu;
   g.epi = EPI_GATEUP; g.g_out = g_save; g.u_out = u_save; g.h_out = t.H; g.hdim = h; g.act = w->act;
   // Ud = H Ad^T ; Y = H Wd^T + s Ud Bd^T
-  const bool rp = rp_epilogue(mode, r, m);
+  const bool rp = rp_epilogue(r, m);
   if (rp) { g.rp_l = w->a_down; g.rp_ldl = h; g.rp_r = (int)r; g.rp_part = t.rpart; }
   if (staged) QL_TRY(side.wait(1), "mlp_fwd: wait");
   QL_TRY(run_gemm(g, r, st), "mlp_fwd: gate/up GEMM");
@@ -1033,7 +1032,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
   g.M = (int)m; g.N = (int)h; g.K = (int)d; g.KE = KEd;
   g.epi = EPI_ACT_BWD; g.g_in = g_save; g.u_in = u_save; g.dgu = t.dgu; g.hdim = h; g.act = w->act;
   // [Tg | Tu] = [dg | du] blockdiag(Bg, Bu): in the epilogue, or below
-  const bool rp = rp_epilogue(mode, r, m);
+  const bool rp = rp_epilogue(r, m);
   if (rp) {
     g.rp_l = t.ltgu; g.rp_l2 = t.ltgu + r * 2 * h + h; g.rp_ldl = 2 * h;
     g.rp_r = (int)r; g.rp_part = t.rpart;
@@ -1236,7 +1235,7 @@ static size_t plan_qkv_fwd(Carver& c, int64_t m, int64_t d, int64_t nt, int64_t 
   t.uext = c.take<uint16_t>(m * KE);
   t.wcat = c.take<uint16_t>(nt * d);
   t.rpart = c.take<float>(16 * m * 3 * r);
-  t.kpart = c.take<float>(splitk_elems(m, nt, d, true));
+  t.kpart = c.take<float>(splitk_elems(m, nt, d));
   if (w) *w = t;
   return c.off;
 }
@@ -1266,7 +1265,7 @@ static size_t plan_qkv_bwd(Carver& c, int64_t m, int64_t d, const int64_t n[3], 
   t.part = c.take<float>(chunks * std::max(nmax * r, d * ra));
   t.wt = c.take<uint16_t>(d * nt);
   t.rpart = c.take<float>(16 * m * r);
-  t.kpart = c.take<float>(splitk_elems(m, d, nt, true));
+  t.kpart = c.take<float>(splitk_elems(m, d, nt));
   if (w) *w = t;
   return c.off;
 }

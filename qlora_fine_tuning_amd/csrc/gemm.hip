@@ -597,6 +597,18 @@ void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < 6; ++t) qtable_part(t, wq, D, P);
     };
+    // MFMA q of a substep: tile (q / 4, q % 4)
+    auto mma_ab = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], int q) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q >> 2], fb[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+    };
+    // fragment tile idx of A (idx 0-3) or of row-major B (idx 4-7), substep ks of step st
+    auto frag1 = [&](Frag& f, int st, int ks, int idx) {
+      if (idx < 4) f.a[idx] = *(const bf16x8_t*)(slot(2 * st) + fq + idx * 256 + fpos(ks));
+      else f.b[idx - 4] = *(const bf16x8_t*)(slot(2 * st + 1) + gq + (idx - 4) * 256 + fpos(ks));
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    if constexpr (!NT) {
     // Prologue, branch-free: the loads of steps 1 and 2 are issued even when
     // the job has fewer steps (they then read rows past the end, or zeros,
     // into slots nothing reads), so every path reaches the loop with the
@@ -623,16 +635,6 @@ void gemm_bf16_kernel(GemmArgs p) {
     ring_barrier();
     Frag f0, f1;
     load_frag(f0, 0, 0);
-    // one fragment register (0-3: A tiles, 4-7: B tiles) of substep ks of step st
-    auto frag1 = [&](Frag& f, int st, int ks, int idx) {
-      if (idx < 4) f.a[idx] = *(const bf16x8_t*)(slot(2 * st) + fq + idx * 256 + fpos(ks));
-      else if constexpr (NT) f.b[idx - 4] = trb(slot(2 * st + 1), ks, idx - 4);
-      else f.b[idx - 4] = *(const bf16x8_t*)(slot(2 * st + 1) + gq + (idx - 4) * 256 + fpos(ks));
-    };
-    // MFMA q of a substep: tile (q / 4, q % 4)
-    auto mma1 = [&](const Frag& f, int q) {
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
-    };
     // Step st, with the order of its instructions fixed: each MFMA is followed
     // by its share of the other work. Substeps 0-2 dequantize B of step st+1
     // (its NPART parts over their 48 MFMAs) into the slot of A of step st-1,
@@ -652,7 +654,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         Frag& nxt = (ss & 1) ? f0 : f1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          mma1(cur, i);
+          mma_ab(cur.a, cur.b, i);
           __builtin_amdgcn_sched_barrier(0);
           if (i < 8) frag1(nxt, st, ss + 1, i);
           if (b2 && ss < 2 && i >= 8 && i < 12) issue_half(2 * st + 4, 4 * ss + i - 8);
@@ -671,7 +673,7 @@ void gemm_bf16_kernel(GemmArgs p) {
       ring_barrier();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        mma1(f1, i);
+        mma_ab(f1.a, f1.b, i);
         __builtin_amdgcn_sched_barrier(0);
         if (b1 && i < 8) frag1(f0, st + 1, 0, i);
         if (b2) {
@@ -681,13 +683,102 @@ void gemm_bf16_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    using T_ = std::integral_constant<bool, true>;
-    using F_ = std::integral_constant<bool, false>;
     int st = 0;
     for (; st < ns - 3; ++st) stepq(st, T_(), T_(), T_());
     if (ns >= 3) stepq(st++, T_(), T_(), F_());
     if (ns >= 2) stepq(st++, T_(), F_(), F_());
     stepq(st, F_(), F_(), F_());
+    } else {
+    // Transposed B. The compiler waits for every LDS-DMA load in flight before
+    // an LDS transpose read (it cannot tell which LDS bytes they write), so
+    // all of a step's B fragments (16 tiles, 32 transpose reads) are read in
+    // the fourth substep of the step before, right after its barrier, when no
+    // DMA is in flight; A of step s+2 is loaded after them, at the end of
+    // that substep, and waited for at the end of step s+1. The codes of step
+    // s+3 are issued at its start, ahead of that A.
+    bf16x8_t tb[4][4];      // B fragments of the current step [substep][tile]
+    bf16x8_t fa0[4], fa1[4];
+    auto afrag = [&](bf16x8_t (&fa)[4], int st, int ks, int mt) {
+      fa[mt] = *(const bf16x8_t*)(slot(2 * st) + fq + mt * 256 + fpos(ks));
+    };
+    // prologue (branch-free, as row-major): A of steps 0, 1 and the codes of
+    // step 0; B of step 0 dequantized; its fragments read; the codes of step
+    // 1 taken, those of step 2 issued; A of step 2 issued.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_half(0, j);
+    issue_q(kt0, cq);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_half(2, j);
+    wait_vm<0>();
+    take_q(kt0 + 1, std::true_type());
+    table_all();
+    {
+      QStep S0;
+#pragma unroll
+      for (int pp = 0; pp < NPART; ++pp) qpart(S0, pp, wq, P, bslot(0));
+    }
+    wait_vm<NQ>();
+    ring_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) tb[ks][nt] = trb(bslot(0), ks, nt);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) afrag(fa0, 0, 0, mt);
+    take_q(kt0 + 2, std::true_type());
+    table_all();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_half(4, j);
+    auto stepq_t = [&](int st, auto b1_c, auto b2_c, auto c3_c) {
+      constexpr bool b1 = decltype(b1_c)::value, b2 = decltype(b2_c)::value;
+      uint8_t* sb = bslot(st + 1);
+      QStep S;
+#pragma unroll
+      for (int ss = 0; ss < 3; ++ss) {
+        bf16x8_t (&cur)[4] = (ss & 1) ? fa1 : fa0;
+        bf16x8_t (&nxt)[4] = (ss & 1) ? fa0 : fa1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          mma_ab(cur, tb[ss], i);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < 4) afrag(nxt, st, ss + 1, i);
+          if (b1) {
+            const int sl = 16 * ss + i;
+#pragma unroll
+            for (int pp = 0; pp < NPART; ++pp)
+              if ((pp * 48) / NPART == sl) qpart(S, pp, wq, P, sb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (b1) wait_vm<0>();   // A of step st+1 (the codes of step st+2, older, too)
+      ring_barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mma_ab(fa1, tb[3], i);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b1) {
+          if (b2 && i == 0) take_q(kt0 + st + 3, c3_c);
+          // fragments of step st+1: tiles of substeps 0-2 two reads per MFMA,
+          // those of substep 3 each after the last MFMA that reads its register
+          if (i < 12) tb[i >> 2][i & 3] = trb(sb, i >> 2, i & 3);
+          else tb[3][i - 12] = trb(sb, 3, i - 12);
+          if (i < 4) afrag(fa0, st + 1, 0, i);
+          if (b2 && i >= 1 && i < 7) qtable_part(i - 1, wq, D, P);
+        }
+        if (b2 && i == 15) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) issue_half(2 * st + 4, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    int st = 0;
+    for (; st < ns - 3; ++st) stepq_t(st, T_(), T_(), T_());
+    if (ns >= 3) stepq_t(st++, T_(), T_(), F_());
+    if (ns >= 2) stepq_t(st++, T_(), F_(), F_());
+    stepq_t(st, F_(), F_(), F_());
+    }
   } else {
   for (int i = 0; i < 4 && i < nh; ++i) {
 #pragma unroll
@@ -1150,7 +1241,7 @@ static hipError_t launch_b(const GemmArgs& a, hipStream_t stream) {
     }
     return hipErrorInvalidValue;
   }
-  if (a.A1 || a.splits > 1 || !a.codes0 || !a.absmax0 || a.N % 64 || a.K % BK) return hipErrorInvalidValue;
+  if (a.A1 || !a.codes0 || !a.absmax0 || a.N % 64 || a.K % BK) return hipErrorInvalidValue;
   if (BSRC == BSRC_NF4_PAIR && (!a.codes1 || !a.absmax1)) return hipErrorInvalidValue;
   if (BSRC == BSRC_NF4_T && a.ksplit > 0 && (a.ksplit % BK || a.ksplit >= a.K || !a.codes1 || !a.absmax1))
     return hipErrorInvalidValue;

@@ -97,7 +97,7 @@ struct GemmArgs {
   const uint16_t* Be;
   int64_t ldbe;
   int M, N, K, KE;
-  // split-K (EPI_STORE / EPI_STORE3, bf16 B source): splits > 1 runs each
+  // split-K (EPI_STORE / EPI_STORE3): splits > 1 runs each
   // tile as `splits` K ranges writing fp32 partials part [splits][M][N], then a
   // reduction sums them in order and stores; the K-extension rides on split 0
   int splits;
