@@ -274,7 +274,9 @@ void gemm_bf16_kernel(GemmArgs p) {
   constexpr bool NF4 = BSRC != BSRC_BF16;
   constexpr bool NT = BSRC == BSRC_NF4_T;
   constexpr int NQ = NT ? 3 : 5;      // loads per thread per step
-  constexpr int NPART = NT ? 44 : 40; // dequant parts per step
+  constexpr int NPART = 56;           // dequant parts per step
+  constexpr int NPRE = 8;             // of them done in the fourth substep of the step before
+  static_assert(NPART - NPRE == 48, "one dequant part per MFMA of substeps 0-2");
   struct QRegs {
     uint32_t c[8];
     float a[1];
@@ -395,62 +397,78 @@ void gemm_bf16_kernel(GemmArgs p) {
       }
     }
   };
-  // A step's dequant in NPART parts, which the main loop places one per MFMA.
-  // Code dword c holds elements 8 c .. 8 c + 7 of the thread's block (element
-  // 2 m in the high nibble of byte m). Per dword: part 0 the selectors, 1 the
-  // low-byte lookups, 2 the high-byte lookups; row-major then 3 the
-  // interleave into bf16 pairs and 4 the store (chunk = dword); transposed
-  // 3 the pairs (element y, element y + 2) of the dword, then 4 parts
-  // joining dwords 2 q, 2 q + 1 into the pairs of the stores, then the 8
-  // stores (store y: elements 8 x + y).
+  // A step's dequant in NPART parts of about 4 VALU instructions each, which
+  // the main loop places one per MFMA. Code dword c holds elements 8 c ..
+  // 8 c + 7 of the thread's block (element 2 m in the high nibble of byte m).
+  // Per dword: part 0 the lookup selectors, 1 the merge selectors, 2 the
+  // low-byte lookups, 3 the high-byte lookups; row-major then 4-5 the
+  // interleave into bf16 pairs and 6 the store (chunk = dword); transposed 4
+  // the pairs (element y, element y + 2) of the dword, then (per two dwords
+  // 2 q, 2 q + 1) two parts forming word q of the 8 stores, and after all
+  // dwords the 8 stores (store y: elements 8 x + y).
   struct QStep {
     uint32_t s0[8], s1[8], m0[8], m1[8], a0[8], a1[8], b0[8], b1[8];
     uint32_t ev[8][4];
     u32x4_t o[8];
   };
   auto qpart = [&](QStep& S, int pp, const QRegs& r, const uint32_t (&P)[8], uint8_t* sbase) {
-    const int c = NT ? (pp < 32 ? pp >> 2 : 0) : pp / 5, part = NT ? (pp < 32 ? pp & 3 : 5) : pp % 5;
-    if (part == 0) {
+    // decode part pp into (kind, dword c / store y / pair q)
+    int kind, c = 0;
+    if constexpr (!NT) {
+      c = pp / 7;
+      kind = pp % 7;
+    } else if (pp < 48) {
+      const int q = pp / 12, rr = pp % 12;
+      if (rr < 10) { c = 2 * q + rr / 5; kind = rr % 5; }
+      else { c = q; kind = 8 + (rr - 10); }   // pair q, half 0 / 1
+    } else {
+      c = pp - 48;
+      kind = 10;                               // store y = c
+    }
+    if (kind == 0) {
       const uint32_t d = r.c[c];
       S.s0[c] = d & 0x07070707u;                          // low nibbles: elements 1, 3, 5, 7
       S.s1[c] = (d >> 4) & 0x07070707u;                   // high nibbles: elements 0, 2, 4, 6
+    } else if (kind == 1) {
+      const uint32_t d = r.c[c];
       S.m0[c] = ((d >> 1) & 0x04040404u) | 0x03020100u;
       S.m1[c] = ((d >> 5) & 0x04040404u) | 0x03020100u;
-    } else if (part == 1) {
+    } else if (kind == 2) {
       S.a0[c] = qlook(P, S.s0[c], S.m0[c]);
       S.a1[c] = qlook(P, S.s1[c], S.m1[c]);
-    } else if (part == 2) {
+    } else if (kind == 3) {
       S.b0[c] = qlook(P + 4, S.s0[c], S.m0[c]);
       S.b1[c] = qlook(P + 4, S.s1[c], S.m1[c]);
-    } else if (!NT && part == 3) {
-      const uint32_t u0 = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x05010400u);
-      const uint32_t v0 = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x05010400u);
-      const uint32_t u1 = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x07030602u);
-      const uint32_t v1 = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x07030602u);
-      S.o[c][0] = __builtin_amdgcn_perm(v0, u0, 0x05010400u);
-      S.o[c][1] = __builtin_amdgcn_perm(v0, u0, 0x07030602u);
-      S.o[c][2] = __builtin_amdgcn_perm(v1, u1, 0x05010400u);
-      S.o[c][3] = __builtin_amdgcn_perm(v1, u1, 0x07030602u);
-    } else if (!NT && part == 4) {
+    } else if (!NT && kind == 4) {
+      S.ev[c][0] = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x05010400u);
+      S.ev[c][1] = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x05010400u);
+      S.ev[c][2] = __builtin_amdgcn_perm(S.a0[c], S.a1[c], 0x07030602u);
+      S.ev[c][3] = __builtin_amdgcn_perm(S.b0[c], S.b1[c], 0x07030602u);
+    } else if (!NT && kind == 5) {
+      S.o[c][0] = __builtin_amdgcn_perm(S.ev[c][1], S.ev[c][0], 0x05010400u);
+      S.o[c][1] = __builtin_amdgcn_perm(S.ev[c][1], S.ev[c][0], 0x07030602u);
+      S.o[c][2] = __builtin_amdgcn_perm(S.ev[c][3], S.ev[c][2], 0x05010400u);
+      S.o[c][3] = __builtin_amdgcn_perm(S.ev[c][3], S.ev[c][2], 0x07030602u);
+    } else if (!NT && kind == 6) {
       lds_store16(sbase + woff[c], S.o[c]);
-    } else if (NT && part == 3) {
+    } else if (NT && kind == 4) {
       // bf16 pairs of one dword: elements (0, 2), (4, 6), (1, 3), (5, 7)
       S.ev[c][0] = __builtin_amdgcn_perm(S.b1[c], S.a1[c], 0x05010400u);
       S.ev[c][1] = __builtin_amdgcn_perm(S.b1[c], S.a1[c], 0x07030602u);
       S.ev[c][2] = __builtin_amdgcn_perm(S.b0[c], S.a0[c], 0x05010400u);
       S.ev[c][3] = __builtin_amdgcn_perm(S.b0[c], S.a0[c], 0x07030602u);
-    } else if (NT && pp < 36) {
-      // dwords 2 q, 2 q + 1 -> word q of store y: (element y of 2 q, of 2 q + 1)
-      const int q = pp - 32;
+    } else if (NT && kind < 10) {
+      // dwords 2 q, 2 q + 1 -> word q of stores y (half 0: y = 0..3, 1: 4..7):
+      // (element y of 2 q, element y of 2 q + 1)
+      const int q = c;
 #pragma unroll
-      for (int y = 0; y < 8; ++y) {
+      for (int y = 4 * (kind - 8); y < 4 * (kind - 8) + 4; ++y) {
         const int src = (y & 1) ? 2 + ((y >> 2) & 1) : ((y >> 2) & 1);   // ev index
         const uint32_t sel = ((y >> 1) & 1) ? 0x07060302u : 0x05040100u;
         S.o[y][q] = __builtin_amdgcn_perm(S.ev[2 * q + 1][src], S.ev[2 * q][src], sel);
       }
     } else if (NT) {
-      const int y = pp - 36;
-      lds_store16(sbase + woff[y], S.o[y]);
+      lds_store16(sbase + woff[c], S.o[c]);
     }
   };
   // DMA: wave w, load j (0..7) fills block q = 8w + j; lane l writes position
@@ -631,23 +649,26 @@ void gemm_bf16_kernel(GemmArgs p) {
     wait_vmem<4>();   // codes of step 1 (A[4-7] of step 1 behind them)
     take_q(kt0 + 2, std::true_type());
     table_all();
+    QStep S;   // the dequant state of the B half-stage in progress, across steps
+#pragma unroll
+    for (int pp = 0; pp < NPRE; ++pp) qpart(S, pp, wq, P, bslot(1));
     wait_vm<4 + NQ>();
     ring_barrier();
     Frag f0, f1;
     load_frag(f0, 0, 0);
     // Step st, with the order of its instructions fixed: each MFMA is followed
-    // by its share of the other work. Substeps 0-2 dequantize B of step st+1
-    // (its NPART parts over their 48 MFMAs) into the slot of A of step st-1,
+    // by its share of the other work. Substeps 0-2 finish B of step st+1 (its
+    // last NPART - NPRE parts, one per MFMA) in the slot of A of step st-1,
     // read the next substep's fragments (one after each of the first 8 MFMAs)
     // and load A of step st+2 (substeps 0-1, after MFMAs 8-11). Substep 3
     // (after the barrier) takes the codes of step st+2, issues those of step
-    // st+3 and forms the table for B of step st+2.
+    // st+3, forms the table for B of step st+2 and does that B's first NPRE
+    // parts (its slot, that of A of step st, is free from the barrier on).
     // b1: B of step st+1 to write (st+1 < ns); b2: codes of step st+2 to take
     // and A of step st+2 to load (st+2 < ns); c3: codes of step st+3 to load.
     auto stepq = [&](int st, auto b1_c, auto b2_c, auto c3_c) {
       constexpr bool b1 = decltype(b1_c)::value, b2 = decltype(b2_c)::value;
       uint8_t* sb = bslot(st + 1);
-      QStep S;
 #pragma unroll
       for (int ss = 0; ss < 3; ++ss) {
         Frag& cur = (ss & 1) ? f1 : f0;
@@ -658,12 +679,7 @@ void gemm_bf16_kernel(GemmArgs p) {
           __builtin_amdgcn_sched_barrier(0);
           if (i < 8) frag1(nxt, st, ss + 1, i);
           if (b2 && ss < 2 && i >= 8 && i < 12) issue_half(2 * st + 4, 4 * ss + i - 8);
-          if (b1) {
-            const int sl = 16 * ss + i;
-#pragma unroll
-            for (int pp = 0; pp < NPART; ++pp)
-              if ((pp * 48) / NPART == sl) qpart(S, pp, wq, P, sb);
-          }
+          if (b1) qpart(S, NPRE + 16 * ss + i, wq, P, sb);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -679,6 +695,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         if (b2) {
           if (i == 1) take_q(kt0 + st + 3, c3_c);
           if (i >= 2 && i < 8) qtable_part(i - 2, wq, D, P);
+          if (i >= 8) qpart(S, i - 8, wq, P, bslot(st + 2));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -727,12 +744,14 @@ void gemm_bf16_kernel(GemmArgs p) {
     for (int mt = 0; mt < 4; ++mt) afrag(fa0, 0, 0, mt);
     take_q(kt0 + 2, std::true_type());
     table_all();
+    QStep S;   // the dequant state of the B half-stage in progress, across steps
+#pragma unroll
+    for (int pp = 0; pp < NPRE; ++pp) qpart(S, pp, wq, P, bslot(1));
 #pragma unroll
     for (int j = 0; j < 8; ++j) issue_half(4, j);
     auto stepq_t = [&](int st, auto b1_c, auto b2_c, auto c3_c) {
       constexpr bool b1 = decltype(b1_c)::value, b2 = decltype(b2_c)::value;
       uint8_t* sb = bslot(st + 1);
-      QStep S;
 #pragma unroll
       for (int ss = 0; ss < 3; ++ss) {
         bf16x8_t (&cur)[4] = (ss & 1) ? fa1 : fa0;
@@ -742,12 +761,7 @@ void gemm_bf16_kernel(GemmArgs p) {
           mma_ab(cur, tb[ss], i);
           __builtin_amdgcn_sched_barrier(0);
           if (i < 4) afrag(nxt, st, ss + 1, i);
-          if (b1) {
-            const int sl = 16 * ss + i;
-#pragma unroll
-            for (int pp = 0; pp < NPART; ++pp)
-              if ((pp * 48) / NPART == sl) qpart(S, pp, wq, P, sb);
-          }
+          if (b1) qpart(S, NPRE + 16 * ss + i, wq, P, sb);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -765,6 +779,7 @@ void gemm_bf16_kernel(GemmArgs p) {
           else tb[3][i - 12] = trb(sb, 3, i - 12);
           if (i < 4) afrag(fa0, st + 1, 0, i);
           if (b2 && i >= 1 && i < 7) qtable_part(i - 1, wq, D, P);
+          if (b2 && i >= 8) qpart(S, i - 8, wq, P, bslot(st + 2));
         }
         if (b2 && i == 15) {
 #pragma unroll
