@@ -85,6 +85,11 @@ __global__ __launch_bounds__(256) void nf4_dequant_rows_kernel(
 // weight rows x 128 input features: the 4 KB of codes go through LDS, then
 // thread t dequantizes 8 weight rows x 4 features and writes 4 output rows
 // of 8 consecutive values; 8 lanes cover one 128-byte output row segment.
+// Blocks of neighbouring features share the 128-byte lines of their codes
+// (2 blocks) and absmax (16 blocks). Consecutive block ids are dealt to the 8
+// XCDs in turn, each with its own L2, so the ids are remapped to give each
+// XCD a contiguous range of blocks, feature-major within a row band: a line
+// is then fetched by one L2 (not by several).
 __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
     const uint8_t* __restrict__ codes, const AbsmaxSrc absmax, int64_t n, int64_t k,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t col_ofs) {
@@ -93,7 +98,11 @@ __global__ __launch_bounds__(256) void nf4_dequant_transpose_kernel(
   __shared__ float at[64][2];
   const int tid = threadIdx.x;
   if (tid < 16) lut[tid] = __uint_as_float(c_nf4_levels[tid]);
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 128;
+  const int gx = (int)((k + 127) / 128), total = gx * (int)(n / 64);
+  const int bid = (int)blockIdx.x;
+  const int per = total / 8, rmd = total % 8, xcd = bid % 8, local = bid / 8;
+  const int job = (xcd < rmd ? xcd * (per + 1) : rmd * (per + 1) + (xcd - rmd) * per) + local;
+  const int64_t n0 = (int64_t)(job / gx) * 64, k0 = (int64_t)(job % gx) * 128;
   const int kvalid = (int)min((int64_t)128, k - k0);   // 64 or 128 (k is a multiple of 64)
   {
     const int r = tid >> 2, c = (tid & 3) * 16;   // 64 rows x 64 code bytes
@@ -258,9 +267,10 @@ hipError_t launch_nf4_dequant_transpose(const uint8_t* codes, AbsmaxSrc absmax, 
                                         int64_t k, uint16_t* out, int64_t ld_out, int64_t col_ofs,
                                         hipStream_t stream) {
   if (n == 0 || k == 0) return hipSuccess;
-  dim3 grid((unsigned)((k + 127) / 128), (unsigned)(n / 64));
-  nf4_dequant_transpose_kernel<<<grid, dim3(256), 0, stream>>>(codes, absmax, n, k, out, ld_out,
-                                                              col_ofs);
+  const int64_t blocks = ((k + 127) / 128) * (n / 64);
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  nf4_dequant_transpose_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      codes, absmax, n, k, out, ld_out, col_ofs);
   return hipGetLastError();
 }
 
