@@ -891,6 +891,30 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
   }
 
+  // ACT_BWD: g and u of one epilogue slab, fetched a slab ahead (the first
+  // before the K-extension) so that their latency overlaps other work. Lane:
+  // 8 consecutive columns of staged rows q * 4 + lane / 16, i.e. tile rows
+  // wm*128 + 8*((lane/16) >> 1) + 2*mt + ((lane/16) & 1) + 16 q; rows past M
+  // and columns past N read nothing (zeros).
+  u32x4_t gw[8], uw[8];
+  auto fetch_gu = [&](int mt) {
+    const int sl = lane >> 4;
+    const int row0 = m0 + wm * 128 + 8 * (sl >> 1) + 2 * mt + (sl & 1);
+    const int col = n0 + wn * 128 + (lane & 15) * 8;
+    const int64_t o0 = (int64_t)row0 * p.hdim + col;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      gw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      uw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (row0 + 16 * q < p.M && col < p.N) {
+        const int64_t o = o0 + (int64_t)(16 * q) * p.hdim;
+        gw[q] = *(const u32x4_t*)(p.g_in + o);
+        uw[q] = *(const u32x4_t*)(p.u_in + o);
+      }
+    }
+  };
+  if (EPI == EPI_ACT_BWD) fetch_gu(0);
+
   // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be in
   // slots 0 and 1, same layout; columns at or past KE read as zeros; split 0
   // only ----
@@ -1011,23 +1035,6 @@ void gemm_bf16_kernel(GemmArgs p) {
     constexpr int mt = decltype(mt_c)::value;
     constexpr int ACT = decltype(act_c)::value;
     auto grow = [&](int s) { return m0 + wm * 128 + 8 * (s >> 1) + 2 * mt + (s & 1); };
-    // ACT_BWD: fetch this slab's g and u first so that their latency overlaps
-    // the staging (rows past M read nothing)
-    u32x4_t gw[8], uw[8];
-    if (EPI == EPI_ACT_BWD) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        // staged row q * 4 + lane / 16 is tile row grow(lane / 16) + 16 q
-        const int row = grow(lane >> 4) + 16 * q, col = col0 + (lane & 15) * 8;
-        gw[q] = u32x4_t{0u, 0u, 0u, 0u};
-        uw[q] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < p.M && col < p.N) {
-          const int64_t o = (int64_t)grow(lane >> 4) * p.hdim + col + (int64_t)(16 * q) * p.hdim;
-          gw[q] = *(const u32x4_t*)(p.g_in + o);
-          uw[q] = *(const u32x4_t*)(p.u_in + o);
-        }
-      }
-    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
@@ -1050,26 +1057,24 @@ void gemm_bf16_kernel(GemmArgs p) {
       const int64_t coff0 = (int64_t)row0 * cld + ccol;
       const int64_t poff0 = ((int64_t)ksp * p.M + row0) * p.N + col;
       const int64_t doff0 = (int64_t)row0 * (2 * p.hdim) + col;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      const bool colok = col < p.N;
+      // one output row segment from its staged values x0 | x1
+      auto emit = [&](int q, const f32x4_t x0, const f32x4_t x1, auto split_c) {
+        constexpr bool SPLIT = decltype(split_c)::value;
         const int s = q * 4 + (lane >> 4);
         const int row = row0 + 16 * q;
         u32x4_t odg = u32x4_t{0u, 0u, 0u, 0u}, odu = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < p.M && col < p.N) {
-          const float* x = &stage[s * SP + cc];
-          if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1) {   // fp32 partial
+        if (row < p.M && colok) {
+          if ((EPI == EPI_STORE || EPI == EPI_STORE3) && SPLIT) {   // fp32 partial
             float* o = p.part + poff0 + (int64_t)(16 * q) * p.N;
-            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             *(f32x4_t*)o = f32x4_t{x0[0], x1[0], x0[1], x1[1]};
             *(f32x4_t*)(o + 4) = f32x4_t{x0[2], x1[2], x0[3], x1[3]};
           } else if (EPI == EPI_STORE || EPI == EPI_STORE3) {
-            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
             u32x4_t o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x0[e], x1[e]);
             *(u32x4_t*)(cbase + coff0 + (int64_t)(16 * q) * cld) = o;
           } else {  // staged values are dH
-            const f32x4_t x0 = *(const f32x4_t*)x, x1 = *(const f32x4_t*)(x + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float dg[2], du[2];
@@ -1096,7 +1101,31 @@ void gemm_bf16_kernel(GemmArgs p) {
           *(u32x4_t*)pr = odg;
           *(u32x4_t*)(pr + 128) = odu;
         }
-      }
+      };
+      // the staged values of QG rows are read before any of them is used, so
+      // that the LDS latency is waited for once per group instead of per row
+      // (a row's row-product bf16 overwrite comes after its group's reads)
+      auto rows = [&](auto split_c) {
+        constexpr int QG = EPI == EPI_ACT_BWD ? 4 : 8;
+#pragma unroll
+        for (int qg = 0; qg < 8; qg += QG) {
+          f32x4_t xs[QG][2];
+#pragma unroll
+          for (int i = 0; i < QG; ++i) {
+            const float* x = &stage[((qg + i) * 4 + (lane >> 4)) * SP + cc];
+            xs[i][0] = *(const f32x4_t*)x;
+            xs[i][1] = *(const f32x4_t*)(x + 4);
+          }
+#pragma unroll
+          for (int i = 0; i < QG; ++i) emit(qg + i, xs[i][0], xs[i][1], split_c);
+        }
+      };
+      if ((EPI == EPI_STORE || EPI == EPI_STORE3) && nsplit > 1)
+        rows(std::integral_constant<bool, true>());
+      else
+        rows(std::integral_constant<bool, false>());
+      // the next slab's g and u: this slab's are consumed
+      if constexpr (EPI == EPI_ACT_BWD && mt < 3) fetch_gu(mt + 1);
       if (EPI == EPI_ACT_BWD && rp_on) {
         wave_sync();
         const uint16_t* pan = reinterpret_cast<const uint16_t*>(stage);
@@ -1113,16 +1142,25 @@ void gemm_bf16_kernel(GemmArgs p) {
       // staged row q * 8 + lane / 8 is tile row row0 + 32 q
       const int row0 = grow(lane >> 3);
       const int64_t hoff0 = (int64_t)row0 * p.hdim + j;
+      // all four rows' staged values first: one LDS wait for the slab (a
+      // row's H overwrite comes after every read)
+      f32x4_t gx[4][2], ux[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* gs = &stage[(q * 8 + (lane >> 3)) * SP + gcol];
+        gx[q][0] = *(const f32x4_t*)gs;
+        gx[q][1] = *(const f32x4_t*)(gs + 4);
+        ux[q][0] = *(const f32x4_t*)(gs + 32);
+        ux[q][1] = *(const f32x4_t*)(gs + 36);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int s = q * 8 + (lane >> 3);
         const int row = row0 + 32 * q;
         u32x4_t oh = u32x4_t{0u, 0u, 0u, 0u};
         if (row < p.M && col0 < p.N) {
-          const float* gs = &stage[s * SP + gcol];
-          const float* us = gs + 32;
-          const f32x4_t g0 = *(const f32x4_t*)gs, g1 = *(const f32x4_t*)(gs + 4);
-          const f32x4_t u0 = *(const f32x4_t*)us, u1 = *(const f32x4_t*)(us + 4);
+          const f32x4_t g0 = gx[q][0], g1 = gx[q][1];
+          const f32x4_t u0 = ux[q][0], u1 = ux[q][1];
           float gv[8], uv[8];   // tile order
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
