@@ -580,6 +580,75 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
   };
 
+  const bool rp_on = (EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.rp_r > 0;
+  // ACT_BWD: g and u of one epilogue slab, fetched a slab ahead (the first
+  // before the K-extension) so that their latency overlaps other work. Lane:
+  // 8 consecutive columns of staged rows q * 4 + lane / 16, i.e. tile rows
+  // wm*128 + 8*((lane/16) >> 1) + 2*mt + ((lane/16) & 1) + 16 q; rows past M
+  // and columns past N read nothing (zeros).
+  u32x4_t gw[8], uw[8];
+  auto fetch_gu = [&](int mt) {
+    const int sl = lane >> 4;
+    const int row0 = m0 + wm * 128 + 8 * (sl >> 1) + 2 * mt + (sl & 1);
+    const int col = n0 + wn * 128 + (lane & 15) * 8;
+    const int64_t o0 = (int64_t)row0 * p.hdim + col;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      gw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      uw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (row0 + 16 * q < p.M && col < p.N) {
+        const int64_t o = o0 + (int64_t)(16 * q) * p.hdim;
+        gw[q] = *(const u32x4_t*)(p.g_in + o);
+        uw[q] = *(const u32x4_t*)(p.u_in + o);
+      }
+    }
+  };
+  // GATEUP row product: the rank-r fragments of the wave's 64 H columns
+  // (registers), waited for before the epilogue: waited for behind its
+  // conditional stores, they would cost a wait for all of those.
+  bf16x8_t rpb[2];
+  auto load_rpb = [&]() {
+    const int jr = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int64_t c = (int64_t)((n0 + wn * 128) >> 1) + 32 * kc + 8 * kq;
+      rpb[kc] = bf16x8_t{};
+      if (jr < p.rp_r && c < p.hdim) rpb[kc] = *(const bf16x8_t*)(p.rp_l + (int64_t)jr * p.rp_ldl + c);
+    }
+  };
+  // ACT_BWD row product: the rank-r operand over the tile's 256 columns
+  // (gate rows 0-15, then up rows 16-31: 32 x 256 bf16) is brought by DMA
+  // into the end of ring slot 4, which the epilogue's staging leaves alone;
+  // the epilogue reads it from LDS. Row i keeps logical 16-byte chunk c at
+  // physical chunk c ^ (i & 15) of its 512 bytes: the 16 rows of a fragment
+  // read hit 16 different bank groups. Rows j >= rp_r and columns at or past
+  // hdim load as zeros.
+  constexpr int RPL_OFF = 5 * G_SLOT - 16384;
+  auto issue_rpl = [&]() {
+    const int up = wave >= 2;   // waves 0, 1: gate rows; 2, 3: up rows
+    const uint64_t base = (uint64_t)(up ? p.rp_l2 : p.rp_l);
+    const int nrec = rec_bytes(p.rp_r, p.rp_ldl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int inst = 4 * wave + q;
+      const int i = 2 * inst + (lane >> 5), j = i & 15;
+      const int c = (lane & 31) ^ j;
+      const int64_t col = n0 + 8 * c;
+      const bool in = j < p.rp_r && col < p.hdim;
+      bload_lds<16>(base, nrec, smem + RPL_OFF + inst * 1024,
+                    in ? (uint32_t)((int64_t)j * p.rp_ldl + col) * 2u : OOB, 0);
+    }
+  };
+  // The bf16 B path loads the tile's tail operands beside its last step's
+  // MFMAs, when ring slots f, f+1, f+2 (mod 5, f = 2 ns for ns steps) are
+  // free (the last step reads the other two): the K-extension's first step
+  // goes to slots ka, kb, ACT_BWD's rank-r operand to slot 4 if that is free
+  // and not one of them, the row-product operands and g/u to registers.
+  constexpr bool tail_pre = !NF4;
+  const int tail_f = tail_pre ? (2 * (kt1 - kt0)) % 5 : 0;
+  const bool rpl_pre = tail_pre && EPI == EPI_ACT_BWD && rp_on && tail_f >= 2;
+  const int ka = rpl_pre && tail_f == 4 ? 1 : tail_f;
+  const int kb = rpl_pre && tail_f == 3 ? 0 : (tail_f + 1) % 5;
   // ---- main loop ----
   // Step s frees the slots of step s-1, so it issues H_2s+3 (B of step s+1,
   // for s >= 1: the prologue has B of step 1) over its first two substeps and
@@ -837,105 +906,73 @@ void gemm_bf16_kernel(GemmArgs p) {
     interleave(8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // the tile's tail operands, beside the last step's MFMAs
+  auto tail = [&]() {
+    if (p.KE > 0 && ksp == 0) {   // the K-extension's first step, as the K-extension loop lays it out
+      const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
+      const int neA = rec_bytes(rowsA, p.ldae);
+      const int neB = rec_bytes(rowsB, p.ldbe);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = drow(j), c = dcol(j);
+        const bool in = c < p.KE;
+        bload_lds<16>(eA, neA, slot(ka) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
+        bload_lds<16>(eB, neB, slot(kb) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
+      }
+    }
+    if (rpl_pre) issue_rpl();
+    if (EPI == EPI_GATEUP && rp_on) load_rpb();
+    if (EPI == EPI_ACT_BWD) fetch_gu(0);
+  };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   if (ns >= 3) {
     step(0, F_(), T_());
     for (int st = 1; st < ns - 2; ++st) step(st, T_(), T_());
     step(ns - 2, T_(), F_());
+    tail();
     step(ns - 1, F_(), F_());
+  } else if (ns == 2) {
+    step(0, F_(), F_());
+    tail();
+    step(1, F_(), F_());
   } else {
-    for (int st = 0; st < ns; ++st) step(st, F_(), F_());
+    tail();
+    step(0, F_(), F_());
   }
   }   // bf16 B
-  // GATEUP row product: the rank-r fragments of the wave's 64 H columns,
-  // loaded here so that the wait below covers them. Waited for later, behind
-  // the epilogue's conditional stores, they would cost a wait for all of those.
-  const bool rp_on = (EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.rp_r > 0;
-  bf16x8_t rpb[2];
-  if (EPI == EPI_GATEUP && rp_on) {
-    const int jr = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int64_t c = (int64_t)((n0 + wn * 128) >> 1) + 32 * kc + 8 * kq;
-      rpb[kc] = bf16x8_t{};
-      if (jr < p.rp_r && c < p.hdim) rpb[kc] = *(const bf16x8_t*)(p.rp_l + (int64_t)jr * p.rp_ldl + c);
-    }
-  }
+  if (!tail_pre && EPI == EPI_GATEUP && rp_on) load_rpb();
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   __syncthreads();
 
-  // ACT_BWD row product: the rank-r operand over the tile's 256 columns
-  // (gate rows 0-15, then up rows 16-31: 32 x 256 bf16) is brought by DMA
-  // into the end of the last ring slot, which nothing else uses from here on;
-  // the wait of the K-extension (or the one before the epilogue) covers it,
-  // so the epilogue reads it from LDS. Row i keeps logical 16-byte chunk c at
-  // physical chunk c ^ (i & 15) of its 512 bytes: the 16 rows of a fragment
-  // read hit 16 different bank groups. Rows j >= rp_r and columns at or past
-  // hdim load as zeros.
-  constexpr int RPL_OFF = 5 * G_SLOT - 16384;
-  if (EPI == EPI_ACT_BWD && rp_on) {
-    const int up = wave >= 2;   // waves 0, 1: gate rows; 2, 3: up rows
-    const uint64_t base = (uint64_t)(up ? p.rp_l2 : p.rp_l);
-    const int nrec = rec_bytes(p.rp_r, p.rp_ldl);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int inst = 4 * wave + q;
-      const int i = 2 * inst + (lane >> 5), j = i & 15;
-      const int c = (lane & 31) ^ j;
-      const int64_t col = n0 + 8 * c;
-      const bool in = j < p.rp_r && col < p.hdim;
-      bload_lds<16>(base, nrec, smem + RPL_OFF + inst * 1024,
-                    in ? (uint32_t)((int64_t)j * p.rp_ldl + col) * 2u : OOB, 0);
-    }
-  }
+  if (EPI == EPI_ACT_BWD && rp_on && !rpl_pre) issue_rpl();
+  if (EPI == EPI_ACT_BWD && !tail_pre) fetch_gu(0);
 
-  // ACT_BWD: g and u of one epilogue slab, fetched a slab ahead (the first
-  // before the K-extension) so that their latency overlaps other work. Lane:
-  // 8 consecutive columns of staged rows q * 4 + lane / 16, i.e. tile rows
-  // wm*128 + 8*((lane/16) >> 1) + 2*mt + ((lane/16) & 1) + 16 q; rows past M
-  // and columns past N read nothing (zeros).
-  u32x4_t gw[8], uw[8];
-  auto fetch_gu = [&](int mt) {
-    const int sl = lane >> 4;
-    const int row0 = m0 + wm * 128 + 8 * (sl >> 1) + 2 * mt + (sl & 1);
-    const int col = n0 + wn * 128 + (lane & 15) * 8;
-    const int64_t o0 = (int64_t)row0 * p.hdim + col;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      gw[q] = u32x4_t{0u, 0u, 0u, 0u};
-      uw[q] = u32x4_t{0u, 0u, 0u, 0u};
-      if (row0 + 16 * q < p.M && col < p.N) {
-        const int64_t o = o0 + (int64_t)(16 * q) * p.hdim;
-        gw[q] = *(const u32x4_t*)(p.g_in + o);
-        uw[q] = *(const u32x4_t*)(p.u_in + o);
-      }
-    }
-  };
-  if (EPI == EPI_ACT_BWD) fetch_gu(0);
-
-  // ---- K-extension (LoRA up-projection): 64-wide steps over Ae / Be in
-  // slots 0 and 1, same layout; columns at or past KE read as zeros; split 0
-  // only ----
+  // ---- K-extension ----
   if (p.KE > 0 && ksp == 0) {
     const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
     const int neA = rec_bytes(rowsA, p.ldae);
     const int neB = rec_bytes(rowsB, p.ldbe);
     for (int e = 0; e * BK < p.KE; ++e) {
+      const bool pre = e == 0 && tail_pre;   // already in slots ka, kb
+      if (!pre) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = drow(j), c = e * BK + dcol(j);   // c < KE covers all 8 columns (KE % 16 == 0)
-        const bool in = c < p.KE;
-        bload_lds<16>(eA, neA, slot(0) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
-        bload_lds<16>(eB, neB, slot(1) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
+        for (int j = 0; j < 8; ++j) {
+          const int row = drow(j), c = e * BK + dcol(j);   // c < KE covers all 8 columns (KE % 16 == 0)
+          const bool in = c < p.KE;
+          bload_lds<16>(eA, neA, slot(0) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
+          bload_lds<16>(eB, neB, slot(1) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
+        }
       }
       wait_vm<0>();
       ring_barrier();
       const int nsub = (min(BK, p.KE - e * BK) + 15) >> 4;
+      const uint8_t* sa = pre ? slot(ka) : slot(0);
+      const uint8_t* sb = pre ? slot(kb) : slot(1);
       for (int ks = 0; ks < nsub; ++ks) {
         Frag f;
-        load_frag_at(f, slot(0), slot(1), ks, false);
+        load_frag_at(f, sa, sb, ks, false);
         mma(f);
       }
       __syncthreads();
