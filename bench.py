@@ -16,7 +16,7 @@ Prints ONE JSON line. Extra fields: roofline (the base-GEMM kernel, timed
 live with HIP events on its launch stream) and cpu_baseline (the fp64 CPU
 oracle on a bounded token sample of the same workload).
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama7b_mlp]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama7b_mlp]
 """
 import argparse
 import hashlib
@@ -44,8 +44,8 @@ QUANT_BYTES_PER_WEIGHT = 2 + 0.5 + 4 / 64   # bf16 in; codes + fp32 absmax out
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_mlp",
                    choices=MLP_WORKLOADS + QKV_WORKLOADS + LINEAR_WORKLOADS + [QUANT_WORKLOAD]
                    + FAST_WORKLOADS)
