@@ -51,6 +51,8 @@ def parse():
                    + FAST_WORKLOADS)
     p.add_argument("--tokens", type=int, default=0,
                    help="token count instead of the workload's 8192 (e.g. one GPU's data-parallel share)")
+    p.add_argument("--rank", type=int, default=0,
+                   help="LoRA rank r instead of the workload's 16 (1..64)")
     p.add_argument("--mode", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--base", default="nf4", choices=["nf4", "bf16"],
                    help="base weights: NF4 (QLoRA, default) or bf16 (16-bit LoRA variant)")
@@ -426,9 +428,13 @@ def main():
            "gemma7b_mlp": I.GEMMA_MLP, "mistral7b_qkv": I.MISTRAL_QKV,
            "llama7b_qkv": I.LLAMA_QKV, "llama7b_q_proj": I.QPROJ,
            "mistral7b_kv_proj": I.MISTRAL_KV}[a.workload]
-    full_m = cfg.m
+    full_m, full_r = cfg.m, cfg.r
     if a.tokens:
         cfg = dataclasses.replace(cfg, m=a.tokens)
+    if a.rank:
+        if not 1 <= a.rank <= 64:
+            sys.exit("--rank must be in 1..64")
+        cfg = dataclasses.replace(cfg, r=a.rank)
     dev = "cuda:0"
     w16 = a.base == "bf16"
     if lin:
@@ -511,7 +517,7 @@ def main():
         flops = mlp_flops(cfg.m, cfg.d, cfg.h, cfg.r)
     tflops = flops / (ms / 1e3) / 1e12
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
-    traffic = None if (w16 or cfg.m != full_m) else gemm_traffic(
+    traffic = None if (w16 or cfg.m != full_m or cfg.r != full_r) else gemm_traffic(
         os.path.join(os.path.dirname(_lib.__file__), "csrc"), cfg.name,
         "staged" if (qkv or a.mode == "auto") else a.mode)
     if lin:

@@ -950,32 +950,49 @@ void gemm_bf16_kernel(GemmArgs p) {
   if (EPI == EPI_ACT_BWD && !tail_pre) fetch_gu(0);
 
   // ---- K-extension ----
+  // Two slot pairs take turns, so that step e+1 loads while step e multiplies:
+  // pair 0 is where the bf16 path put step 0 (ka, kb), pair 1 the first two
+  // other slots (not slot 4 while it holds dH's rank-r operand).
   if (p.KE > 0 && ksp == 0) {
     const uint64_t eA = (uint64_t)(p.Ae + (int64_t)m0 * p.ldae), eB = (uint64_t)(p.Be + (int64_t)n0 * p.ldbe);
     const int neA = rec_bytes(rowsA, p.ldae);
     const int neB = rec_bytes(rowsB, p.ldbe);
-    for (int e = 0; e * BK < p.KE; ++e) {
-      const bool pre = e == 0 && tail_pre;   // already in slots ka, kb
-      if (!pre) {
+    auto issue_ke = [&](int e, uint8_t* sa, uint8_t* sb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = drow(j), c = e * BK + dcol(j);   // c < KE covers all 8 columns (KE % 16 == 0)
-          const bool in = c < p.KE;
-          bload_lds<16>(eA, neA, slot(0) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
-          bload_lds<16>(eB, neB, slot(1) + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int row = drow(j), c = e * BK + dcol(j);   // c < KE covers all 8 columns (KE % 16 == 0)
+        const bool in = c < p.KE;
+        bload_lds<16>(eA, neA, sa + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldae + c) * 2u : OOB, 0);
+        bload_lds<16>(eB, neB, sb + (8 * wave + j) * 1024, in ? (uint32_t)(row * p.ldbe + c) * 2u : OOB, 0);
       }
-      wait_vm<0>();
+    };
+    const int p0a = tail_pre ? ka : 0, p0b = tail_pre ? kb : 1;
+    int p1a = -1, p1b = -1;
+    for (int i = 0; i < 5; ++i) {
+      if (i == p0a || i == p0b || (EPI == EPI_ACT_BWD && rp_on && i == 4)) continue;
+      if (p1a < 0) p1a = i;
+      else if (p1b < 0) p1b = i;
+    }
+    const int nke = (p.KE + BK - 1) / BK;
+    if (!tail_pre) issue_ke(0, slot(p0a), slot(p0b));
+    for (int e = 0; e < nke; ++e) {
+      const bool odd = e & 1;
+      if (e + 1 < nke) {   // its pair was last read before the previous barrier
+        issue_ke(e + 1, slot(odd ? p0a : p1a), slot(odd ? p0b : p1b));
+        wait_vm<16>();     // all but step e+1's 16 loads per wave
+      } else {
+        wait_vm<0>();
+      }
       ring_barrier();
       const int nsub = (min(BK, p.KE - e * BK) + 15) >> 4;
-      const uint8_t* sa = pre ? slot(ka) : slot(0);
-      const uint8_t* sb = pre ? slot(kb) : slot(1);
+      const uint8_t* sa = slot(odd ? p1a : p0a);
+      const uint8_t* sb = slot(odd ? p1b : p0b);
       for (int ks = 0; ks < nsub; ++ks) {
         Frag f;
         load_frag_at(f, sa, sb, ks, false);
         mma(f);
       }
-      __syncthreads();
+      ring_barrier();
     }
   }
 
