@@ -20,7 +20,11 @@
 // conflict-free; the MFMA row order is permuted to match and undone in the
 // epilogue. Fragments of the next substep are read while the matrix cores
 // work on the current one, and sched_group_barrier hints interleave the LDS
-// reads and load issues with the MFMAs.
+// reads and load issues with the MFMAs. With a bf16 B operand the last
+// k-step also loads what the tile needs after its main loop (the
+// K-extension's first step into free ring slots, the row-product operands,
+// the first g/u slab of the ACT_BWD epilogue), and the K-extension's later
+// steps load while the previous one multiplies.
 // Optional extras: A split along K into up to three matrices (dX = sum of
 // dY_p W_p over separately stored dY_p), and an epilogue that writes column
 // ranges to three outputs (q, k, v from one GEMM).
@@ -38,7 +42,8 @@
 //
 // Epilogues: each wave stages a 32-row slab of its
 // accumulators through its own LDS region, so only wave-local ordering is
-// needed, and stores 16 bytes per lane. The gated epilogues take the
+// needed, reads a slab's staged values back in one batch (one LDS wait per
+// slab) and stores 16 bytes per lane. The gated epilogues take the
 // activation as a compile-time constant (one branch per launch, none per
 // value): with one wave per SIMD the epilogue runs with the matrix cores
 // idle, so its instruction count matters.
