@@ -587,7 +587,8 @@ void gemm_bf16_kernel(GemmArgs p) {
 
   const bool rp_on = (EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.rp_r > 0;
   // ACT_BWD: g and u of one epilogue slab, fetched a slab ahead (the first
-  // before the K-extension) so that their latency overlaps other work. Lane:
+  // beside the last k-step, or with an NF4 B before the K-extension) so that
+  // their latency overlaps other work. Lane:
   // 8 consecutive columns of staged rows q * 4 + lane / 16, i.e. tile rows
   // wm*128 + 8*((lane/16) >> 1) + 2*mt + ((lane/16) & 1) + 16 q; rows past M
   // and columns past N read nothing (zeros).
