@@ -251,7 +251,11 @@ TINY_MLP = [I.MlpCfg("tiny_swiglu", 200, 128, 192, 8, 2.0, "swiglu", 1.0),
             I.MlpCfg("r64_swiglu", 150, 128, 192, 64, 0.25, "swiglu", 1.0),
             I.MlpCfg("r64_geglu", 97, 192, 256, 64, 0.5, "geglu_tanh", 1.0),
             I.MlpCfg("r33_swiglu", 130, 64, 128, 33, 1.0, "swiglu", 1.0),
-            I.MlpCfg("r40_geglu", 64, 128, 320, 40, 0.4, "geglu_tanh", 1.0)]
+            I.MlpCfg("r40_geglu", 64, 128, 320, 40, 0.4, "geglu_tanh", 1.0),
+            # d = 320: 5 k-steps in the gate/up and dH GEMMs, so the last step's
+            # free ring slots start at slot 0 (the other starts come from d = 64,
+            # 128, 3072 and 4096)
+            I.MlpCfg("d320_swiglu", 150, 320, 256, 8, 1.0, "swiglu", 1.0)]
 
 
 @pytest.mark.parametrize("cfg", TINY_MLP, ids=lambda c: c.name)
