@@ -173,6 +173,32 @@ hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint1
 hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, int j0, int nj,
                                    float s, uint16_t* out, int64_t ocs, int64_t ojs,
                                    hipStream_t stream);
+// Up to kMaxColJobs independent reductions in one launch each: the first
+// stage for jobs that share M, R and ldv (each with its own G, ldg, C, V and
+// partial buffer), the second for jobs that share chunks, nj and s. Each job
+// computes exactly what the single-job call computes.
+constexpr int kMaxColJobs = 3;
+struct ColJobs {
+  const uint16_t* G[kMaxColJobs];
+  int64_t ldg[kMaxColJobs];
+  int C[kMaxColJobs];
+  const float* V[kMaxColJobs];
+  float* part[kMaxColJobs];
+};
+struct ColFinishJobs {
+  const float* part[kMaxColJobs];
+  int C[kMaxColJobs];
+  int R[kMaxColJobs];
+  int j0[kMaxColJobs];
+  uint16_t* out[kMaxColJobs];
+  int64_t ocs[kMaxColJobs];
+  int64_t ojs[kMaxColJobs];
+};
+hipError_t launch_colreduce_jobs(const ColJobs& jobs, int njobs, const uint16_t* gate,
+                                 const uint16_t* up, int act, int M, int64_t ldv, int R,
+                                 hipStream_t stream);
+hipError_t launch_colreduce_finish_jobs(const ColFinishJobs& jobs, int njobs, int chunks, int nj,
+                                        float s, hipStream_t stream);
 
 // ---- small layout kernels (lora.hip) ----
 // One copy (src != null) or zero-fill (src == null) job:

@@ -281,19 +281,26 @@ int colreduce_chunks(int M) {
 // transposed and permuted, so its fragments are single 16-byte LDS reads;
 // hi and lo are accumulated by two MFMAs into the same fp32 sum.
 // HMODE: G = H = bf16(act(g) * u), recomputed from g and u.
+// Several independent reductions of one shape class (same M, R, ldv) run as
+// one launch: blockIdx.z picks the job.
 template <int RT, bool HMODE>
-__global__ __launch_bounds__(256) void colreduce_kernel(const uint16_t* __restrict__ G,
+__global__ __launch_bounds__(256) void colreduce_kernel(ColJobs jobs,
                                                         const uint16_t* __restrict__ gate,
                                                         const uint16_t* __restrict__ up, int act,
-                                                        int64_t ldg, int M, int C,
-                                                        const float* __restrict__ V, int64_t ldv,
-                                                        int R, int rows_per_chunk,
-                                                        float* __restrict__ part) {
+                                                        int M, int64_t ldv, int R,
+                                                        int rows_per_chunk) {
   constexpr int CT = 256, KS = 32, PITCH = 544;
   __shared__ __attribute__((aligned(16))) uint8_t gt[2][KS * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][2][RT * 16][KS];
+  const int jb = blockIdx.z;
+  const uint16_t* __restrict__ G = jobs.G[jb];
+  const int64_t ldg = jobs.ldg[jb];
+  const int C = jobs.C[jb];
+  const float* __restrict__ V = jobs.V[jb];
+  float* __restrict__ part = jobs.part[jb];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * CT;
+  if (c0 >= C) return;   // the grid covers the widest job
   const int chunk = blockIdx.y;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(M, r0 + rows_per_chunk);
@@ -406,23 +413,28 @@ __global__ __launch_bounds__(256) void colreduce_kernel(const uint16_t* __restri
       }
 }
 
-hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint16_t* up, int act,
-                            int64_t ldg, int M, int C, const float* V, int64_t ldv, int R,
-                            float* part, hipStream_t stream) {
-  if (M <= 0 || C <= 0) return hipSuccess;
-  if (R < 1 || R > 64 || C % 8) return hipErrorInvalidValue;
+hipError_t launch_colreduce_jobs(const ColJobs& jobs, int njobs, const uint16_t* gate,
+                                 const uint16_t* up, int act, int M, int64_t ldv, int R,
+                                 hipStream_t stream) {
+  if (M <= 0 || njobs <= 0) return hipSuccess;
+  if (njobs > kMaxColJobs || R < 1 || R > 64) return hipErrorInvalidValue;
+  int cmax = 0;
+  for (int i = 0; i < njobs; ++i) {
+    if (jobs.C[i] <= 0 || jobs.C[i] % 8) return hipErrorInvalidValue;
+    cmax = std::max(cmax, jobs.C[i]);
+  }
   const int chunks = colreduce_chunks(M);
   const int rpc = (M + chunks - 1) / chunks;
-  dim3 grid((unsigned)((C + 255) / 256), (unsigned)chunks), block(256);
+  dim3 grid((unsigned)((cmax + 255) / 256), (unsigned)chunks, (unsigned)njobs), block(256);
   const bool hm = gate != nullptr;
 #define QL_CR(RTV)                                                                              \
   do {                                                                                          \
     if (hm)                                                                                     \
-      colreduce_kernel<RTV, true><<<grid, block, 0, stream>>>(G, gate, up, act, ldg, M, C, V,   \
-                                                              ldv, R, rpc, part);               \
+      colreduce_kernel<RTV, true><<<grid, block, 0, stream>>>(jobs, gate, up, act, M, ldv, R,   \
+                                                              rpc);                             \
     else                                                                                        \
-      colreduce_kernel<RTV, false><<<grid, block, 0, stream>>>(G, gate, up, act, ldg, M, C, V,  \
-                                                               ldv, R, rpc, part);              \
+      colreduce_kernel<RTV, false><<<grid, block, 0, stream>>>(jobs, gate, up, act, M, ldv, R,  \
+                                                               rpc);                            \
   } while (0)
   if (R <= 16) QL_CR(1);
   else if (R <= 32) QL_CR(2);
@@ -431,11 +443,23 @@ hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint1
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void colreduce_finish_kernel(const float* __restrict__ part,
-                                                               int chunks, int C, int R, int j0,
-                                                               int nj, float s,
-                                                               uint16_t* __restrict__ out,
-                                                               int64_t ocs, int64_t ojs) {
+hipError_t launch_colreduce(const uint16_t* G, const uint16_t* gate, const uint16_t* up, int act,
+                            int64_t ldg, int M, int C, const float* V, int64_t ldv, int R,
+                            float* part, hipStream_t stream) {
+  if (M <= 0 || C <= 0) return hipSuccess;
+  ColJobs j{};
+  j.G[0] = G; j.ldg[0] = ldg; j.C[0] = C; j.V[0] = V; j.part[0] = part;
+  return launch_colreduce_jobs(j, 1, gate, up, act, M, ldv, R, stream);
+}
+
+// blockIdx.y picks the job; the grid covers the largest one
+__global__ __launch_bounds__(256) void colreduce_finish_kernel(ColFinishJobs jobs, int chunks,
+                                                               int nj, float s) {
+  const int jb = blockIdx.y;
+  const float* __restrict__ part = jobs.part[jb];
+  const int C = jobs.C[jb], R = jobs.R[jb], j0 = jobs.j0[jb];
+  uint16_t* __restrict__ out = jobs.out[jb];
+  const int64_t ocs = jobs.ocs[jb], ojs = jobs.ojs[jb];
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (int64_t)C * nj) return;
   const int col = (int)(e / nj);
@@ -444,14 +468,24 @@ __global__ __launch_bounds__(256) void colreduce_finish_kernel(const float* __re
   out[(int64_t)col * ocs + (int64_t)jj * ojs] = (uint16_t)f32_to_bf16(s * sum);
 }
 
+hipError_t launch_colreduce_finish_jobs(const ColFinishJobs& jobs, int njobs, int chunks, int nj,
+                                        float s, hipStream_t stream) {
+  if (njobs <= 0 || nj <= 0) return hipSuccess;
+  if (njobs > kMaxColJobs) return hipErrorInvalidValue;
+  int64_t total = 0;
+  for (int i = 0; i < njobs; ++i) total = std::max<int64_t>(total, (int64_t)jobs.C[i] * nj);
+  if (total <= 0) return hipSuccess;
+  colreduce_finish_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)njobs), dim3(256), 0,
+                            stream>>>(jobs, chunks, nj, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, int j0, int nj,
                                    float s, uint16_t* out, int64_t ocs, int64_t ojs,
                                    hipStream_t stream) {
-  const int64_t total = (int64_t)C * nj;
-  if (total <= 0) return hipSuccess;
-  colreduce_finish_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-      part, chunks, C, R, j0, nj, s, out, ocs, ojs);
-  return hipGetLastError();
+  ColFinishJobs j{};
+  j.part[0] = part; j.C[0] = C; j.R[0] = R; j.j0[0] = j0; j.out[0] = out; j.ocs[0] = ocs; j.ojs[0] = ojs;
+  return launch_colreduce_finish_jobs(j, 1, chunks, nj, s, stream);
 }
 
 // ---------------------------------------------------------------- layout --
