@@ -1340,15 +1340,19 @@ static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t*
   const QkvExt ex{3 * r <= 64, r};
   const float s = w.s;
 
-  // LoRA operand layouts (Bext starts as zeros: each row block holds only its
-  // own projection's B)
-  QL_TRY(launch_zero(t.bext, (size_t)(nt * KE) * 2, st), "qkv_fwd: LoRA layouts");
+  // LoRA operand layouts, one launch: each row block of Bext holds its own
+  // projection's B at the hi and lo columns and zeros in the rest of the row
   {
     PrepJobs J;
     for (int p = 0; p < 3; ++p) {
       if (ex.one) J.copy(w.a[p], d, 1, r, d, t.lqkv + p * r * d, d, 1);
-      J.copy(w.b[p], r, 1, n[p], r, t.bext + off[p] * KE + ex.hi(p), KE, 1);
-      J.copy(w.b[p], r, 1, n[p], r, t.bext + off[p] * KE + ex.lo(p), KE, 1);
+      uint16_t* rows = t.bext + off[p] * KE;
+      const int64_t h0 = ex.hi(p), l0 = ex.lo(p);   // h0 + r <= l0
+      J.copy(w.b[p], r, 1, n[p], r, rows + h0, KE, 1);
+      J.copy(w.b[p], r, 1, n[p], r, rows + l0, KE, 1);
+      J.zero(n[p], h0, rows, KE, 1);
+      J.zero(n[p], l0 - h0 - r, rows + h0 + r, KE, 1);
+      J.zero(n[p], KE - l0 - r, rows + l0 + r, KE, 1);
     }
     if (!ex.one) J.zero(m, KE - 6 * r, t.uext + 6 * r, KE, 1);
     QL_TRY(launch_prep(J, st), "qkv_fwd: LoRA layouts");

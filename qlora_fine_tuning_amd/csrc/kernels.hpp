@@ -212,18 +212,21 @@ struct PrepJob {
   int64_t d_rs, d_cs;
   int interleave;
 };
-constexpr int kMaxPrepJobs = 16;
+constexpr int kMaxPrepJobs = 24;
 struct PrepJobs {
   PrepJob j[kMaxPrepJobs];
   int n = 0;
+  // a job past the capacity is not stored; n then exceeds it and launch_prep
+  // reports the overflow
   void copy(const uint16_t* src, int64_t s_rs, int64_t s_cs, int64_t rows, int64_t cols,
             uint16_t* dst, int64_t d_rs, int64_t d_cs, int interleave = 0) {
-    j[n++] = PrepJob{src, s_rs, s_cs, (int)rows, (int)cols, dst, d_rs, d_cs, interleave};
+    if (n < kMaxPrepJobs)
+      j[n] = PrepJob{src, s_rs, s_cs, (int)rows, (int)cols, dst, d_rs, d_cs, interleave};
+    ++n;
   }
   void zero(int64_t rows, int64_t cols, uint16_t* dst, int64_t d_rs, int64_t d_cs,
             int interleave = 0) {
-    if (rows > 0 && cols > 0)
-      j[n++] = PrepJob{nullptr, 0, 0, (int)rows, (int)cols, dst, d_rs, d_cs, interleave};
+    if (rows > 0 && cols > 0) copy(nullptr, 0, 0, rows, cols, dst, d_rs, d_cs, interleave);
   }
 };
 // Jobs must write disjoint elements (they run concurrently).
