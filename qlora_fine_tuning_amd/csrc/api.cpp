@@ -836,11 +836,17 @@ static int mlp_fwd_impl(const uint16_t* X, int64_t m, const MlpSrc* w, uint16_t*
     if (!wide)
       return launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)(2 * r), s, Ug, Uu, (int)r, r,
                            t.uextgu, KEgu, KEgu, t.rpart, q);
-    hipError_t e = launch_rowdot(X, d, t.lgu, d, (int)m, (int)d, (int)r, s, Ug, nullptr, (int)r, r,
-                                 t.uextgu, KEgu, E, t.rpart, q);
-    if (e != hipSuccess) return e;
-    return launch_rowdot(X, d, t.lgu + r * d, d, (int)m, (int)d, (int)r, s, Uu, nullptr, (int)r, r,
-                         t.uextgu + E, KEgu, E, t.rpart, q);
+    // Ug and Uu as two jobs of one launch, each with its own partials
+    RowJobs in{};
+    RowFinishJobs out{};
+    float* uo[2] = {Ug, Uu};
+    for (int q2 = 0; q2 < 2; ++q2) {
+      in.G[q2] = X; in.ldg[q2] = d; in.L[q2] = t.lgu + q2 * r * d; in.ldl[q2] = d; in.K[q2] = (int)d;
+      in.part[q2] = t.rpart + (int64_t)q2 * 16 * m * r;
+      out.Uf[q2] = uo[q2]; out.Uf2[q2] = nullptr; out.split[q2] = (int)r; out.ldu[q2] = r;
+      out.Ue[q2] = t.uextgu + q2 * E; out.ldue[q2] = KEgu; out.KE[q2] = (int)E;
+    }
+    return launch_rowdot_jobs(in, out, 2, (int)m, (int)r, s, q);
   };
   if (staged) {
     QL_TRY(side.open(), "mlp_fwd: helper stream");
@@ -1087,13 +1093,16 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* g
     QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)(2 * h), (int)(2 * r), s,
                          t.tgu, nullptr, (int)(2 * r), 2 * r, t.textgu, KEgu, KEgu, t.rpart, st),
            "mlp_bwd: Tg, Tu");
-  else {   // Tg = dg Bg, Tu = du Bu: one row product each, own K-extension segment
-    QL_TRY(launch_rowdot(t.dgu, 2 * h, t.ltgu, 2 * h, (int)m, (int)h, (int)r, s, t.tgu, nullptr,
-                         (int)r, 2 * r, t.textgu, KEgu, E, t.rpart, st),
-           "mlp_bwd: Tg");
-    QL_TRY(launch_rowdot(t.dgu + h, 2 * h, t.ltgu + r * 2 * h + h, 2 * h, (int)m, (int)h, (int)r, s,
-                         t.tgu + r, nullptr, (int)r, 2 * r, t.textgu + E, KEgu, E, t.rpart, st),
-           "mlp_bwd: Tu");
+  else {   // Tg = dg Bg, Tu = du Bu: one row product each (two jobs of one launch), own K-extension segment
+    RowJobs in{};
+    RowFinishJobs out{};
+    for (int q = 0; q < 2; ++q) {
+      in.G[q] = t.dgu + q * h; in.ldg[q] = 2 * h; in.L[q] = t.ltgu + q * (r * 2 * h + h);
+      in.ldl[q] = 2 * h; in.K[q] = (int)h; in.part[q] = t.rpart + (int64_t)q * 16 * m * r;
+      out.Uf[q] = t.tgu + q * r; out.Uf2[q] = nullptr; out.split[q] = (int)r; out.ldu[q] = 2 * r;
+      out.Ue[q] = t.textgu + q * E; out.ldue[q] = KEgu; out.KE[q] = (int)E;
+    }
+    QL_TRY(launch_rowdot_jobs(in, out, 2, (int)m, (int)r, s, st), "mlp_bwd: Tg, Tu");
   }
   QL_TRY(side.fork(4), "mlp_bwd: fork");
   // dAg = s Tg^T X ; dAu = s Tu^T X (helper stream, beside the dX GEMM)
@@ -1297,7 +1306,7 @@ static size_t plan_qkv_bwd(Carver& c, int64_t m, int64_t d, const int64_t n[3], 
   // the dA sets (one [d][3r] set, or three [d][r] sets side by side)
   t.part = c.take<float>(chunks * std::max(nt * r, 3 * d * r));
   t.wt = c.take<uint16_t>(d * nt);
-  t.rpart = c.take<float>(16 * m * r);
+  t.rpart = c.take<float>(3 * 16 * m * r);   // the three T_p row products' partials
   t.kpart = c.take<float>(splitk_elems(m, d, nt));
   if (w) *w = t;
   return c.off;
@@ -1377,11 +1386,16 @@ static int qkv_fwd_impl(const uint16_t* X, int64_t m, const QkvSrc& w, uint16_t*
     QL_TRY(launch_rowdot(X, d, t.lqkv, d, (int)m, (int)d, (int)(3 * r), s, U, nullptr,
                          (int)(3 * r), 3 * r, t.uext, KE, (int)KE, t.rpart, st),
            "qkv_fwd: U");
-  } else {
-    for (int p = 0; p < 3; ++p)
-      QL_TRY(launch_rowdot(X, d, w.a[p], d, (int)m, (int)d, (int)r, s, U + p * r, nullptr, (int)r,
-                           3 * r, t.uext + ex.hi(p), KE, (int)(2 * r), t.rpart, st),
-             "qkv_fwd: U");
+  } else {   // one row product per projection: three jobs of one launch, own partials
+    RowJobs in{};
+    RowFinishJobs out{};
+    for (int p = 0; p < 3; ++p) {
+      in.G[p] = X; in.ldg[p] = d; in.L[p] = w.a[p]; in.ldl[p] = d; in.K[p] = (int)d;
+      in.part[p] = t.rpart + (int64_t)p * 16 * m * r;
+      out.Uf[p] = U + p * r; out.Uf2[p] = nullptr; out.split[p] = (int)r; out.ldu[p] = 3 * r;
+      out.Ue[p] = t.uext + ex.hi(p); out.ldue[p] = KE; out.KE[p] = (int)(2 * r);
+    }
+    QL_TRY(launch_rowdot_jobs(in, out, 3, (int)m, (int)r, s, st), "qkv_fwd: U");
   }
   GemmArgs g = gemm_args();
   g.A = X; g.lda = d;
@@ -1482,11 +1496,17 @@ static int qkv_bwd_impl(const uint16_t* const dy[3], const int64_t lddy[3], cons
            "qkv_bwd: dB partials");
     QL_TRY(launch_colreduce_finish_jobs(fj, 3, chunks, (int)r, s, ss), "qkv_bwd: dB");
   }
-  for (int p = 0; p < 3; ++p)     // T_p = dY_p B_p, and [hi(sT_p) | lo(sT_p)]
-    QL_TRY(launch_rowdot(dy[p], lddy[p], t.lt + off[p], nt, (int)m, (int)n[p], (int)r, s,
-                         t.t + p * r, nullptr, (int)r, 3 * r, t.text + 2 * r * p, KE, (int)(2 * r),
-                         t.rpart, st),
-           "qkv_bwd: T");
+  {   // T_p = dY_p B_p, and [hi(sT_p) | lo(sT_p)]: three jobs of one launch, own partials
+    RowJobs in{};
+    RowFinishJobs out{};
+    for (int p = 0; p < 3; ++p) {
+      in.G[p] = dy[p]; in.ldg[p] = lddy[p]; in.L[p] = t.lt + off[p]; in.ldl[p] = nt;
+      in.K[p] = (int)n[p]; in.part[p] = t.rpart + (int64_t)p * 16 * m * r;
+      out.Uf[p] = t.t + p * r; out.Uf2[p] = nullptr; out.split[p] = (int)r; out.ldu[p] = 3 * r;
+      out.Ue[p] = t.text + 2 * r * p; out.ldue[p] = KE; out.KE[p] = (int)(2 * r);
+    }
+    QL_TRY(launch_rowdot_jobs(in, out, 3, (int)m, (int)r, s, st), "qkv_bwd: T");
+  }
   QL_TRY(side.fork(2), "qkv_bwd: fork");
   if (one_a) {   // dA_p = s T_p^T X, one read of X for all three
     QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, d, (int)m, (int)d, t.t, 3 * r, (int)(3 * r),

@@ -160,6 +160,37 @@ hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int6
 hipError_t launch_rowdot_finish(const float* part, int nsplit, int M, int R, float s, float* Uf,
                                 float* Uf2, int split, int64_t ldu, uint16_t* Ue, int64_t ldue,
                                 int KE, hipStream_t stream);
+// Up to kMaxRowJobs independent products with the same M and R in one launch
+// per stage: job i is what launch_rowdot(in.G[i], in.ldg[i], in.L[i],
+// in.ldl[i], M, in.K[i], R, s, out.Uf[i], out.Uf2[i], out.split[i],
+// out.ldu[i], out.Ue[i], out.ldue[i], out.KE[i], in.part[i]) computes, with
+// its own partial buffer (the split counts and K ranges are filled in here).
+constexpr int kMaxRowJobs = 3;
+struct RowJobs {
+  const uint16_t* G[kMaxRowJobs];
+  int64_t ldg[kMaxRowJobs];
+  const uint16_t* L[kMaxRowJobs];
+  int64_t ldl[kMaxRowJobs];
+  int K[kMaxRowJobs];
+  int kper[kMaxRowJobs];
+  int nsplit[kMaxRowJobs];
+  float* part[kMaxRowJobs];
+};
+struct RowFinishJobs {
+  const float* part[kMaxRowJobs];
+  int nsplit[kMaxRowJobs];
+  float* Uf[kMaxRowJobs];
+  float* Uf2[kMaxRowJobs];
+  int split[kMaxRowJobs];
+  int64_t ldu[kMaxRowJobs];
+  uint16_t* Ue[kMaxRowJobs];
+  int64_t ldue[kMaxRowJobs];
+  int KE[kMaxRowJobs];
+};
+hipError_t launch_rowdot_jobs(const RowJobs& in, const RowFinishJobs& out, int njobs, int M, int R,
+                              float s, hipStream_t stream);
+hipError_t launch_rowdot_finish_jobs(const RowFinishJobs& jobs, int njobs, int M, int R, float s,
+                                     hipStream_t stream);
 
 // Column reduction over tokens, first stage: for each chunk c of rows,
 // part[c][col][j] = sum_{i in chunk} G[i][col] * V[i][vofs + j], j < R.

@@ -66,16 +66,24 @@ int rowdot_splits(int M, int K) {
 // part[split][i][j] = sum over the split's K range of G[i][k] * L[j][k].
 // 64 rows x 128 K per step, staged by direct-to-LDS loads in a 3-deep ring;
 // wave w owns rows 16w..16w+15 and all RT*16 columns (MFMA 16x16x32).
+// Several independent products with the same M and R run as one launch:
+// blockIdx.z picks the job, and the grid's y extent covers the job with the
+// most K splits.
 template <int RT>
-__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ G, int64_t ldg,
-                                                     const uint16_t* __restrict__ L, int64_t ldl,
-                                                     int M, int K, int R, int kper,
-                                                     float* __restrict__ part) {
+__global__ __launch_bounds__(256) void rowdot_kernel(RowJobs jobs, int M, int R) {
   constexpr int GB = RD_ROWS * RD_KT * 2;     // G tile bytes
   constexpr int LB = RT * 16 * RD_KT * 2;     // L tile bytes
   constexpr int STAGE = GB + LB;
   constexpr int NL = 4 + RT;                  // DMA instructions per stage per wave
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RD_STAGES * STAGE];
+  const int jb = blockIdx.z;
+  if ((int)blockIdx.y >= jobs.nsplit[jb]) return;
+  const uint16_t* __restrict__ G = jobs.G[jb];
+  const int64_t ldg = jobs.ldg[jb];
+  const uint16_t* __restrict__ L = jobs.L[jb];
+  const int64_t ldl = jobs.ldl[jb];
+  const int K = jobs.K[jb], kper = jobs.kper[jb];
+  float* __restrict__ part = jobs.part[jb];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * RD_ROWS;
   const int kbeg = blockIdx.y * kper;
@@ -189,12 +197,16 @@ __device__ __forceinline__ f32x4_t ordered_sum4(const float* __restrict__ p, int
 // two outputs at column `split`) and the bf16 K-extension operand
 // Ue = [hi(sU) | lo(sU) | 0]. A thread takes 4 consecutive columns of one row
 // of [0, max(R, KE)): with R % 4 == 0 it reads them as one 16-byte partial.
-__global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restrict__ part,
-                                                            int nsplit, int M, int R, float s,
-                                                            float* __restrict__ Uf,
-                                                            float* __restrict__ Uf2, int split,
-                                                            int64_t ldu, uint16_t* __restrict__ Ue,
-                                                            int64_t ldue, int KE) {
+// blockIdx.y picks the job; the grid covers the widest one
+__global__ __launch_bounds__(256) void rowdot_finish_kernel(RowFinishJobs jobs, int M, int R,
+                                                            float s) {
+  const int jb = blockIdx.y;
+  const float* __restrict__ part = jobs.part[jb];
+  const int nsplit = jobs.nsplit[jb], split = jobs.split[jb], KE = jobs.KE[jb];
+  float* __restrict__ Uf = jobs.Uf[jb];
+  float* __restrict__ Uf2 = jobs.Uf2[jb];
+  const int64_t ldu = jobs.ldu[jb], ldue = jobs.ldue[jb];
+  uint16_t* __restrict__ Ue = jobs.Ue[jb];
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int W4 = ((KE > R ? KE : R) + 3) >> 2;
   if (e >= (int64_t)M * W4) return;
@@ -230,37 +242,70 @@ __global__ __launch_bounds__(256) void rowdot_finish_kernel(const float* __restr
   }
 }
 
-hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
-                         int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
-                         uint16_t* Ue, int64_t ldue, int KE, float* part, hipStream_t stream) {
-  if (M <= 0) return hipSuccess;
-  if (R < 1 || R > 64 || K % 64) return hipErrorInvalidValue;
-  const int ns = rowdot_splits(M, K);
-  int kper = (K + ns - 1) / ns;
-  kper = (kper + RD_KT - 1) / RD_KT * RD_KT;
-  const int nsplit = (K + kper - 1) / kper;
-  dim3 grid((unsigned)((M + RD_ROWS - 1) / RD_ROWS), (unsigned)nsplit), block(256);
+hipError_t launch_rowdot_finish_jobs(const RowFinishJobs& jobs, int njobs, int M, int R, float s,
+                                     hipStream_t stream) {
+  if (M <= 0 || njobs <= 0) return hipSuccess;
+  if (njobs > kMaxRowJobs || R < 1 || R > 64) return hipErrorInvalidValue;
+  int64_t total = 0;
+  for (int i = 0; i < njobs; ++i) {
+    if (jobs.nsplit[i] < 1) return hipErrorInvalidValue;
+    const int W4 = ((jobs.KE[i] > R ? jobs.KE[i] : R) + 3) / 4;
+    total = std::max<int64_t>(total, (int64_t)M * W4);
+  }
+  rowdot_finish_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)njobs), dim3(256), 0,
+                         stream>>>(jobs, M, R, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot_jobs(const RowJobs& in, const RowFinishJobs& out, int njobs, int M, int R,
+                              float s, hipStream_t stream) {
+  if (M <= 0 || njobs <= 0) return hipSuccess;
+  if (njobs > kMaxRowJobs || R < 1 || R > 64) return hipErrorInvalidValue;
+  RowJobs jobs = in;
+  RowFinishJobs fin = out;
+  int nsmax = 1;
+  for (int i = 0; i < njobs; ++i) {
+    const int K = jobs.K[i];
+    if (K <= 0 || K % 64) return hipErrorInvalidValue;
+    const int ns = rowdot_splits(M, K);
+    int kper = (K + ns - 1) / ns;
+    kper = (kper + RD_KT - 1) / RD_KT * RD_KT;
+    jobs.kper[i] = kper;
+    jobs.nsplit[i] = (K + kper - 1) / kper;
+    fin.part[i] = jobs.part[i];
+    fin.nsplit[i] = jobs.nsplit[i];
+    nsmax = std::max(nsmax, jobs.nsplit[i]);
+  }
+  dim3 grid((unsigned)((M + RD_ROWS - 1) / RD_ROWS), (unsigned)nsmax, (unsigned)njobs), block(256);
   switch ((R + 15) / 16) {
-    case 1: rowdot_kernel<1><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
-    case 2: rowdot_kernel<2><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
-    case 3: rowdot_kernel<3><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
-    case 4: rowdot_kernel<4><<<grid, block, 0, stream>>>(G, ldg, L, ldl, M, K, R, kper, part); break;
+    case 1: rowdot_kernel<1><<<grid, block, 0, stream>>>(jobs, M, R); break;
+    case 2: rowdot_kernel<2><<<grid, block, 0, stream>>>(jobs, M, R); break;
+    case 3: rowdot_kernel<3><<<grid, block, 0, stream>>>(jobs, M, R); break;
+    case 4: rowdot_kernel<4><<<grid, block, 0, stream>>>(jobs, M, R); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_rowdot_finish(part, nsplit, M, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE, stream);
+  return launch_rowdot_finish_jobs(fin, njobs, M, R, s, stream);
+}
+
+hipError_t launch_rowdot(const uint16_t* G, int64_t ldg, const uint16_t* L, int64_t ldl, int M,
+                         int K, int R, float s, float* Uf, float* Uf2, int split, int64_t ldu,
+                         uint16_t* Ue, int64_t ldue, int KE, float* part, hipStream_t stream) {
+  RowJobs in{};
+  RowFinishJobs out{};
+  in.G[0] = G; in.ldg[0] = ldg; in.L[0] = L; in.ldl[0] = ldl; in.K[0] = K; in.part[0] = part;
+  out.Uf[0] = Uf; out.Uf2[0] = Uf2; out.split[0] = split; out.ldu[0] = ldu; out.Ue[0] = Ue;
+  out.ldue[0] = ldue; out.KE[0] = KE;
+  return launch_rowdot_jobs(in, out, 1, M, R, s, stream);
 }
 
 hipError_t launch_rowdot_finish(const float* part, int nsplit, int M, int R, float s, float* Uf,
                                 float* Uf2, int split, int64_t ldu, uint16_t* Ue, int64_t ldue,
                                 int KE, hipStream_t stream) {
-  if (M <= 0) return hipSuccess;
-  if (R < 1 || R > 64 || nsplit < 1) return hipErrorInvalidValue;
-  const int W4 = ((KE > R ? KE : R) + 3) / 4;
-  const int64_t total = (int64_t)M * W4;
-  rowdot_finish_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-      part, nsplit, M, R, s, Uf, Uf2, split, ldu, Ue, ldue, KE);
-  return hipGetLastError();
+  RowFinishJobs out{};
+  out.part[0] = part; out.nsplit[0] = nsplit; out.Uf[0] = Uf; out.Uf2[0] = Uf2;
+  out.split[0] = split; out.ldu[0] = ldu; out.Ue[0] = Ue; out.ldue[0] = ldue; out.KE[0] = KE;
+  return launch_rowdot_finish_jobs(out, 1, M, R, s, stream);
 }
 
 // --------------------------------------------------------------- colreduce --
