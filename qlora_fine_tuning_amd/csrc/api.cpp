@@ -205,7 +205,7 @@ size_t plan_linear_bwd(Carver& c, int64_t m, int64_t k, int64_t n, int64_t r, in
   t.bext = c.take<uint16_t>(k * KE);
   t.t = c.take<float>(m * r);
   t.text = c.take<uint16_t>(m * KE);
-  t.part = c.take<float>(chunks * std::max(n, k) * r);
+  t.part = c.take<float>(chunks * (n + k) * r);   // dB and dA partial sets side by side
   t.wt = staged_like(mode) ? c.take<uint16_t>(k * n) : nullptr;
   t.rpart = c.take<float>(16 * m * r);
   t.kpart = c.take<float>(splitk_elems(m, k, n));
@@ -620,11 +620,6 @@ static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U
   QL_TRY(launch_rowdot(dY, n, t.lt, n, (int)m, (int)n, (int)r, s, t.t, nullptr, (int)r, r, t.text,
                        KE, KE, t.rpart, st),
          "linear_bwd: T = dY B");
-  // dB = s dY^T U
-  QL_TRY(launch_colreduce(dY, nullptr, nullptr, 0, n, (int)m, (int)n, U, r, (int)r, t.part, st),
-         "linear_bwd: dB partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)n, (int)r, 0, (int)r, s, dB, r, 1, st),
-         "linear_bwd: dB");
   // dX = dY W + s T A
   if (dX) {
     GemmArgs g = gemm_args();
@@ -646,11 +641,22 @@ static int linear_bwd_impl(const uint16_t* dY, const uint16_t* X, const float* U
     use_splitk(g, t.kpart);
     QL_TRY(run_gemm(g, r, st), "linear_bwd: dX GEMM");
   }
-  // dA = s T^T X
-  QL_TRY(launch_colreduce(X, nullptr, nullptr, 0, k, (int)m, (int)k, t.t, r, (int)r, t.part, st),
-         "linear_bwd: dA partials");
-  QL_TRY(launch_colreduce_finish(t.part, chunks, (int)k, (int)r, 0, (int)r, s, dA, 1, k, st),
-         "linear_bwd: dA");
+  // dB = s dY^T U and dA = s T^T X: two jobs of one launch per stage, their
+  // partial sets side by side
+  {
+    ColJobs cj{};
+    ColFinishJobs fj{};
+    cj.G[0] = dY; cj.ldg[0] = n; cj.C[0] = (int)n; cj.V[0] = U; cj.part[0] = t.part;
+    cj.G[1] = X; cj.ldg[1] = k; cj.C[1] = (int)k; cj.V[1] = t.t;
+    cj.part[1] = t.part + (int64_t)chunks * n * r;
+    fj.part[0] = cj.part[0]; fj.C[0] = (int)n; fj.R[0] = (int)r; fj.j0[0] = 0; fj.out[0] = dB;
+    fj.ocs[0] = r; fj.ojs[0] = 1;
+    fj.part[1] = cj.part[1]; fj.C[1] = (int)k; fj.R[1] = (int)r; fj.j0[1] = 0; fj.out[1] = dA;
+    fj.ocs[1] = 1; fj.ojs[1] = k;
+    QL_TRY(launch_colreduce_jobs(cj, 2, nullptr, nullptr, 0, (int)m, r, (int)r, st),
+           "linear_bwd: dB, dA partials");
+    QL_TRY(launch_colreduce_finish_jobs(fj, 2, chunks, (int)r, s, st), "linear_bwd: dB, dA");
+  }
   return QLORA_OK;
 }
 
