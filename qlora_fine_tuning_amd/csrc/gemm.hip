@@ -224,6 +224,10 @@ void gemm_bf16_kernel(GemmArgs p) {
   const int tm = first_m + (pid % per_group) % gsz;
   const int tn = (pid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+  // every row and column of the tile is inside the output: the epilogue then
+  // runs without per-row bounds checks (no predicated stores, no merged
+  // zero/value registers)
+  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
   const int nk = p.K / BK;
   // this job's k-steps [kt0, kt1) (the host keeps every split non-empty)
   const int kper = (nk + nsplit - 1) / nsplit;
@@ -593,7 +597,8 @@ void gemm_bf16_kernel(GemmArgs p) {
   // wm*128 + 8*((lane/16) >> 1) + 2*mt + ((lane/16) & 1) + 16 q; rows past M
   // and columns past N read nothing (zeros).
   u32x4_t gw[8], uw[8];
-  auto fetch_gu = [&](int mt) {
+  auto fetch_gu = [&](int mt, auto in_c) {
+    constexpr bool IN = decltype(in_c)::value;
     const int sl = lane >> 4;
     const int row0 = m0 + wm * 128 + 8 * (sl >> 1) + 2 * mt + (sl & 1);
     const int col = n0 + wn * 128 + (lane & 15) * 8;
@@ -602,7 +607,7 @@ void gemm_bf16_kernel(GemmArgs p) {
     for (int q = 0; q < 8; ++q) {
       gw[q] = u32x4_t{0u, 0u, 0u, 0u};
       uw[q] = u32x4_t{0u, 0u, 0u, 0u};
-      if (row0 + 16 * q < p.M && col < p.N) {
+      if (IN || (row0 + 16 * q < p.M && col < p.N)) {
         const int64_t o = o0 + (int64_t)(16 * q) * p.hdim;
         gw[q] = *(const u32x4_t*)(p.g_in + o);
         uw[q] = *(const u32x4_t*)(p.u_in + o);
@@ -928,7 +933,10 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
     if (rpl_pre) issue_rpl();
     if (EPI == EPI_GATEUP && rp_on) load_rpb();
-    if (EPI == EPI_ACT_BWD) fetch_gu(0);
+    if (EPI == EPI_ACT_BWD) {
+      if (interior) fetch_gu(0, std::integral_constant<bool, true>());
+      else fetch_gu(0, std::integral_constant<bool, false>());
+    }
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
@@ -953,7 +961,10 @@ void gemm_bf16_kernel(GemmArgs p) {
   __syncthreads();
 
   if (EPI == EPI_ACT_BWD && rp_on && !rpl_pre) issue_rpl();
-  if (EPI == EPI_ACT_BWD && !tail_pre) fetch_gu(0);
+  if (EPI == EPI_ACT_BWD && !tail_pre) {
+    if (interior) fetch_gu(0, std::integral_constant<bool, true>());
+    else fetch_gu(0, std::integral_constant<bool, false>());
+  }
 
   // ---- K-extension ----
   // Two slot pairs take turns, so that step e+1 loads while step e multiplies:
@@ -1091,9 +1102,10 @@ void gemm_bf16_kernel(GemmArgs p) {
   };
 
   // one slab per call; mt is a compile-time constant so that acc stays in registers
-  auto slab = [&](auto mt_c, auto act_c) {
+  auto slab = [&](auto mt_c, auto act_c, auto in_c) {
     constexpr int mt = decltype(mt_c)::value;
     constexpr int ACT = decltype(act_c)::value;
+    constexpr bool IN = decltype(in_c)::value;
     auto grow = [&](int s) { return m0 + wm * 128 + 8 * (s >> 1) + 2 * mt + (s & 1); };
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -1124,7 +1136,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int s = q * 4 + (lane >> 4);
         const int row = row0 + 16 * q;
         u32x4_t odg = u32x4_t{0u, 0u, 0u, 0u}, odu = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < p.M && colok) {
+        if (IN || (row < p.M && colok)) {
           if ((EPI == EPI_STORE || EPI == EPI_STORE3) && SPLIT) {   // fp32 partial
             float* o = p.part + poff0 + (int64_t)(16 * q) * p.N;
             *(f32x4_t*)o = f32x4_t{x0[0], x1[0], x0[1], x1[1]};
@@ -1185,7 +1197,7 @@ void gemm_bf16_kernel(GemmArgs p) {
       else
         rows(std::integral_constant<bool, false>());
       // the next slab's g and u: this slab's are consumed
-      if constexpr (EPI == EPI_ACT_BWD && mt < 3) fetch_gu(mt + 1);
+      if constexpr (EPI == EPI_ACT_BWD && mt < 3) fetch_gu(mt + 1, in_c);
       if (EPI == EPI_ACT_BWD && rp_on) {
         wave_sync();
         const uint16_t* pan = reinterpret_cast<const uint16_t*>(stage);
@@ -1218,7 +1230,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int s = q * 8 + (lane >> 3);
         const int row = row0 + 32 * q;
         u32x4_t oh = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < p.M && col0 < p.N) {
+        if (IN || (row < p.M && col0 < p.N)) {
           const f32x4_t g0 = gx[q][0], g1 = gx[q][1];
           const f32x4_t u0 = ux[q][0], u1 = ux[q][1];
           float gv[8], uv[8];   // tile order
@@ -1255,16 +1267,21 @@ void gemm_bf16_kernel(GemmArgs p) {
     wave_sync();
   };
   // the activation is fixed per launch: one branch here, none per value
-  auto slabs = [&](auto act_c) {
-    slab(std::integral_constant<int, 0>(), act_c);
-    slab(std::integral_constant<int, 1>(), act_c);
-    slab(std::integral_constant<int, 2>(), act_c);
-    slab(std::integral_constant<int, 3>(), act_c);
+  auto slabs = [&](auto act_c, auto in_c) {
+    slab(std::integral_constant<int, 0>(), act_c, in_c);
+    slab(std::integral_constant<int, 1>(), act_c, in_c);
+    slab(std::integral_constant<int, 2>(), act_c, in_c);
+    slab(std::integral_constant<int, 3>(), act_c, in_c);
+  };
+  auto slabs_in = [&](auto act_c) {
+    // the three-output epilogue keeps one body: a second copy spills there
+    if (EPI != EPI_STORE3 && interior) slabs(act_c, std::integral_constant<bool, true>());
+    else slabs(act_c, std::integral_constant<bool, false>());
   };
   if ((EPI == EPI_GATEUP || EPI == EPI_ACT_BWD) && p.act != 0)
-    slabs(std::integral_constant<int, 1>());
+    slabs_in(std::integral_constant<int, 1>());
   else
-    slabs(std::integral_constant<int, 0>());
+    slabs_in(std::integral_constant<int, 0>());
   if (rp_on) {
     // every wave's parked results are in LDS (lgkmcnt(0)); the global stores
     // in flight are not waited for
