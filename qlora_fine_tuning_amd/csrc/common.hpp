@@ -38,37 +38,54 @@ __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
 // Activations of the gated MLP and their derivatives (fp32).
-//   act 0: silu(g) = g * sigmoid(g);  silu'(g) = sig * (1 + g * (1 - sig))
+//   act 0: silu(g) = g * sig(g);  silu'(g) = sig * (1 + g * (1 - sig))
+//          = sig + silu(g) * (1 - sig)
 //   act 1: gelu_tanh(g) = g/2 * (1 + tanh z), z = sqrt(2/pi) (g + 0.044715 g^3)
 //          gelu'(g) = (1 + tanh z)/2 + g/2 (1 - tanh^2 z) sqrt(2/pi) (1 + 3*0.044715 g^2)
-// tanh z is formed as 2 * sigmoid(2z) - 1.
+//   With 1 + tanh z = 2 sig(2z) and 1 - tanh^2 z = 4 sig(2z) (1 - sig(2z)),
+//   writing S = sig(2z):  gelu_tanh(g) = g * S,
+//          gelu'(g) = S + g S (1 - S) (2 sqrt(2/pi) + 6 sqrt(2/pi) 0.044715 g^2).
+//   The exponent of sig(2z), -2z log2(e), is g (c1 + c2 g^2) with folded
+//   constants, so one v_exp_f32 (2^x) and one reciprocal form S; the forms
+//   with S avoid the cancellation in 1 + tanh z for large negative z.
 // ACT is a compile-time constant here so that code applying it to many values
 // has no branch per value; the int overloads pick one of the two.
+namespace actc {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kS2pi = 0.7978845608028654f;          // sqrt(2/pi)
+constexpr float kGk = 0.044715f;
+constexpr float kC1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;            // -2 log2(e) sqrt(2/pi)
+constexpr float kC2 = -2.0f * 1.4426950408889634f * 0.7978845608028654f * 0.044715f;
+constexpr float kD0 = 2.0f * 0.7978845608028654f;                                   // 2 sqrt(2/pi)
+constexpr float kD2 = 6.0f * 0.7978845608028654f * 0.044715f;
+}  // namespace actc
+
+// sig(2z) for the tanh-GELU, from g and g^2
+__device__ __forceinline__ float gelu_sig2z(float g, float g2) {
+  const float x = g * __builtin_fmaf(g2, actc::kC2, actc::kC1);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+}
+
 template <int ACT>
 __device__ __forceinline__ void act_fwd_bwd_t(float g, float* a, float* da) {
   if (ACT == 0) {
-    float sg = sigmoidf_(g);
-    *a = g * sg;
-    *da = sg * (1.0f + g * (1.0f - sg));
+    const float sg = sigmoidf_(g);
+    const float av = g * sg;
+    *a = av;
+    *da = __builtin_fmaf(av, 1.0f - sg, sg);
   } else {
-    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-    const float k1 = 0.044715f;
-    float g2 = g * g;
-    float z = k0 * (g + k1 * g2 * g);
-    float th = 2.0f * sigmoidf_(2.0f * z) - 1.0f;
-    *a = 0.5f * g * (1.0f + th);
-    *da = 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * k0 * (1.0f + 3.0f * k1 * g2);
+    const float g2 = g * g;
+    const float S = gelu_sig2z(g, g2);
+    const float av = g * S;
+    *a = av;
+    *da = __builtin_fmaf(av * (1.0f - S), __builtin_fmaf(g2, actc::kD2, actc::kD0), S);
   }
 }
 
 template <int ACT>
 __device__ __forceinline__ float act_fwd_t(float g) {
   if (ACT == 0) return g * sigmoidf_(g);
-  const float k0 = 0.7978845608028654f;
-  const float k1 = 0.044715f;
-  float z = k0 * (g + k1 * g * g * g);
-  float th = 2.0f * sigmoidf_(2.0f * z) - 1.0f;
-  return 0.5f * g * (1.0f + th);
+  return g * gelu_sig2z(g, g * g);
 }
 
 __device__ __forceinline__ void act_fwd_bwd(int act, float g, float* a, float* da) {
