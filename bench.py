@@ -506,6 +506,19 @@ def main():
     ms = ev0.elapsed_time(ev1) / a.steps
     launches, gemm_ms, gemm_flops = Q.trace_read()
     Q.trace_enable(False)
+    # per-step median and minimum: a second pass of the same steps with an
+    # event at every step boundary (kept out of the timed region above, so
+    # those events do not add to `value`)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(a.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
+    step_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
 
     peak_meas, shader_ghz = Q.probe_mfma_peak(20000)
 
@@ -541,6 +554,7 @@ def main():
                    "global_batch": cfg.m, "parallelism": "none (1 GPU)"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.m / (ms / 1e3), 1),
+        "step_ms_median": round(step_median, 4), "step_ms_min": round(per_step[0], 4),
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (base GEMMs, LoRA as K-extension)",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
