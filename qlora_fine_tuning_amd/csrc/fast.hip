@@ -295,6 +295,9 @@ hipError_t launch_rope(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t ldy,
 namespace {
 
 constexpr int XENT_THREADS = 256;
+// 16-byte loads a thread issues before it uses any of them (the row passes
+// are bound by how many bytes each workgroup keeps in flight)
+constexpr int XENT_LOADS = 8;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -336,6 +339,36 @@ __device__ __forceinline__ void block_lse(float& mx, float& sm) {
   for (int i = 1; i < XENT_THREADS / 64; ++i) lse_merge(mx, sm, smx[i], ssm[i]);
 }
 
+// The gradient of one row's 8-value chunks, c = threadIdx.x + k * XENT_THREADS:
+// dx = (2^(x log2(e) - l2) - onehot(lab)) * scale. Each chunk is read and
+// written by the same thread, so dx may be x; the loads of a batch of chunks
+// are issued before any of its stores (a store to dx could otherwise alias
+// the next load, and the loop would keep one load in flight).
+__device__ __forceinline__ void xent_grad_chunks(const uint16_t* x, uint16_t* dx, int64_t nc,
+                                                 int64_t lab, float l2, float scale, bool on) {
+  auto grad = [&](const u32x4_t& v, int64_t c) {
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = on ? exp2_hw(fmaf(f[e], LOG2E, -l2)) : 0.0f;
+      f[e] = (p - (c * 8 + e == lab ? 1.0f : 0.0f)) * scale;
+    }
+    *(u32x4_t*)(dx + c * 8) = pack8(f);
+  };
+  constexpr int U = 4;
+  int64_t c = threadIdx.x;
+  for (; c + (U - 1) * XENT_THREADS < nc; c += U * XENT_THREADS) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) grad(v[u], c + u * XENT_THREADS);
+  }
+  for (; c < nc; c += XENT_THREADS) grad(*(const u32x4_t*)(x + c * 8), c);
+}
+
 }  // namespace
 
 // One workgroup per row of logits X [m][V] (row pitch ld, a multiple of 8).
@@ -365,12 +398,12 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fwd_kernel(const uint16_t* 
     sm = cs;
   };
   int64_t c = threadIdx.x;
-  for (; c + 3 * XENT_THREADS < nc; c += 4 * XENT_THREADS) {   // 4 loads in flight
-    u32x4_t v[4];
+  for (; c + (XENT_LOADS - 1) * XENT_THREADS < nc; c += XENT_LOADS * XENT_THREADS) {   // loads in flight
+    u32x4_t v[XENT_LOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+    for (int u = 0; u < XENT_LOADS; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fold(v[u]);
+    for (int u = 0; u < XENT_LOADS; ++u) fold(v[u]);
   }
   for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)   // tail of V % 8
@@ -441,17 +474,7 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_bwd_kernel(const uint16_t* 
   const uint16_t* x = X + row * ld;
   uint16_t* dx = dX + row * ldd;
   const int64_t nc = V / 8;
-  #pragma unroll 4
-  for (int64_t c = threadIdx.x; c < nc; c += XENT_THREADS) {
-    float f[8];
-    unpack8(*(const u32x4_t*)(x + c * 8), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = on ? exp2_hw(fmaf(f[e], LOG2E, -l2)) : 0.0f;
-      f[e] = (p - (c * 8 + e == lab ? 1.0f : 0.0f)) * scale;
-    }
-    *(u32x4_t*)(dx + c * 8) = pack8(f);
-  }
+  xent_grad_chunks(x, dx, nc, lab, l2, scale, on);
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS) {
     const float p = on ? exp2_hw(fmaf(bf16_to_f32(x[j]), LOG2E, -l2)) : 0.0f;
     dx[j] = (uint16_t)f32_to_bf16((p - (j == lab ? 1.0f : 0.0f)) * scale);
@@ -508,12 +531,12 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fused_kernel(const uint16_t
     sm = cs;
   };
   int64_t c = threadIdx.x;
-  for (; c + 3 * XENT_THREADS < nc; c += 4 * XENT_THREADS) {
-    u32x4_t v[4];
+  for (; c + (XENT_LOADS - 1) * XENT_THREADS < nc; c += XENT_LOADS * XENT_THREADS) {   // loads in flight
+    u32x4_t v[XENT_LOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+    for (int u = 0; u < XENT_LOADS; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fold(v[u]);
+    for (int u = 0; u < XENT_LOADS; ++u) fold(v[u]);
   }
   for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)
@@ -531,17 +554,7 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fused_kernel(const uint16_t
   const float scale = on ? dloss / (float)n : 0.0f;
   const float l2 = lse * LOG2E;
   uint16_t* dx = dX + row * ldd;
-#pragma unroll 4
-  for (int64_t cc = threadIdx.x; cc < nc; cc += XENT_THREADS) {
-    float f[8];
-    unpack8(*(const u32x4_t*)(x + cc * 8), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = on ? exp2_hw(fmaf(f[e], LOG2E, -l2)) : 0.0f;
-      f[e] = (p - (cc * 8 + e == lab ? 1.0f : 0.0f)) * scale;
-    }
-    *(u32x4_t*)(dx + cc * 8) = pack8(f);
-  }
+  xent_grad_chunks(x, dx, nc, lab, l2, scale, on);
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS) {
     const float p = on ? exp2_hw(fmaf(bf16_to_f32(x[j]), LOG2E, -l2)) : 0.0f;
     dx[j] = (uint16_t)f32_to_bf16((p - (j == lab ? 1.0f : 0.0f)) * scale);
