@@ -71,10 +71,16 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __rest
   const float wo = gemma ? 1.0f : 0.0f;
   float ss = 0.0f;
   if constexpr (NCH > 0) {
-    u32x4_t v[NCH];
+    // the weight's chunks are loaded with the row's (up to 8 per lane), so
+    // that the scaling pass does not wait for them after the reduction
+    constexpr bool WPRE = NCH <= 8;
+    u32x4_t v[NCH], vw[WPRE ? NCH : 1];
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
-      if (lane + 64 * i < nc) v[i] = *(const u32x4_t*)(x + (lane + 64 * i) * 8);
+      if (lane + 64 * i < nc) {
+        v[i] = *(const u32x4_t*)(x + (lane + 64 * i) * 8);
+        if constexpr (WPRE) vw[i] = *(const u32x4_t*)(w + (lane + 64 * i) * 8);
+      }
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
       if (lane + 64 * i < nc) {
@@ -91,7 +97,8 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __rest
       if (c < nc) {
         float f[8], g[8];
         unpack8(v[i], f);
-        unpack8(*(const u32x4_t*)(w + c * 8), g);
+        if constexpr (WPRE) unpack8(vw[i], g);
+        else unpack8(*(const u32x4_t*)(w + c * 8), g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = f[e] * r * (g[e] + wo);
         *(u32x4_t*)(Y + row * d + c * 8) = pack8(f);
@@ -137,12 +144,15 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
   const float r = rstd[row];
   float dot = 0.0f;
   if constexpr (NCH > 0) {
-    u32x4_t vx[NCH], vg[NCH];
+    // the weight's chunks are loaded once, with the row's (up to 8 per lane)
+    constexpr bool WPRE = NCH <= 8;
+    u32x4_t vx[NCH], vg[NCH], vw[WPRE ? NCH : 1];
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
       if (lane + 64 * i < nc) {
         vx[i] = *(const u32x4_t*)(x + (lane + 64 * i) * 8);
         vg[i] = *(const u32x4_t*)(dy + (lane + 64 * i) * 8);
+        if constexpr (WPRE) vw[i] = *(const u32x4_t*)(w + (lane + 64 * i) * 8);
       }
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
@@ -150,7 +160,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
         float f[8], g[8], ww[8];
         unpack8(vx[i], f);
         unpack8(vg[i], g);
-        unpack8(*(const u32x4_t*)(w + (lane + 64 * i) * 8), ww);
+        if constexpr (WPRE) unpack8(vw[i], ww);
+        else unpack8(*(const u32x4_t*)(w + (lane + 64 * i) * 8), ww);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot += g[e] * (ww[e] + wo) * f[e];
       }
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
         float f[8], g[8], ww[8];
         unpack8(vx[i], f);
         unpack8(vg[i], g);
-        unpack8(*(const u32x4_t*)(w + c * 8), ww);   // w is small and cached
+        if constexpr (WPRE) unpack8(vw[i], ww);
+        else unpack8(*(const u32x4_t*)(w + c * 8), ww);   // w is small and cached
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = r * (g[e] * (ww[e] + wo) - f[e] * k);
         *(u32x4_t*)(dX + row * d + c * 8) = pack8(f);
