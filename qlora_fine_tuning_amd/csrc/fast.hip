@@ -251,28 +251,37 @@ __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* X, int64_t ld
   const int64_t rest = e / groups;
   const int hb = (int)(rest % hblocks) * ROPE_HEADS_PER_THREAD;
   const int64_t t = rest / hblocks;
+  const int half = hd / 2;
+  const int nh = min(heads - hb, ROPE_HEADS_PER_THREAD);
+  // All loads are issued before the angles are formed: first the position and
+  // the group's 8 inverse frequencies (64 bytes of the argument block), which
+  // the angles wait for, then the head values, which stay in flight meanwhile
+  // (X and Y may be one buffer, so the compiler could not move a later head's
+  // loads above an earlier head's stores by itself). Formed one after
+  // another, each angle had waited for its own frequency's load first.
   const double p = (double)pos[t];
+  double fi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fi[i] = fr.inv_freq[q * 8 + i];
+  __builtin_amdgcn_sched_barrier(0);
+  // (heads past the last one reload that one: no branch between the loads,
+  // so the wait for the frequencies leaves the head loads in flight)
+  u32x4_t va[ROPE_HEADS_PER_THREAD], vb[ROPE_HEADS_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < ROPE_HEADS_PER_THREAD; ++i) {
+    const uint16_t* xs = X + t * ldx + (int64_t)(hb + min(i, nh - 1)) * hd + q * 8;
+    va[i] = *(const u32x4_t*)xs;
+    vb[i] = *(const u32x4_t*)(xs + half);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const double two_pi = 6.283185307179586476925286766559;
   float c[8], s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const double a = p * fr.inv_freq[q * 8 + i];
+    const double a = p * fi[i];
     const double red = a - rint(a / two_pi) * two_pi;   // |red| <= pi
     sincosf((float)red, &s[i], &c[i]);
     s[i] *= sign;
-  }
-  const int half = hd / 2;
-  const int nh = min(heads - hb, ROPE_HEADS_PER_THREAD);
-  // all loads first: X and Y may be one buffer, so the compiler could not
-  // move a later head's loads above an earlier head's stores by itself
-  u32x4_t va[ROPE_HEADS_PER_THREAD], vb[ROPE_HEADS_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < ROPE_HEADS_PER_THREAD; ++i) {
-    if (i < nh) {
-      const uint16_t* xs = X + t * ldx + (int64_t)(hb + i) * hd + q * 8;
-      va[i] = *(const u32x4_t*)xs;
-      vb[i] = *(const u32x4_t*)(xs + half);
-    }
   }
 #pragma unroll
   for (int i = 0; i < ROPE_HEADS_PER_THREAD; ++i) {
