@@ -537,16 +537,40 @@ hipError_t launch_colreduce_finish(const float* part, int chunks, int C, int R, 
 // All small LoRA operand layouts of one entry point in a single launch: job j
 // (blockIdx.y) copies a strided rows x cols view (or writes zeros when its
 // source is null). Jobs never overlap, so their order does not matter.
+// A thread takes up to 8 elements, spaced by the grid's thread count, and
+// loads all of its batch before it stores any of it (sources and
+// destinations of the jobs are disjoint). Few workgroups per job: when this
+// launch runs beside another kernel, its workgroups are dispatched in turn
+// with that kernel's, so a wide grid had stretched it several-fold.
 __global__ __launch_bounds__(256) void prep_kernel(PrepJobs jobs) {
+  constexpr int U = 8;
   const PrepJob& jb = jobs.j[blockIdx.y];
   const int64_t total = (int64_t)jb.rows * jb.cols;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int r = (int)(e / jb.cols);
-    const int c = (int)(e - (int64_t)r * jb.cols);
+  if (total <= 0) return;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  // element e (clamped to the job, so that every load is in bounds and none
+  // sits behind a branch): its destination and source offsets
+  // (job sizes fit 32 bits, which keeps the division short; the host checks)
+  auto offs = [&](int64_t e, int64_t& d, int64_t& sidx) {
+    const int r = (int)((uint32_t)e / (uint32_t)jb.cols);
+    const int c = (int)e - r * jb.cols;
     int64_t dr = r;
     if (jb.interleave) dr = 64 * (r >> 5) + 32 * (jb.interleave - 1) + (r & 31);
-    jb.dst[dr * jb.d_rs + (int64_t)c * jb.d_cs] =
-        jb.src ? jb.src[(int64_t)r * jb.s_rs + (int64_t)c * jb.s_cs] : (uint16_t)0;
+    d = dr * jb.d_rs + (int64_t)c * jb.d_cs;
+    sidx = (int64_t)r * jb.s_rs + (int64_t)c * jb.s_cs;
+  };
+  for (int64_t e0 = (int64_t)blockIdx.x * 256 + threadIdx.x; e0 < total; e0 += U * stride) {
+    uint16_t v[U];
+    int64_t d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t sidx;
+      offs(min(e0 + u * stride, total - 1), d[u], sidx);
+      v[u] = jb.src ? jb.src[sidx] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (e0 + u * stride < total) jb.dst[d[u]] = v[u];
   }
 }
 
@@ -554,10 +578,14 @@ hipError_t launch_prep(const PrepJobs& jobs, hipStream_t stream) {
   if (jobs.n <= 0) return hipSuccess;
   if (jobs.n > kMaxPrepJobs) return hipErrorInvalidValue;
   int64_t most = 0;
-  for (int i = 0; i < jobs.n; ++i) most = std::max(most, (int64_t)jobs.j[i].rows * jobs.j[i].cols);
-  int64_t bx = (most + 255) / 256;
+  for (int i = 0; i < jobs.n; ++i) {
+    const int64_t t = (int64_t)jobs.j[i].rows * jobs.j[i].cols;
+    if (jobs.j[i].rows < 0 || jobs.j[i].cols < 0 || t >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    most = std::max(most, t);
+  }
+  int64_t bx = (most + 256 * 8 - 1) / (256 * 8);   // one batch of 8 per thread
   if (bx < 1) bx = 1;
-  if (bx > 512) bx = 512;
+  if (bx > 64) bx = 64;
   prep_kernel<<<dim3((unsigned)bx, (unsigned)jobs.n), dim3(256), 0, stream>>>(jobs);
   return hipGetLastError();
 }
