@@ -65,7 +65,7 @@ typedef enum {
   QLORA_ESHAPE = -2,     /* k or n not a multiple of 64, negative m, size overflow */
   QLORA_EWORKSPACE = -3, /* ws NULL or ws_bytes below the query's answer */
   QLORA_EHIP = -4,       /* HIP launch/runtime error (including no device) */
-  QLORA_ENOTIMPL = -5    /* valid request that this build does not implement */
+  QLORA_ENOTIMPL = -5    /* valid request that this library does not implement */
 } qlora_status;
 
 typedef enum { QLORA_ACT_SWIGLU = 0, QLORA_ACT_GEGLU_TANH = 1 } qlora_act;

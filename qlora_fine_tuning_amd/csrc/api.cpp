@@ -414,7 +414,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ESHAPE: return "invalid shape (k, n, d, h must be positive multiples of 64; m >= 0)";
     case QLORA_EWORKSPACE: return "workspace missing, misaligned or smaller than the query's answer";
     case QLORA_EHIP: return "HIP runtime or launch error (see qlora_last_error)";
-    case QLORA_ENOTIMPL: return "not implemented in this build";
+    case QLORA_ENOTIMPL: return "not implemented in this library";
   }
   return "unknown status";
 }
