@@ -360,6 +360,34 @@ __device__ __forceinline__ void block_lse(float& mx, float& sm) {
   for (int i = 1; i < XENT_THREADS / 64; ++i) lse_merge(mx, sm, smx[i], ssm[i]);
 }
 
+// One thread's online (max, sum) over its chunks c = threadIdx.x + k *
+// XENT_THREADS of a row, XENT_LOADS chunk loads in flight (the forward and
+// the fused kernel share this pass, so they give the same bits).
+__device__ __forceinline__ void row_lse_pass(const uint16_t* x, int64_t nc, float& mx, float& sm) {
+  auto fold = [&](const u32x4_t& v, float& m_, float& s_) {
+    float f[8];
+    unpack8(v, f);
+    float cm = f[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
+    const float mn = fmaxf(m_, cm * LOG2E);
+    float cs = s_ * exp2_hw(m_ - mn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs += exp2_hw(fmaf(f[e], LOG2E, -mn));
+    m_ = mn;
+    s_ = cs;
+  };
+  int64_t c = threadIdx.x;
+  for (; c + (XENT_LOADS - 1) * XENT_THREADS < nc; c += XENT_LOADS * XENT_THREADS) {   // loads in flight
+    u32x4_t v[XENT_LOADS];
+#pragma unroll
+    for (int u = 0; u < XENT_LOADS; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
+#pragma unroll
+    for (int u = 0; u < XENT_LOADS; ++u) fold(v[u], mx, sm);
+  }
+  for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8), mx, sm);
+}
+
 // The gradient of one row's 8-value chunks, c = threadIdx.x + k * XENT_THREADS:
 // dx = (2^(x log2(e) - l2) - onehot(lab)) * scale. Each chunk is read and
 // written by the same thread, so dx may be x; the loads of a batch of chunks
@@ -402,31 +430,11 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fwd_kernel(const uint16_t* 
   const int64_t row = blockIdx.x;
   const uint16_t* x = X + row * ld;
   const int64_t nc = V / 8;
+  // fold 8 finite values at a time: rescale the running sum to the new
+  // maximum (no branch; 2^(-inf) = 0 covers the empty start), then add their
+  // exponentials
   float mx = -INFINITY, sm = 0.0f;
-  // fold 8 finite values: rescale the running sum to the new maximum (no
-  // branch; 2^(-inf) = 0 covers the empty start), then add their exponentials
-  auto fold = [&](const u32x4_t& v) {
-    float f[8];
-    unpack8(v, f);
-    float cm = f[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
-    const float mn = fmaxf(mx, cm * LOG2E);
-    float cs = sm * exp2_hw(mx - mn);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs += exp2_hw(fmaf(f[e], LOG2E, -mn));
-    mx = mn;
-    sm = cs;
-  };
-  int64_t c = threadIdx.x;
-  for (; c + (XENT_LOADS - 1) * XENT_THREADS < nc; c += XENT_LOADS * XENT_THREADS) {   // loads in flight
-    u32x4_t v[XENT_LOADS];
-#pragma unroll
-    for (int u = 0; u < XENT_LOADS; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
-#pragma unroll
-    for (int u = 0; u < XENT_LOADS; ++u) fold(v[u]);
-  }
-  for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
+  row_lse_pass(x, nc, mx, sm);
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)   // tail of V % 8
     lse_merge(mx, sm, bf16_to_f32(x[j]) * LOG2E, 1.0f);
   block_lse(mx, sm);
@@ -538,28 +546,7 @@ __global__ __launch_bounds__(XENT_THREADS) void xent_fused_kernel(const uint16_t
   const uint16_t* x = X + row * ld;
   const int64_t nc = V / 8;
   float mx = -INFINITY, sm = 0.0f;
-  auto fold = [&](const u32x4_t& v) {
-    float f[8];
-    unpack8(v, f);
-    float cm = f[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
-    const float mn = fmaxf(mx, cm * LOG2E);
-    float cs = sm * exp2_hw(mx - mn);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs += exp2_hw(fmaf(f[e], LOG2E, -mn));
-    mx = mn;
-    sm = cs;
-  };
-  int64_t c = threadIdx.x;
-  for (; c + (XENT_LOADS - 1) * XENT_THREADS < nc; c += XENT_LOADS * XENT_THREADS) {   // loads in flight
-    u32x4_t v[XENT_LOADS];
-#pragma unroll
-    for (int u = 0; u < XENT_LOADS; ++u) v[u] = *(const u32x4_t*)(x + (c + u * XENT_THREADS) * 8);
-#pragma unroll
-    for (int u = 0; u < XENT_LOADS; ++u) fold(v[u]);
-  }
-  for (; c < nc; c += XENT_THREADS) fold(*(const u32x4_t*)(x + c * 8));
+  row_lse_pass(x, nc, mx, sm);
   for (int64_t j = nc * 8 + threadIdx.x; j < V; j += XENT_THREADS)
     lse_merge(mx, sm, bf16_to_f32(x[j]) * LOG2E, 1.0f);
   block_lse(mx, sm);   // ends with every thread past the block's barrier
